@@ -1,0 +1,293 @@
+"""The DiT denoiser step written out as plain fp64 formulas (test
+infrastructure only; see the package docstring).
+
+Sources (web pages; cited by title and section):
+
+* "Difflet" paper (paperpeel.com/paper/2610.23047): section 1 Introduction and
+  section 3 Model Pipelines (the denoiser predicts a velocity from latent,
+  timestep and conditioning; the scheduler turns it into a less noisy
+  latent), section 4 (joint attention: one softmax over visual and text
+  keys), section 4.2 Representing Attention Mask (padded text keys placed
+  after all valid keys, excluded by a contiguous [0, bound) interval).
+* "Difflet Engineering Report: Diffusion Inference on AWS Trainium":
+  "Terms used in this report" (AdaLN: LayerNorm whose scale and shift come
+  from the timestep conditioning; UniPC state kept in fp32), "Wan attention
+  head sharding and global RMS" (Q/K RMS over the whole projection, not per
+  head shard), "Video output corrections" (scheduler state in fp32),
+  "Attention CTE routing and mask representation" (only contiguous hard
+  masks take the bounded path).
+* "ChunkFlow" Appendix B, equations (13)-(17): a block's dominant work is the
+  QKV and output projections, joint attention and the MLP.
+
+Where the pages leave a step open, the plainest reading is taken and stated
+in the docstring of the function that implements it.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf
+
+from .numerics import bf16_decode, round_bf16
+
+
+# ----------------------------------------------------------------------------
+# per-token steps
+# ----------------------------------------------------------------------------
+
+def adaln_modulate(x, shift, scale, eps):
+    """Adaptive LayerNorm ("Difflet Engineering Report", Terms used in this
+    report: AdaLN).  Normalise every token over the hidden width with the
+    biased variance and no learned affine, then apply the timestep
+    modulation as x_hat * (1 + scale) + shift.  ``shift`` and ``scale``
+    broadcast against ``x`` (one vector per batch row)."""
+    x = np.asarray(x, dtype=np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    x_hat = (x - mu) / np.sqrt(var + eps)
+    return x_hat * (1.0 + scale) + shift
+
+
+def linear(a, w, b=None):
+    """y = a W^T + b with W stored [out, in] ("ChunkFlow" Appendix B, the
+    projection and MLP terms of equations (13) and (16))."""
+    y = np.asarray(a, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+    if b is not None:
+        y = y + b
+    return y
+
+
+def rms_norm_full(q, gain, eps):
+    """RMSNorm of a Q or K projection over its full width (all heads at once):
+    q / sqrt(mean(q^2) + eps) * gain.  The pages require the sum of squares
+    to cover the whole projection, not each head shard ("Difflet Engineering
+    Report", Wan attention head sharding and global RMS)."""
+    q = np.asarray(q, dtype=np.float64)
+    ms = (q * q).mean(axis=-1, keepdims=True)
+    return q / np.sqrt(ms + eps) * gain
+
+
+def gelu_erf(z):
+    """GELU in its exact form z * Phi(z) = z * (1 + erf(z / sqrt 2)) / 2.
+    The pages name the MLP but not its activation; the erf form is taken."""
+    z = np.asarray(z, dtype=np.float64)
+    return z * 0.5 * (1.0 + erf(z / math.sqrt(2.0)))
+
+
+def silu(z):
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+# ----------------------------------------------------------------------------
+# positions and RoPE
+# ----------------------------------------------------------------------------
+
+def token_positions(grid, n_txt):
+    """Integer (t, h, w) position of every token of the joint sequence
+    [visual; text].  Visual token i of a (T, H, W) latent grid, row-major,
+    sits at t = i // (H W), h = (i // W) mod H, w = i mod W.  Text tokens get
+    position (0, 0, 0), so RoPE leaves them unrotated (the pages name image
+    RoPE but do not define text positions; this is the reading taken)."""
+    T, H, W = (int(g) for g in grid)
+    i = np.arange(T * H * W, dtype=np.int64)
+    vis = np.stack([i // (H * W), (i // W) % H, i % W], axis=1)
+    txt = np.zeros((int(n_txt), 3), dtype=np.int64)
+    return np.concatenate([vis, txt], axis=0)
+
+
+def rope_axial(x, pos, dims, theta):
+    """Axial rotary embedding on x [..., N, heads, d].
+
+    The head dimension is split into consecutive blocks of dims = (d_t, d_h,
+    d_w) for the three axes (a zero entry skips that axis).  Inside the block
+    of axis a, the pair (2j, 2j+1) is rotated by the angle
+    pos_a * theta**(-2j / d_a), j = 0 .. d_a/2 - 1:
+    (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos).
+    Base theta, interleaved pairing and the block order are the reading taken
+    (the pages only name RoPE)."""
+    x = np.asarray(x, dtype=np.float64)
+    pos = np.asarray(pos)
+    out = x.copy()
+    off = 0
+    for axis, d_a in enumerate(dims):
+        d_a = int(d_a)
+        if d_a == 0:
+            continue
+        j = np.arange(d_a // 2, dtype=np.float64)
+        inv_freq = float(theta) ** (-2.0 * j / d_a)
+        ang = pos[:, axis].astype(np.float64)[:, None] * inv_freq[None, :]  # [N, d_a/2]
+        c = np.cos(ang)[:, None, :]  # [N, 1, d_a/2] broadcast over heads
+        s = np.sin(ang)[:, None, :]
+        ev = off + 2 * np.arange(d_a // 2)
+        x0 = x[..., ev]
+        x1 = x[..., ev + 1]
+        out[..., ev] = x0 * c - x1 * s
+        out[..., ev + 1] = x0 * s + x1 * c
+        off += d_a
+    return out
+
+
+# ----------------------------------------------------------------------------
+# joint attention
+# ----------------------------------------------------------------------------
+
+def attention_probs(q, k, n_keys_valid, scale):
+    """Softmax weights of one (batch row, head): q [Nq, d], k [Nk, d].
+
+    Scores s_ij = scale * q_i . k_j.  Keys j >= n_keys_valid are padding and
+    get weight exactly 0; the valid keys form the interval [0, n_keys_valid)
+    ("Difflet", section 4.2 Representing Attention Mask).  Every query row is
+    normalised by one softmax over all its valid keys, visual and text
+    together ("Difflet", section 4, joint attention)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    nv = int(n_keys_valid)
+    s = (q @ k[:nv].T) * scale
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    p = np.zeros((q.shape[0], k.shape[0]), dtype=np.float64)
+    p[:, :nv] = e / e.sum(axis=1, keepdims=True)
+    lse = (m + np.log(e.sum(axis=1, keepdims=True)))[:, 0]
+    return p, lse
+
+
+def joint_attention(q, k, v, n_vis, txt_valid, scale=None, chunk=1024):
+    """Joint attention over [visual; text] tokens.
+
+    k, v: [B, N, heads, d] (N = n_vis + n_txt); row b's keys
+    j < n_vis + txt_valid[b] are valid.  q: [B, R, heads, d] holds the query
+    rows wanted -- all N of them (padded text rows included) or any subset:
+    there is no positional mask, so every output row depends only on its own
+    query and on all keys, and a subset is exact.  The default scale is
+    1/sqrt(d).  Returns (o [B, R, heads, d], lse [B, heads, R]) where lse is
+    the natural log of each row's softmax denominator (max included).
+    """
+    qsel = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, N, Hh, d = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    R = qsel.shape[1]
+    o = np.zeros((B, R, Hh, d), dtype=np.float64)
+    lse = np.zeros((B, Hh, R), dtype=np.float64)
+    for b in range(B):
+        nk = int(n_vis) + int(txt_valid[b])
+        for h in range(Hh):
+            kh = k[b, :, h, :]
+            vh = v[b, :, h, :]
+            for r0 in range(0, R, chunk):
+                r1 = min(R, r0 + chunk)
+                p, l = attention_probs(qsel[b, r0:r1, h, :], kh, nk, scale)
+                o[b, r0:r1, h, :] = p[:, :nk] @ vh[:nk]
+                lse[b, h, r0:r1] = l
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# the block
+# ----------------------------------------------------------------------------
+
+def _dec(a):
+    return bf16_decode(a) if np.asarray(a).dtype == np.uint16 else np.asarray(a, np.float64)
+
+
+def block_forward(inp, shape, round_points=True, rows=None, keep=False):
+    """One DiT block on x [B, N, D] (N = visual then text tokens).
+
+    Order of steps (a joint-attention block with adaLN modulation; the
+    dominant work is equations (13) and (16) of "ChunkFlow" Appendix B, the
+    attention is "Difflet" section 4 with the section 4.2 interval mask):
+
+      h  = adaLN(x; shift1, scale1)
+      q, k, v = split(h W_qkv^T + b_qkv)
+      q^ = RoPE(RMSNorm_D(q) * g_q), k^ = RoPE(RMSNorm_D(k) * g_k)
+      o  = JointAttention(q^, k^, v; n_vis + txt_valid[b])
+      x1 = x + gate1 * (o W_o^T + b_o)
+      h2 = adaLN(x1; shift2, scale2)
+      u  = GELU(h2 W_up^T + b_up)
+      x2 = x1 + gate2 * (u W_dn^T + b_dn)
+
+    The modulation vector per batch row is (shift1, scale1, gate1, shift2,
+    scale2, gate2), each of width D.  With ``round_points`` the value is
+    rounded to bfloat16 wherever the GPU path stores bfloat16 (h, qkv, q^,
+    k^, o, x1, h2, u, x2); everything between those points is fp64.
+
+    ``rows`` restricts the output to a set of token indices (same for every
+    batch row): only keys and values need every token, every other step is
+    per token, so the restricted result is exact for those rows.
+    Returns x2 [B, R, D] (and the intermediates when ``keep``).
+    """
+    R_ = round_bf16 if round_points else (lambda a: a)
+    B, N, D = shape.batch, shape.n_tok, shape.hidden
+    H, d = shape.heads, shape.head_dim
+    x = _dec(inp["x"]).reshape(B, N, D)
+    mod = _dec(inp["mod"]).reshape(B, 6, D)
+    shift1, scale1, gate1, shift2, scale2, gate2 = (mod[:, i][:, None, :] for i in range(6))
+    w_qkv, b_qkv = _dec(inp["w_qkv"]), _dec(inp["b_qkv"])
+    valid = np.asarray(inp["txt_valid"], dtype=np.int64)
+    pos = token_positions(shape.grid, shape.n_txt)
+
+    h = R_(adaln_modulate(x, shift1, scale1, shape.ln_eps))
+    # keys and values for every token
+    kv = R_(linear(h, w_qkv[D:], b_qkv[D:]))
+    k_raw, v = kv[..., :D], kv[..., D:]
+    k_hat = R_(rope_axial(rms_norm_full(k_raw, _dec(inp["g_k"]), shape.rms_eps)
+                          .reshape(B, N, H, d), pos, shape.rope, shape.rope_theta))
+    sel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    q_raw = R_(linear(h[:, sel], w_qkv[:D], b_qkv[:D]))
+    q_hat = R_(rope_axial(rms_norm_full(q_raw, _dec(inp["g_q"]), shape.rms_eps)
+                          .reshape(B, len(sel), H, d), pos[sel], shape.rope, shape.rope_theta))
+    o, _ = joint_attention(q_hat, k_hat, v.reshape(B, N, H, d), shape.n_vis, valid)
+    o = R_(o.reshape(B, len(sel), D))
+    xs = x[:, sel]
+    x1 = R_(xs + gate1 * linear(o, _dec(inp["w_o"]), _dec(inp["b_o"])))
+    h2 = R_(adaln_modulate(x1, shift2, scale2, shape.ln_eps))
+    u = R_(gelu_erf(linear(h2, _dec(inp["w_up"]), _dec(inp["b_up"]))))
+    x2 = R_(x1 + gate2 * linear(u, _dec(inp["w_dn"]), _dec(inp["b_dn"])))
+    if keep:
+        return x2, {"h": h[:, sel], "q_hat": q_hat, "k_hat": k_hat, "v": v, "o": o,
+                    "x1": x1, "h2": h2, "u": u, "qkv_q": q_raw, "k_raw": k_raw}
+    return x2
+
+
+# ----------------------------------------------------------------------------
+# sampler
+# ----------------------------------------------------------------------------
+
+def sigma_schedule(steps):
+    """Noise levels sigma_i = 1 - i/steps, i = 0..steps (a linear schedule from
+    1 to 0; sigma = 0 is only ever a target, never evaluated)."""
+    return 1.0 - np.arange(steps + 1, dtype=np.float64) / steps
+
+
+def cfg_combine(v_cond, v_uncond, guidance):
+    """Classifier-free guidance, applied once to the two predictions
+    ("Difflet Engineering Report", CFG parallelism applies the guidance
+    combination once): v_uncond + g (v_cond - v_uncond)."""
+    v_cond = np.asarray(v_cond, dtype=np.float64)
+    v_uncond = np.asarray(v_uncond, dtype=np.float64)
+    return v_uncond + guidance * (v_cond - v_uncond)
+
+
+def euler_update(x, v, sigma, sigma_next):
+    """Explicit Euler step of the flow-matching ODE dx/dsigma = v: the
+    denoiser's velocity moves the latent from sigma to sigma_next
+    ("Difflet", section 1 and section 3: the scheduler turns the velocity into
+    a less noisy latent).  The latent is kept in full precision (fp32 on the
+    GPU, "Difflet Engineering Report", Video output corrections)."""
+    return np.asarray(x, dtype=np.float64) + (sigma_next - sigma) * np.asarray(v, np.float64)
+
+
+def timestep_features(t, dim):
+    """Sinusoidal features of a scalar timestep t (DiT-style): with
+    half = dim/2 and f_j = 10000**(-j/half), the vector [cos(t f), sin(t f)].
+    The pages do not define the timestep embedding; this is the reading
+    taken."""
+    half = dim // 2
+    f = np.exp(-math.log(10000.0) * np.arange(half, dtype=np.float64) / half)
+    a = float(t) * f
+    return np.concatenate([np.cos(a), np.sin(a)])
