@@ -214,7 +214,9 @@ def block_forward(inp, shape, round_points=True, rows=None, keep=False):
     The modulation vector per batch row is (shift1, scale1, gate1, shift2,
     scale2, gate2), each of width D.  With ``round_points`` the value is
     rounded to bfloat16 wherever the GPU path stores bfloat16 (h, qkv, q^,
-    k^, o, x1, h2, u, x2); everything between those points is fp64.
+    k^, o, h2, u); everything between those points is fp64.  The residual
+    stream x, x1, x2 is kept in full precision (fp32 on the GPU), so it is
+    never rounded.
 
     ``rows`` restricts the output to a set of token indices (same for every
     batch row): only keys and values need every token, every other step is
@@ -244,10 +246,10 @@ def block_forward(inp, shape, round_points=True, rows=None, keep=False):
     o, _ = joint_attention(q_hat, k_hat, v.reshape(B, N, H, d), shape.n_vis, valid)
     o = R_(o.reshape(B, len(sel), D))
     xs = x[:, sel]
-    x1 = R_(xs + gate1 * linear(o, _dec(inp["w_o"]), _dec(inp["b_o"])))
+    x1 = xs + gate1 * linear(o, _dec(inp["w_o"]), _dec(inp["b_o"]))
     h2 = R_(adaln_modulate(x1, shift2, scale2, shape.ln_eps))
     u = R_(gelu_erf(linear(h2, _dec(inp["w_up"]), _dec(inp["b_up"]))))
-    x2 = R_(x1 + gate2 * linear(u, _dec(inp["w_dn"]), _dec(inp["b_dn"])))
+    x2 = x1 + gate2 * linear(u, _dec(inp["w_dn"]), _dec(inp["b_dn"]))
     if keep:
         return x2, {"h": h[:, sel], "q_hat": q_hat, "k_hat": k_hat, "v": v, "o": o,
                     "x1": x1, "h2": h2, "u": u, "qkv_q": q_raw, "k_raw": k_raw}
