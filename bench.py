@@ -1,0 +1,255 @@
+"""Benchmark of the DiT denoiser hot path on one MI355X.
+
+A step is one denoising step of a single-block video DiT at the 480p shape
+(32,760 visual + 512 text tokens, 226 valid, hidden 5120, 40 heads x 128,
+MLP 13824, batch 1): timestep conditioning, input projection, the block
+(adaLN, QKV GEMM, Q/K RMSNorm + 3D RoPE, joint attention, output projection
+with gated residual, GELU MLP with gated residual), final adaLN + projection
+and the Euler update -- one call of dit_denoise_step.  Inputs are seeded
+synthetic tensors already resident in HBM.
+
+Prints ONE JSON line: ms/step (the value), the block alone, and joint
+attention's TFLOP/s against the bf16 dense MFMA peak (the roofline object),
+plus the CPU oracle timed on a bounded sample of the same step.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DiT block ms/step + joint-attn TFLOP/s (% bf16 MFMA peak) @32760+512 tok"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
+BLOCK_NAMES = ("w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "w_up", "b_up", "w_dn", "b_dn")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=64,
+                   help="query rows in the CPU oracle's bounded sample")
+    return p.parse_args()
+
+
+def dev_bf16(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def attention_flops(n_tok, n_valid_keys, heads, head_dim, batch=1):
+    """Algorithmic FLOPs of joint attention: QK^T and PV over the valid keys
+    of every query row (2 * 2 * d per query-key pair and head)."""
+    return 4.0 * batch * heads * head_dim * n_tok * n_valid_keys
+
+
+def block_flops(s, valid):
+    M = s.batch * s.n_tok
+    D, F = s.hidden, s.mlp
+    gemm = 2.0 * M * D * (3 * D) + 2.0 * M * D * D + 2.0 * M * D * F * 2
+    attn = sum(attention_flops(s.n_tok, s.n_vis + int(L), s.heads, s.head_dim) for L in valid)
+    return gemm + attn
+
+
+def timed(fn, reps, stream):
+    """Average ms of `fn` over `reps` calls, HIP events on the launch stream."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / reps
+
+
+def cpu_baseline(shape, model, n_rows):
+    """The oracle's denoising step (fp64 NumPy, as it stands) on a bounded
+    sample: n_rows seeded query rows, with keys and values computed for every
+    token.  The full-step figure scales the measured time by the ratio of
+    algorithmic FLOPs (full step / sample); the oracle's materialised-softmax
+    attention runs slower than its BLAS GEMMs, so this underestimates a full
+    oracle step."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"), default=1)
+    except Exception:  # noqa: BLE001
+        threads = 1
+    b = shape.block
+    sig = O.sigma_schedule(shape.steps)
+    lat = O.bf16_decode(model["latent"]).reshape(1, b.n_vis, shape.latent_channels)
+    rng = np.random.default_rng(0xD17 + n_rows)
+    rows = np.sort(rng.choice(b.n_vis, size=n_rows, replace=False))
+    t0 = time.perf_counter()
+    O.denoise_step(model["oracle_view"], lat, sig[0], sig[1], shape.guidance, rows=rows)
+    t = time.perf_counter() - t0
+    D, F, C = b.hidden, b.mlp, shape.latent_channels
+    nk = b.n_vis + int(model["oracle_view"].txt_valid[0])
+    per_row = (2.0 * D * D * 2 + 2.0 * D * F * 2 + 4.0 * b.heads * b.head_dim * nk
+               + 2.0 * C * D * 2)
+    kv_all = 2.0 * b.n_tok * D * 2 * D
+    f_sample = kv_all + n_rows * per_row
+    f_full = kv_all + b.n_tok * per_row
+    return {"value": round(t * f_full / f_sample * 1e3, 1), "unit": "ms/step (extrapolated)",
+            "cores": int(threads), "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle, one c3 denoising step restricted to {n_rows} seeded query "
+                       f"rows (keys/values for all {b.n_tok} tokens): {t:.1f} s measured; scaled by "
+                       f"algorithmic FLOPs x{f_full / f_sample:.1f} to the full step (an "
+                       "underestimate: the oracle's attention is slower than its GEMMs)"),
+            "measured_s": round(t, 2),
+            "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import diffusion_transformer_denoising_dit_amd as D
+    from synthetic import configs as C
+    from synthetic import gen as G
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    shape = C.C3_STEP
+    blk = shape.block
+    t_gen = time.perf_counter()
+    inp = G.loop_inputs(shape)
+    layer = inp.layer(0)
+    print(f"[bench] inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr,
+          flush=True)
+
+    glue = {"t_w1": inp.t_w1, "t_b1": inp.t_b1, "t_w2": inp.t_w2, "t_b2": inp.t_b2,
+            "in_w": inp.in_w, "in_b": inp.in_b, "fin_w": inp.fin_mod_w, "fin_b": inp.fin_mod_b,
+            "out_w": inp.out_w, "out_b": inp.out_b, "text": inp.text}
+    dglue = {k: dev_bf16(v) for k, v in glue.items()}
+    dl = {k: dev_bf16(v) for k, v in layer.items()}
+    weights = D.model_weights(dglue, [{n: dl[n] for n in BLOCK_NAMES}], [dl["mod_w"]], [dl["mod_b"]])
+    desc = D.model_desc(shape, inp.txt_valid)
+    ws_bytes = D.dit_denoise_workspace_bytes(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    lat0 = torch.from_numpy(
+        (inp.latent.astype(np.uint32) << 16).view(np.float32).reshape(1, blk.n_vis, -1)).cuda()
+    lat = lat0.clone()
+    stream = torch.cuda.current_stream()
+    sig = [1.0 - i / shape.steps for i in range(shape.steps + 1)]
+    counter = {"i": 0}
+
+    def step():
+        i = counter["i"] % shape.steps
+        D.dit_denoise_step(desc, weights, lat, sig[i], sig[i + 1], shape.guidance, ws, ws_bytes)
+        counter["i"] += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms_step = timed(step, args.steps, stream)
+    assert torch.isfinite(lat).all(), "non-finite latent"
+
+    # the block alone (same weights, modulation from the step's own buffers)
+    bdesc = D.block_desc(blk, inp.txt_valid, 0)
+    bws_bytes = D.dit_block_workspace_bytes(bdesc)
+    bws = torch.empty(bws_bytes, dtype=torch.uint8, device="cuda")
+    x = torch.randn((blk.batch, blk.n_tok, blk.hidden), generator=torch.Generator("cuda").manual_seed(3),
+                    device="cuda")
+    mod = (torch.randn((6, blk.hidden), generator=torch.Generator("cuda").manual_seed(4), device="cuda")
+           * 0.1).to(torch.bfloat16)
+    bw = {n: dl[n] for n in BLOCK_NAMES}
+
+    def block():
+        D.dit_block_forward(bdesc, bw, mod, x, bws, bws_bytes)
+
+    block()
+    ms_block = timed(block, max(3, args.steps), stream)
+
+    # joint attention alone, q/k/v as column blocks of one [N, 3*H*d] buffer (the block layout)
+    HD = blk.hidden
+    qkv = torch.randn((blk.batch, blk.n_tok, 3 * HD), generator=torch.Generator("cuda").manual_seed(5),
+                      device="cuda").to(torch.bfloat16)
+    o = torch.empty((blk.batch, blk.n_tok, HD), dtype=torch.bfloat16, device="cuda")
+    adesc = D.attn_desc(blk.batch, blk.n_vis, blk.n_txt, blk.heads, blk.head_dim, inp.txt_valid)
+
+    def attn():
+        D.dit_joint_attention(adesc, qkv, qkv[..., HD:], qkv[..., 2 * HD:], 3 * HD, o, HD)
+
+    attn()
+    ms_attn = timed(attn, max(5, args.steps), stream)
+    valid = [int(v) for v in inp.txt_valid]
+    a_flop = sum(attention_flops(blk.n_tok, blk.n_vis + L, blk.heads, blk.head_dim) for L in valid)
+    a_dense = attention_flops(blk.n_tok, blk.n_tok, blk.heads, blk.head_dim) * blk.batch
+    a_tflops = a_flop / (ms_attn * 1e-3) / 1e12
+    b_flop = block_flops(blk, valid)
+
+    result = {
+        "metric": METRIC,
+        "value": round(ms_step, 3),
+        "unit": "ms/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("c3 video 480p denoising step, 1 DiT block: 81 frames -> latent 21x30x52 "
+                         "after (1,2,2) patchify = 32760 visual + 512 text tokens (226 valid), "
+                         "hidden 5120, 40 heads x 128, MLP 13824, batch 1, 3D RoPE 44/42/42"),
+            "tokens": blk.n_tok, "valid_keys": blk.n_vis + valid[0], "hidden": blk.hidden,
+            "heads": blk.heads, "head_dim": blk.head_dim, "mlp": blk.mlp, "batch": blk.batch,
+        },
+        "block_ms": round(ms_block, 3),
+        "block_tflops": round(b_flop / (ms_block * 1e-3) / 1e12, 1),
+        "attention": {
+            "ms": round(ms_attn, 3),
+            "tflops": round(a_tflops, 1),
+            "frac_bf16_peak": round(a_tflops / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_tflop": round(a_flop / 1e12, 3),
+            "dense_tflop": round(a_dense / 1e12, 3),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_kernel<128> (joint attention)",
+            "achieved": round(a_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(a_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        # the oracle reads the same seeded model (its layer cached: drawn once)
+        view = G.loop_inputs(shape)
+        view.layer = lambda l, _w=layer: _w
+        del dl, dglue, weights, ws, bws, qkv
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(shape, {"latent": inp.latent, "oracle_view": view},
+                                              args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

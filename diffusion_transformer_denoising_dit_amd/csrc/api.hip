@@ -1,0 +1,629 @@
+// C ABI of the DiT hot path: argument checks on the host, then launches.
+// Every check runs before the first launch of a call, so a call that fails
+// enqueues nothing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dit.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dit_status fail(dit_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dit_status ok() {
+  g_err[0] = '\0';
+  return DIT_OK;
+}
+
+dit_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DIT_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [a0, a0+an) and [b0, b0+bn) byte ranges overlap?
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+dit_status check_attn_desc(const dit_attn_desc* d) {
+  if (!d) return fail(DIT_EINVAL, "attention descriptor is NULL");
+  if (d->batch < 1 || d->batch > DIT_MAX_BATCH)
+    return fail(DIT_EINVAL, "batch %d outside [1, %d]", d->batch, DIT_MAX_BATCH);
+  if (d->n_vis < 0 || d->n_txt < 0)
+    return fail(DIT_EINVAL, "negative token count (n_vis %d, n_txt %d)", d->n_vis, d->n_txt);
+  if (static_cast<int64_t>(d->n_vis) + d->n_txt < 1 ||
+      static_cast<int64_t>(d->n_vis) + d->n_txt > (1 << 30))
+    return fail(DIT_EINVAL, "n_vis + n_txt = %lld outside [1, 2^30]",
+                static_cast<long long>(d->n_vis) + d->n_txt);
+  if (d->heads < 1 || d->heads > 65535) return fail(DIT_EINVAL, "heads %d outside [1, 65535]", d->heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(DIT_EUNSUPPORTED, "head_dim %d: only 64 and 128 are implemented", d->head_dim);
+  for (int b = 0; b < d->batch; ++b) {
+    if (d->txt_valid[b] < 0 || d->txt_valid[b] > d->n_txt)
+      return fail(DIT_EINVAL, "txt_valid[%d] = %d outside [0, n_txt = %d]", b, d->txt_valid[b],
+                  d->n_txt);
+    if (d->n_vis + d->txt_valid[b] < 1)
+      return fail(DIT_EINVAL, "batch row %d has no valid key (n_vis 0, txt_valid 0)", b);
+  }
+  return DIT_OK;
+}
+
+dit_status check_block_desc(const dit_block_desc* d) {
+  if (!d) return fail(DIT_EINVAL, "block descriptor is NULL");
+  dit_status s = check_attn_desc(&d->attn);
+  if (s != DIT_OK) return s;
+  const dit_attn_desc& a = d->attn;
+  if (d->hidden != a.heads * a.head_dim)
+    return fail(DIT_EINVAL, "hidden %d != heads %d * head_dim %d", d->hidden, a.heads, a.head_dim);
+  if (d->hidden % 64 != 0 || d->hidden > 16384)
+    return fail(DIT_EUNSUPPORTED, "hidden %d: must be a multiple of 64 and <= 16384", d->hidden);
+  if (d->mlp < 64 || d->mlp % 64 != 0)
+    return fail(DIT_EUNSUPPORTED, "mlp %d: must be a positive multiple of 64", d->mlp);
+  if (d->grid_t < 1 || d->grid_h < 1 || d->grid_w < 1)
+    return fail(DIT_EINVAL, "grid (%d, %d, %d) must be positive", d->grid_t, d->grid_h, d->grid_w);
+  if (static_cast<int64_t>(d->grid_t) * d->grid_h * d->grid_w != a.n_vis)
+    return fail(DIT_EINVAL, "grid %d x %d x %d != n_vis %d", d->grid_t, d->grid_h, d->grid_w,
+                a.n_vis);
+  if (d->rope_t < 0 || d->rope_h < 0 || d->rope_w < 0 || d->rope_t % 2 || d->rope_h % 2 ||
+      d->rope_w % 2)
+    return fail(DIT_EINVAL, "rope dims (%d, %d, %d) must be even and >= 0", d->rope_t, d->rope_h,
+                d->rope_w);
+  if (d->rope_t + d->rope_h + d->rope_w != a.head_dim)
+    return fail(DIT_EINVAL, "rope dims sum %d != head_dim %d", d->rope_t + d->rope_h + d->rope_w,
+                a.head_dim);
+  if (!(d->rope_theta > 0.f) || !std::isfinite(d->rope_theta))
+    return fail(DIT_EINVAL, "rope_theta must be finite and > 0");
+  if (!(d->ln_eps >= 0.f) || !(d->rms_eps >= 0.f))
+    return fail(DIT_EINVAL, "ln_eps and rms_eps must be >= 0");
+  if (d->mod_stride < 0 || d->mod_stride % 4 != 0)
+    return fail(DIT_EINVAL, "mod_stride %lld must be >= 0 and a multiple of 4",
+                static_cast<long long>(d->mod_stride));
+  return DIT_OK;
+}
+
+dit::RopeParams rope_params(const dit_block_desc* d, uint16_t* qkv, int64_t row_stride,
+                            const uint16_t* gq, const uint16_t* gk) {
+  dit::RopeParams p{};
+  p.qkv = qkv;
+  p.row_stride = row_stride;
+  p.g_q = gq;
+  p.g_k = gk;
+  p.n_tok = d->attn.n_vis + d->attn.n_txt;
+  p.rows = static_cast<int64_t>(d->attn.batch) * p.n_tok;
+  p.n_vis = d->attn.n_vis;
+  p.hidden = d->hidden;
+  p.head_dim = d->attn.head_dim;
+  p.grid_h = d->grid_h;
+  p.grid_w = d->grid_w;
+  p.rope_t = d->rope_t;
+  p.rope_h = d->rope_h;
+  p.rope_w = d->rope_w;
+  p.theta = d->rope_theta;
+  p.eps = d->rms_eps;
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct WsLayout {
+  size_t h_off, big_off, total;
+};
+
+WsLayout ws_layout(const dit_block_desc* d) {
+  const size_t M = static_cast<size_t>(d->attn.batch) * (d->attn.n_vis + d->attn.n_txt);
+  const size_t D = d->hidden, F = d->mlp;
+  WsLayout w;
+  w.h_off = 0;
+  w.big_off = align256(M * D * 2);
+  w.total = w.big_off + align256(M * (3 * D > F ? 3 * D : F) * 2);
+  return w;
+}
+
+dit_status check_linear(const dit_linear_args* a) {
+  if (!a) return fail(DIT_EINVAL, "linear args are NULL");
+  if (a->m < 0 || a->n < 1 || a->k < 1)
+    return fail(DIT_EINVAL, "bad GEMM shape m %lld n %d k %d", static_cast<long long>(a->m), a->n,
+                a->k);
+  if (a->m == 0) return DIT_OK;
+  if (!a->a || !a->w || !a->out) return fail(DIT_EINVAL, "NULL a, w or out");
+  if (a->k % 64 != 0) return fail(DIT_EUNSUPPORTED, "k %d must be a multiple of 64", a->k);
+  if (a->n % 8 != 0) return fail(DIT_EUNSUPPORTED, "n %d must be a multiple of 8", a->n);
+  if (a->epilogue < DIT_EPI_BF16 || a->epilogue > DIT_EPI_GATED_RES_F32)
+    return fail(DIT_EINVAL, "unknown epilogue %d", a->epilogue);
+  if (a->lda < a->k || a->lda % 8 != 0)
+    return fail(DIT_EINVAL, "lda %lld must be >= k and a multiple of 8", static_cast<long long>(a->lda));
+  if (a->ldc < a->n || a->ldc % 8 != 0)
+    return fail(DIT_EINVAL, "ldc %lld must be >= n and a multiple of 8", static_cast<long long>(a->ldc));
+  if (a->group_rows < 0 || (a->group_rows > 0 && (a->a_group_stride < 0 || a->c_group_stride < 0 ||
+                                                  a->a_group_stride % 8 || a->c_group_stride % 8)))
+    return fail(DIT_EINVAL, "bad row grouping (group_rows %lld)", static_cast<long long>(a->group_rows));
+  if (!aligned(a->a, 16) || !aligned(a->w, 16) || !aligned(a->out, 16) ||
+      (a->bias && !aligned(a->bias, 16)))
+    return fail(DIT_EINVAL, "a, w, bias and out must be 16-byte aligned");
+  if (a->epilogue == DIT_EPI_GATED_RES_F32) {
+    if (!a->gate || a->gate_rows < 1 || a->gate_stride < 0 || a->gate_stride % 4 != 0 ||
+        !aligned(a->gate, 8))
+      return fail(DIT_EINVAL, "gated epilogue needs gate (8-byte aligned), gate_rows >= 1 and a "
+                              "gate_stride that is a multiple of 4");
+  } else {
+    // the output must not overlap the A operand's rows (bytes spanned by A)
+    const int64_t span_rows = a->group_rows > 0 ? a->group_rows : a->m;
+    const int64_t groups = a->group_rows > 0 ? (a->m + a->group_rows - 1) / a->group_rows : 1;
+    const size_t a_bytes = static_cast<size_t>(((groups - 1) * (a->group_rows > 0 ? a->a_group_stride : 0)) +
+                                               (span_rows - 1) * a->lda + a->k) * 2;
+    const size_t esz = a->epilogue == DIT_EPI_F32 ? 4 : 2;
+    const size_t c_bytes = static_cast<size_t>(((groups - 1) * (a->group_rows > 0 ? a->c_group_stride : 0)) +
+                                               (span_rows - 1) * a->ldc + a->n) * esz;
+    if (overlap(a->a, a_bytes, a->out, c_bytes))
+      return fail(DIT_EINVAL, "out overlaps the A operand");
+  }
+  return DIT_OK;
+}
+
+dit::GemmParams gemm_params(const dit_linear_args* a) {
+  dit::GemmParams p{};
+  p.a = a->a;
+  p.lda = a->lda;
+  p.w = a->w;
+  p.bias = a->bias;
+  p.m = a->m;
+  p.n = a->n;
+  p.k = a->k;
+  p.out = a->out;
+  p.ldc = a->ldc;
+  p.gate = a->gate;
+  p.gate_stride = a->gate_stride;
+  p.gate_rows = a->gate_rows > 0 ? a->gate_rows : 1;
+  p.group_rows = a->group_rows;
+  p.a_group_stride = a->a_group_stride;
+  p.c_group_stride = a->c_group_stride;
+  return p;
+}
+
+// The eight launches of one block (argument checks already done).  hbuf holds
+// h, then o, then h2; big holds qkv, then the MLP hidden.
+hipError_t block_launch(const dit_block_desc* desc, const dit_block_weights* w, const uint16_t* mod,
+                        int64_t ms, float* x, char* ws, hipStream_t stream, const char** what) {
+  const int B = desc->attn.batch;
+  const int64_t N = static_cast<int64_t>(desc->attn.n_vis) + desc->attn.n_txt;
+  const int64_t M = B * N;
+  const int D = desc->hidden, F = desc->mlp;
+  const WsLayout L = ws_layout(desc);
+  uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.h_off);   // h, then o, then h2
+  uint16_t* big = reinterpret_cast<uint16_t*>(ws + L.big_off);  // qkv, then the MLP hidden
+
+  hipError_t e;
+  // 1. h = adaLN(x; shift1, scale1)
+  e = dit::launch_adaln(x, M, D, N, mod + 0 * D, mod + 1 * D, ms, desc->ln_eps, hbuf, stream);
+  if (e != hipSuccess) { *what = "block: adaln 1"; return e; }
+  // 2. qkv = h W_qkv^T + b_qkv
+  dit::GemmParams g{};
+  g.a = hbuf; g.lda = D; g.w = w->w_qkv; g.bias = w->b_qkv; g.m = M; g.n = 3 * D; g.k = D;
+  g.out = big; g.ldc = 3 * D; g.gate_rows = 1;
+  e = dit::launch_gemm(g, DIT_EPI_BF16, stream);
+  if (e != hipSuccess) { *what = "block: qkv gemm"; return e; }
+  // 3. q, k <- RoPE(RMSNorm(.) * g)
+  e = dit::launch_qk_rmsnorm_rope(rope_params(desc, big, 3 * D, w->g_q, w->g_k), stream);
+  if (e != hipSuccess) { *what = "block: rmsnorm/rope"; return e; }
+  // 4. o = joint attention
+  dit::AttnParams ap{};
+  ap.q = big; ap.k = big + D; ap.v = big + 2 * D; ap.qkv_stride = 3 * D;
+  ap.out = hbuf; ap.out_stride = D; ap.lse = nullptr;
+  ap.n_tok = static_cast<int>(N); ap.heads = desc->attn.heads; ap.head_dim = desc->attn.head_dim;
+  ap.batch = B;
+  for (int b = 0; b < DIT_MAX_BATCH; ++b)
+    ap.n_valid[b] = b < B ? desc->attn.n_vis + desc->attn.txt_valid[b] : 0;
+  ap.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(desc->attn.head_dim));
+  e = dit::launch_attention(ap, stream);
+  if (e != hipSuccess) { *what = "block: attention"; return e; }
+  // 5. x += gate1 * (o W_o^T + b_o)
+  g = dit::GemmParams{};
+  g.a = hbuf; g.lda = D; g.w = w->w_o; g.bias = w->b_o; g.m = M; g.n = D; g.k = D;
+  g.out = x; g.ldc = D; g.gate = mod + 2 * D; g.gate_stride = ms; g.gate_rows = N;
+  e = dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream);
+  if (e != hipSuccess) { *what = "block: out-proj gemm"; return e; }
+  // 6. h2 = adaLN(x; shift2, scale2)
+  e = dit::launch_adaln(x, M, D, N, mod + 3 * D, mod + 4 * D, ms, desc->ln_eps, hbuf, stream);
+  if (e != hipSuccess) { *what = "block: adaln 2"; return e; }
+  // 7. u = GELU(h2 W_up^T + b_up)
+  g = dit::GemmParams{};
+  g.a = hbuf; g.lda = D; g.w = w->w_up; g.bias = w->b_up; g.m = M; g.n = F; g.k = D;
+  g.out = big; g.ldc = F; g.gate_rows = 1;
+  e = dit::launch_gemm(g, DIT_EPI_GELU_BF16, stream);
+  if (e != hipSuccess) { *what = "block: mlp-up gemm"; return e; }
+  // 8. x += gate2 * (u W_dn^T + b_dn)
+  g = dit::GemmParams{};
+  g.a = big; g.lda = F; g.w = w->w_dn; g.bias = w->b_dn; g.m = M; g.n = D; g.k = F;
+  g.out = x; g.ldc = D; g.gate = mod + 5 * D; g.gate_stride = ms; g.gate_rows = N;
+  e = dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream);
+  if (e != hipSuccess) { *what = "block: mlp-down gemm"; return e; }
+  return hipSuccess;
+}
+
+
+// Workspace of one denoising step: small conditioning buffers, the fp32
+// residual stream x, the final-norm output, the velocity and the block's own
+// workspace.
+struct StepLayout {
+  size_t feat, c, s, mod, fin, lat, x, hf, v, blk, total;
+};
+
+StepLayout step_layout(const dit_model_desc* m) {
+  const dit_block_desc& b = m->block;
+  const size_t B = b.attn.batch, N = static_cast<size_t>(b.attn.n_vis) + b.attn.n_txt;
+  const size_t D = b.hidden, C = m->latent_channels, nv = b.attn.n_vis;
+  const size_t Bl = m->cfg ? 1 : B;
+  StepLayout L;
+  size_t o = 0;
+  L.feat = o; o += align256(static_cast<size_t>(m->freq_dim) * 2);
+  L.c = o; o += align256(D * 2);
+  L.s = o; o += align256(D * 2);
+  L.mod = o; o += align256(6 * D * 2);
+  L.fin = o; o += align256(2 * D * 2);
+  L.lat = o; o += align256(Bl * nv * C * 2);
+  L.x = o; o += align256(B * N * D * 4);
+  L.hf = o; o += align256(B * N * D * 2);
+  L.v = o; o += align256(B * nv * C * 2);
+  L.blk = o; o += ws_layout(&b).total;
+  L.total = o;
+  return L;
+}
+
+dit_status check_model_desc(const dit_model_desc* m) {
+  if (!m) return fail(DIT_EINVAL, "model descriptor is NULL");
+  dit_block_desc b = m->block;
+  b.mod_stride = 0;
+  dit_status s = check_block_desc(&b);
+  if (s != DIT_OK) return s;
+  if (m->depth < 1 || m->depth > 4096) return fail(DIT_EINVAL, "depth %d outside [1, 4096]", m->depth);
+  if (m->latent_channels < 64 || m->latent_channels % 64 != 0)
+    return fail(DIT_EUNSUPPORTED, "latent_channels %d must be a positive multiple of 64",
+                m->latent_channels);
+  if (m->freq_dim < 64 || m->freq_dim % 64 != 0 || m->freq_dim > 4096)
+    return fail(DIT_EUNSUPPORTED, "freq_dim %d must be a multiple of 64 in [64, 4096]", m->freq_dim);
+  if (m->cfg != 0 && m->cfg != 1) return fail(DIT_EINVAL, "cfg must be 0 or 1");
+  if (m->cfg && b.attn.batch != 2) return fail(DIT_EINVAL, "cfg needs batch == 2 (cond, uncond)");
+  if (b.attn.n_vis < 1) return fail(DIT_EINVAL, "a denoising step needs visual tokens");
+  if (!std::isfinite(m->t_scale)) return fail(DIT_EINVAL, "t_scale must be finite");
+  return DIT_OK;
+}
+
+dit_status check_block_weights(const dit_block_weights* w) {
+  if (!w) return fail(DIT_EINVAL, "block weights are NULL");
+  const uint16_t* ptrs[] = {w->w_qkv, w->b_qkv, w->g_q, w->g_k, w->w_o,
+                            w->b_o,   w->w_up,  w->b_up, w->w_dn, w->b_dn};
+  for (const uint16_t* p : ptrs)
+    if (!p || !aligned(p, 16)) return fail(DIT_EINVAL, "a weight pointer is NULL or not 16-byte aligned");
+  return DIT_OK;
+}
+
+dit::GemmParams gemm(const uint16_t* a, int64_t lda, const uint16_t* w, const uint16_t* bias, int64_t m,
+                     int n, int k, void* out, int64_t ldc) {
+  dit::GemmParams g{};
+  g.a = a; g.lda = lda; g.w = w; g.bias = bias; g.m = m; g.n = n; g.k = k;
+  g.out = out; g.ldc = ldc; g.gate_rows = 1;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dit_version(void) { return "dit-mi355x 0.1 (gfx950)"; }
+
+const char* dit_last_error(void) { return g_err; }
+
+const char* dit_status_string(dit_status s) {
+  switch (s) {
+    case DIT_OK: return "DIT_OK";
+    case DIT_EINVAL: return "DIT_EINVAL";
+    case DIT_EUNSUPPORTED: return "DIT_EUNSUPPORTED";
+    case DIT_EWORKSPACE: return "DIT_EWORKSPACE";
+    case DIT_EHIP: return "DIT_EHIP";
+  }
+  return "unknown dit_status";
+}
+
+dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q, const uint16_t* k,
+                               const uint16_t* v, int64_t qkv_row_stride, uint16_t* out,
+                               int64_t out_row_stride, float* lse, float softmax_scale,
+                               hipStream_t stream) {
+  dit_status s = check_attn_desc(desc);
+  if (s != DIT_OK) return s;
+  if (!q || !k || !v || !out) return fail(DIT_EINVAL, "NULL q, k, v or out");
+  const int64_t hd = static_cast<int64_t>(desc->heads) * desc->head_dim;
+  if (qkv_row_stride < hd || qkv_row_stride % 8 != 0)
+    return fail(DIT_EINVAL, "qkv_row_stride %lld must be >= heads*head_dim and a multiple of 8",
+                static_cast<long long>(qkv_row_stride));
+  if (out_row_stride < hd || out_row_stride % 8 != 0)
+    return fail(DIT_EINVAL, "out_row_stride %lld must be >= heads*head_dim and a multiple of 8",
+                static_cast<long long>(out_row_stride));
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+      (lse && !aligned(lse, 4)))
+    return fail(DIT_EINVAL, "q, k, v and out must be 16-byte aligned");
+  if (!(softmax_scale >= 0.f) || !std::isfinite(softmax_scale))
+    return fail(DIT_EINVAL, "softmax_scale must be finite and >= 0");
+  const int64_t n_tok = static_cast<int64_t>(desc->n_vis) + desc->n_txt;
+  const size_t in_bytes = static_cast<size_t>((desc->batch * n_tok - 1) * qkv_row_stride + hd) * 2;
+  const size_t out_bytes = static_cast<size_t>((desc->batch * n_tok - 1) * out_row_stride + hd) * 2;
+  if (overlap(out, out_bytes, q, in_bytes) || overlap(out, out_bytes, k, in_bytes) ||
+      overlap(out, out_bytes, v, in_bytes))
+    return fail(DIT_EINVAL, "out overlaps q, k or v");
+  if (lse) {
+    const size_t lse_bytes = static_cast<size_t>(desc->batch) * desc->heads * n_tok * 4;
+    if (overlap(lse, lse_bytes, out, out_bytes) || overlap(lse, lse_bytes, q, in_bytes) ||
+        overlap(lse, lse_bytes, k, in_bytes) || overlap(lse, lse_bytes, v, in_bytes))
+      return fail(DIT_EINVAL, "lse overlaps q, k, v or out");
+  }
+  dit::AttnParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.qkv_stride = qkv_row_stride;
+  p.out = out;
+  p.out_stride = out_row_stride;
+  p.lse = lse;
+  p.n_tok = static_cast<int>(n_tok);
+  p.heads = desc->heads;
+  p.head_dim = desc->head_dim;
+  p.batch = desc->batch;
+  for (int b = 0; b < DIT_MAX_BATCH; ++b)
+    p.n_valid[b] = b < desc->batch ? desc->n_vis + desc->txt_valid[b] : 0;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt(static_cast<float>(desc->head_dim));
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(dit::launch_attention(p, stream), "attention launch");
+}
+
+dit_status dit_linear(const dit_linear_args* args, hipStream_t stream) {
+  dit_status s = check_linear(args);
+  if (s != DIT_OK) return s;
+  if (args->m == 0) return ok();
+  return hip_status(dit::launch_gemm(gemm_params(args), args->epilogue, stream), "gemm launch");
+}
+
+dit_status dit_adaln_modulate(const float* x, int64_t rows, int32_t hidden, int64_t rows_per_batch,
+                              const uint16_t* shift, const uint16_t* scale, int64_t mod_stride,
+                              float eps, uint16_t* out, hipStream_t stream) {
+  if (rows < 0) return fail(DIT_EINVAL, "rows %lld < 0", static_cast<long long>(rows));
+  if (rows == 0) return ok();
+  if (!x || !shift || !scale || !out) return fail(DIT_EINVAL, "NULL x, shift, scale or out");
+  if (hidden < 8 || hidden % 8 != 0 || hidden > 16384)
+    return fail(DIT_EUNSUPPORTED, "hidden %d must be a multiple of 8 in [8, 16384]", hidden);
+  if (rows_per_batch < 1) return fail(DIT_EINVAL, "rows_per_batch must be >= 1");
+  if (mod_stride < 0 || mod_stride % 4 != 0)
+    return fail(DIT_EINVAL, "mod_stride must be >= 0 and a multiple of 4");
+  if (!(eps >= 0.f)) return fail(DIT_EINVAL, "eps must be >= 0");
+  if (!aligned(x, 16) || !aligned(out, 8) || !aligned(shift, 8) || !aligned(scale, 8))
+    return fail(DIT_EINVAL, "x must be 16-byte aligned; out, shift, scale 8-byte aligned");
+  if (overlap(x, static_cast<size_t>(rows) * hidden * 4, out, static_cast<size_t>(rows) * hidden * 2))
+    return fail(DIT_EINVAL, "out overlaps x");
+  return hip_status(dit::launch_adaln(x, rows, hidden, rows_per_batch, shift, scale, mod_stride, eps,
+                                      out, stream),
+                    "adaln launch");
+}
+
+dit_status dit_qk_rmsnorm_rope(const dit_block_desc* desc, uint16_t* qkv, int64_t row_stride,
+                               const uint16_t* g_q, const uint16_t* g_k, hipStream_t stream) {
+  dit_status s = check_block_desc(desc);
+  if (s != DIT_OK) return s;
+  if (!qkv || !g_q || !g_k) return fail(DIT_EINVAL, "NULL qkv, g_q or g_k");
+  if (row_stride < 2 * static_cast<int64_t>(desc->hidden) || row_stride % 8 != 0)
+    return fail(DIT_EINVAL, "row_stride must be >= 2*hidden and a multiple of 8");
+  if (!aligned(qkv, 16) || !aligned(g_q, 16) || !aligned(g_k, 16))
+    return fail(DIT_EINVAL, "qkv, g_q and g_k must be 16-byte aligned");
+  return hip_status(dit::launch_qk_rmsnorm_rope(rope_params(desc, qkv, row_stride, g_q, g_k), stream),
+                    "rmsnorm/rope launch");
+}
+
+dit_status dit_debug_positions(const dit_block_desc* desc, int32_t* out, hipStream_t stream) {
+  dit_status s = check_block_desc(desc);
+  if (s != DIT_OK) return s;
+  if (!out) return fail(DIT_EINVAL, "NULL out");
+  return hip_status(dit::launch_positions(rope_params(desc, nullptr, 0, nullptr, nullptr), out, stream),
+                    "positions launch");
+}
+
+size_t dit_block_workspace_bytes(const dit_block_desc* desc) {
+  if (check_block_desc(desc) != DIT_OK) return 0;
+  ok();
+  return ws_layout(desc).total;
+}
+
+dit_status dit_block_forward(const dit_block_desc* desc, const dit_block_weights* w,
+                             const uint16_t* mod, float* x, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  dit_status s = check_block_desc(desc);
+  if (s != DIT_OK) return s;
+  if (!w) return fail(DIT_EINVAL, "weights struct is NULL");
+  const uint16_t* ptrs[] = {w->w_qkv, w->b_qkv, w->g_q, w->g_k, w->w_o,
+                            w->b_o,   w->w_up,  w->b_up, w->w_dn, w->b_dn};
+  for (const uint16_t* p : ptrs)
+    if (!p || !aligned(p, 16)) return fail(DIT_EINVAL, "a weight pointer is NULL or not 16-byte aligned");
+  if (!mod || !aligned(mod, 16)) return fail(DIT_EINVAL, "mod is NULL or not 16-byte aligned");
+  if (!x || !aligned(x, 16)) return fail(DIT_EINVAL, "x is NULL or not 16-byte aligned");
+  if (!workspace || !aligned(workspace, 256)) return fail(DIT_EINVAL, "workspace is NULL or not 256-byte aligned");
+  const WsLayout L = ws_layout(desc);
+  if (workspace_bytes < L.total)
+    return fail(DIT_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, L.total);
+  const int64_t M = static_cast<int64_t>(desc->attn.batch) * (desc->attn.n_vis + desc->attn.n_txt);
+  if (overlap(x, static_cast<size_t>(M) * desc->hidden * 4, workspace, L.total))
+    return fail(DIT_EINVAL, "x overlaps the workspace");
+  const char* what = nullptr;
+  const hipError_t e = block_launch(desc, w, mod, desc->mod_stride, x, static_cast<char*>(workspace),
+                                    stream, &what);
+  if (e != hipSuccess) return hip_status(e, what);
+  return ok();
+}
+
+dit_status dit_euler_step(float* x, const uint16_t* v_cond, const uint16_t* v_uncond, int64_t n,
+                          float guidance, float sigma, float sigma_next, hipStream_t stream) {
+  if (n < 0) return fail(DIT_EINVAL, "n %lld < 0", static_cast<long long>(n));
+  if (n == 0) return ok();
+  if (!x || !v_cond) return fail(DIT_EINVAL, "NULL x or v_cond");
+  if (!aligned(x, 16) || !aligned(v_cond, 8) || (v_uncond && !aligned(v_uncond, 8)))
+    return fail(DIT_EINVAL, "x must be 16-byte aligned, v_cond/v_uncond 8-byte aligned");
+  if (!std::isfinite(guidance) || !std::isfinite(sigma) || !std::isfinite(sigma_next))
+    return fail(DIT_EINVAL, "guidance and sigmas must be finite");
+  if (overlap(x, static_cast<size_t>(n) * 4, v_cond, static_cast<size_t>(n) * 2) ||
+      (v_uncond && overlap(x, static_cast<size_t>(n) * 4, v_uncond, static_cast<size_t>(n) * 2)))
+    return fail(DIT_EINVAL, "x overlaps a velocity buffer");
+  return hip_status(dit::launch_euler(x, v_cond, v_uncond, n, guidance, sigma_next - sigma, stream),
+                    "euler launch");
+}
+
+dit_status dit_timestep_features(const float* sigma, int32_t n, int32_t dim, float t_scale,
+                                 uint16_t* out, hipStream_t stream) {
+  if (n < 0) return fail(DIT_EINVAL, "n < 0");
+  if (n == 0) return ok();
+  if (!sigma || !out) return fail(DIT_EINVAL, "NULL sigma or out");
+  if (dim < 2 || dim > 4096 || dim % 2) return fail(DIT_EINVAL, "dim %d must be even in [2, 4096]", dim);
+  if (!std::isfinite(t_scale)) return fail(DIT_EINVAL, "t_scale must be finite");
+  return hip_status(dit::launch_timestep_features(sigma, 0.f, n, dim, t_scale, out, stream),
+                    "timestep launch");
+}
+
+dit_status dit_cast_f32_bf16(const float* in, int64_t ld_in, int64_t rows, int32_t cols,
+                             uint16_t* out, int64_t ld_out, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return fail(DIT_EINVAL, "negative rows/cols");
+  if (rows == 0 || cols == 0) return ok();
+  if (!in || !out) return fail(DIT_EINVAL, "NULL in or out");
+  if (cols % 4 || ld_in % 4 || ld_out % 4 || ld_in < cols || ld_out < cols)
+    return fail(DIT_EINVAL, "cols and strides must be multiples of 4, strides >= cols");
+  if (!aligned(in, 16) || !aligned(out, 8)) return fail(DIT_EINVAL, "in 16-byte, out 8-byte alignment");
+  return hip_status(dit::launch_cast_f32_bf16(in, ld_in, rows, cols, out, ld_out, stream), "cast launch");
+}
+
+dit_status dit_cast_bf16_f32(const uint16_t* in, int64_t ld_in, int64_t rows, int32_t cols,
+                             float* out, int64_t ld_out, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return fail(DIT_EINVAL, "negative rows/cols");
+  if (rows == 0 || cols == 0) return ok();
+  if (!in || !out) return fail(DIT_EINVAL, "NULL in or out");
+  if (cols % 4 || ld_in % 4 || ld_out % 4 || ld_in < cols || ld_out < cols)
+    return fail(DIT_EINVAL, "cols and strides must be multiples of 4, strides >= cols");
+  if (!aligned(in, 8) || !aligned(out, 16)) return fail(DIT_EINVAL, "in 8-byte, out 16-byte alignment");
+  return hip_status(dit::launch_cast_bf16_f32(in, ld_in, rows, cols, out, ld_out, stream), "cast launch");
+}
+
+size_t dit_denoise_workspace_bytes(const dit_model_desc* desc) {
+  if (check_model_desc(desc) != DIT_OK) return 0;
+  ok();
+  return step_layout(desc).total;
+}
+
+dit_status dit_denoise_step(const dit_model_desc* desc, const dit_model_weights* w, float* latent,
+                            float sigma, float sigma_next, float guidance, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  dit_status st = check_model_desc(desc);
+  if (st != DIT_OK) return st;
+  if (!w) return fail(DIT_EINVAL, "model weights are NULL");
+  const uint16_t* glue[] = {w->t_w1, w->t_b1, w->t_w2, w->t_b2, w->in_w, w->in_b,
+                            w->fin_w, w->fin_b, w->out_w, w->out_b, w->text};
+  for (const uint16_t* p : glue)
+    if (!p || !aligned(p, 16)) return fail(DIT_EINVAL, "a model weight is NULL or not 16-byte aligned");
+  if (!w->blocks || !w->mod_w || !w->mod_b) return fail(DIT_EINVAL, "NULL per-layer arrays");
+  for (int l = 0; l < desc->depth; ++l) {
+    st = check_block_weights(&w->blocks[l]);
+    if (st != DIT_OK) return st;
+    if (!w->mod_w[l] || !w->mod_b[l] || !aligned(w->mod_w[l], 16) || !aligned(w->mod_b[l], 16))
+      return fail(DIT_EINVAL, "modulation weights of layer %d are NULL or misaligned", l);
+  }
+  if (!latent || !aligned(latent, 16)) return fail(DIT_EINVAL, "latent is NULL or not 16-byte aligned");
+  if (!std::isfinite(sigma) || !std::isfinite(sigma_next) || !std::isfinite(guidance))
+    return fail(DIT_EINVAL, "sigma, sigma_next and guidance must be finite");
+  if (!workspace || !aligned(workspace, 256)) return fail(DIT_EINVAL, "workspace is NULL or not 256-byte aligned");
+  const StepLayout L = step_layout(desc);
+  if (workspace_bytes < L.total)
+    return fail(DIT_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, L.total);
+
+  dit_block_desc bd = desc->block;
+  bd.mod_stride = 0;  // one modulation vector per step, shared by every batch row
+  const int B = bd.attn.batch, nv = bd.attn.n_vis;
+  const int64_t N = static_cast<int64_t>(nv) + bd.attn.n_txt;
+  const int D = bd.hidden, C = desc->latent_channels, Fq = desc->freq_dim;
+  const int Bl = desc->cfg ? 1 : B;
+  if (overlap(latent, static_cast<size_t>(Bl) * nv * C * 4, workspace, L.total))
+    return fail(DIT_EINVAL, "latent overlaps the workspace");
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* feat = reinterpret_cast<uint16_t*>(ws + L.feat);
+  uint16_t* cbuf = reinterpret_cast<uint16_t*>(ws + L.c);
+  uint16_t* sbuf = reinterpret_cast<uint16_t*>(ws + L.s);
+  uint16_t* mod = reinterpret_cast<uint16_t*>(ws + L.mod);
+  uint16_t* fin = reinterpret_cast<uint16_t*>(ws + L.fin);
+  uint16_t* lat = reinterpret_cast<uint16_t*>(ws + L.lat);
+  float* x = reinterpret_cast<float*>(ws + L.x);
+  uint16_t* hf = reinterpret_cast<uint16_t*>(ws + L.hf);
+  uint16_t* v = reinterpret_cast<uint16_t*>(ws + L.v);
+  char* blk = ws + L.blk;
+
+#define DIT_TRY(expr, what)                            \
+  do {                                                 \
+    const hipError_t e_ = (expr);                      \
+    if (e_ != hipSuccess) return hip_status(e_, what); \
+  } while (0)
+
+  // timestep conditioning: f -> c = SiLU(f W1 + b1) -> s = SiLU(c W2 + b2)
+  DIT_TRY(dit::launch_timestep_features(nullptr, sigma, 1, Fq, desc->t_scale, feat, stream), "step: timestep");
+  DIT_TRY(dit::launch_gemm(gemm(feat, Fq, w->t_w1, w->t_b1, 1, D, Fq, cbuf, D), DIT_EPI_SILU_BF16, stream),
+          "step: t-mlp 1");
+  DIT_TRY(dit::launch_gemm(gemm(cbuf, D, w->t_w2, w->t_b2, 1, D, D, sbuf, D), DIT_EPI_SILU_BF16, stream),
+          "step: t-mlp 2");
+  // tokens: projected latent rows, then the text rows of each batch row
+  DIT_TRY(dit::launch_cast_f32_bf16(latent, C, static_cast<int64_t>(Bl) * nv, C, lat, C, stream),
+          "step: latent cast");
+  {
+    dit::GemmParams g = gemm(lat, C, w->in_w, w->in_b, static_cast<int64_t>(B) * nv, D, C, x, D);
+    g.group_rows = nv;
+    g.a_group_stride = desc->cfg ? 0 : static_cast<int64_t>(nv) * C;
+    g.c_group_stride = N * D;
+    DIT_TRY(dit::launch_gemm(g, DIT_EPI_F32, stream), "step: input projection");
+  }
+  for (int b = 0; b < B; ++b)
+    DIT_TRY(dit::launch_cast_bf16_f32(w->text + static_cast<int64_t>(b) * bd.attn.n_txt * D, D,
+                                      bd.attn.n_txt, D, x + (b * N + nv) * D, D, stream),
+            "step: text rows");
+  // the block stack
+  for (int l = 0; l < desc->depth; ++l) {
+    DIT_TRY(dit::launch_gemm(gemm(sbuf, D, w->mod_w[l], w->mod_b[l], 1, 6 * D, D, mod, 6 * D),
+                             DIT_EPI_BF16, stream),
+            "step: modulation");
+    const char* what = nullptr;
+    const hipError_t e = block_launch(&bd, &w->blocks[l], mod, 0, x, blk, stream, &what);
+    if (e != hipSuccess) return hip_status(e, what);
+  }
+  // final adaLN and projection of the visual rows to the latent channels
+  DIT_TRY(dit::launch_gemm(gemm(sbuf, D, w->fin_w, w->fin_b, 1, 2 * D, D, fin, 2 * D), DIT_EPI_BF16, stream),
+          "step: final modulation");
+  DIT_TRY(dit::launch_adaln(x, B * N, D, N, fin, fin + D, 0, bd.ln_eps, hf, stream), "step: final adaln");
+  {
+    dit::GemmParams g = gemm(hf, D, w->out_w, w->out_b, static_cast<int64_t>(B) * nv, C, D, v, C);
+    g.group_rows = nv;
+    g.a_group_stride = N * D;
+    g.c_group_stride = static_cast<int64_t>(nv) * C;
+    DIT_TRY(dit::launch_gemm(g, DIT_EPI_BF16, stream), "step: output projection");
+  }
+  // guidance + Euler on the fp32 latent
+  const int64_t n_lat = static_cast<int64_t>(nv) * C;
+  if (desc->cfg)
+    DIT_TRY(dit::launch_euler(latent, v, v + n_lat, n_lat, guidance, sigma_next - sigma, stream), "step: euler");
+  else
+    DIT_TRY(dit::launch_euler(latent, v, nullptr, static_cast<int64_t>(B) * n_lat, 1.f, sigma_next - sigma, stream),
+            "step: euler");
+#undef DIT_TRY
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal launchers of the gfx950 kernels (host side).  Arguments are
+// already validated by the C ABI layer in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+struct GemmParams {
+  const uint16_t* a;
+  int64_t lda;
+  const uint16_t* w;
+  const uint16_t* bias;
+  int64_t m;
+  int n, k;
+  void* out;
+  int64_t ldc;
+  const uint16_t* gate;
+  int64_t gate_stride, gate_rows;
+  int64_t group_rows, a_group_stride, c_group_stride;
+};
+hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s);
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t qkv_stride;
+  uint16_t* out;
+  int64_t out_stride;
+  float* lse;
+  int n_tok, heads, head_dim, batch;
+  int n_valid[8];  // n_vis + txt_valid[b]
+  float scale_log2;  // softmax scale * log2(e)
+};
+hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+
+hipError_t launch_adaln(const float* x, int64_t rows, int hidden, int64_t rows_per_batch,
+                        const uint16_t* shift, const uint16_t* scale, int64_t mod_stride,
+                        float eps, uint16_t* out, hipStream_t s);
+
+struct RopeParams {
+  uint16_t* qkv;
+  int64_t row_stride;
+  const uint16_t* g_q;
+  const uint16_t* g_k;
+  int64_t rows;
+  int n_tok, n_vis, hidden, head_dim;
+  int grid_h, grid_w;
+  int rope_t, rope_h, rope_w;
+  float theta, eps;
+};
+hipError_t launch_qk_rmsnorm_rope(const RopeParams& p, hipStream_t s);
+hipError_t launch_positions(const RopeParams& p, int32_t* out, hipStream_t s);
+
+hipError_t launch_euler(float* x, const uint16_t* vc, const uint16_t* vu, int64_t n, float g,
+                        float dt, hipStream_t s);
+hipError_t launch_timestep_features(const float* sigma, float sigma0, int n, int dim,
+                                    float t_scale, uint16_t* out, hipStream_t s);
+hipError_t launch_cast_f32_bf16(const float* in, int64_t ld_in, int64_t rows, int cols,
+                                uint16_t* out, int64_t ld_out, hipStream_t s);
+hipError_t launch_cast_bf16_f32(const uint16_t* in, int64_t ld_in, int64_t rows, int cols,
+                                float* out, int64_t ld_out, hipStream_t s);
+
+}  // namespace dit

@@ -1,0 +1,296 @@
+/*
+ * dit.h -- C ABI of the MI355X (gfx950) DiT denoiser hot path.
+ *
+ * One denoising step, as the pages state it: the denoiser takes the current
+ * latent, the timestep and the text conditioning and predicts a velocity; the
+ * sampler turns that velocity into a less noisy latent ("Difflet" paper,
+ * section 1 Introduction and section 3 Model Pipelines).  Per-request
+ * variation reaches the device only as a small runtime value -- the number of
+ * valid text keys -- never as a mask ("Difflet", section 1 and section 4.2
+ * Representing Attention Mask).
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer unless stated otherwise; every
+ *    descriptor/struct pointer is a HOST pointer, read during the call only.
+ *  - bf16 tensors are passed as uint16_t bit patterns (bfloat16, the top half
+ *    of an IEEE binary32).  All tensors are row-major; strides are counted in
+ *    elements, not bytes.
+ *  - Ownership: the caller allocates and frees every buffer, workspace
+ *    included.  The library allocates nothing and keeps no per-call state.
+ *  - Asynchrony: every call only enqueues kernels on `stream` (0 = the null
+ *    stream) and returns; results are ready when the stream reaches them.
+ *  - Errors: arguments are checked on the host before anything is enqueued.
+ *    A call that returns anything but DIT_OK has enqueued nothing (no partial
+ *    work).  dit_last_error() then holds a thread-local message.  A failed
+ *    launch returns DIT_EHIP.
+ *  - Determinism: no atomics and no data-dependent reduction order; equal
+ *    inputs give bitwise-equal outputs.
+ *  - Unsupported layouts fail here, at the boundary, and are never silently
+ *    rewritten ("Difflet Engineering Report", Backend operation boundary).
+ */
+#ifndef DIT_H_
+#define DIT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dit_status {
+  DIT_OK = 0,
+  DIT_EINVAL = 1,       /* bad argument: null pointer, shape, range, alias    */
+  DIT_EUNSUPPORTED = 2, /* well-formed but outside what the kernels implement */
+  DIT_EWORKSPACE = 3,   /* workspace smaller than dit_block_workspace_bytes() */
+  DIT_EHIP = 4          /* a HIP launch or runtime call failed                */
+} dit_status;
+
+#define DIT_MAX_BATCH 8
+
+/* Static description of a joint-attention call.
+ * Token order of every batch row is [visual (n_vis); text (n_txt)].  Text
+ * padding sits after the valid text tokens, so the valid keys of row b are the
+ * single interval [0, n_vis + txt_valid[b]) ("Difflet", section 4.2
+ * Representing Attention Mask; "Difflet Engineering Report", Attention CTE
+ * routing and mask representation).
+ *   batch      1 .. DIT_MAX_BATCH
+ *   n_vis      >= 0 visual tokens; n_txt >= 0 text slots; n_vis + n_txt >= 1
+ *   heads      >= 1
+ *   head_dim   64 or 128
+ *   txt_valid  host values in [0, n_txt] (entries past `batch` are ignored);
+ *              n_vis + txt_valid[b] must be >= 1 so no row is empty. */
+typedef struct dit_attn_desc {
+  int32_t batch, n_vis, n_txt, heads, head_dim;
+  int32_t txt_valid[DIT_MAX_BATCH];
+} dit_attn_desc;
+
+/* Joint attention ("Difflet", section 4: one softmax over the visual and text
+ * keys of each query; section 4.2: padded text keys excluded by the interval
+ * bound, fully padded key tiles never visited).
+ *
+ * For every batch row b, head h and query token i (all N = n_vis + n_txt
+ * rows, padded text rows included):
+ *   o[b,i,h,:] = sum_{j < n_vis+txt_valid[b]} softmax_j(scale * q.k_j) v_j
+ *
+ *   q, k, v  bf16, element [b, i, h, e] at  ptr + (b*N + i)*qkv_row_stride
+ *            + h*head_dim + e   (e.g. three column blocks of one [B,N,3*H*d]
+ *            buffer with qkv_row_stride = 3*H*d).  Must be 16-byte aligned
+ *            and qkv_row_stride a multiple of 8.
+ *   out      bf16 [b, i, h, e] at  out + (b*N + i)*out_row_stride + h*head_dim
+ *            + e;  out_row_stride >= heads*head_dim, multiple of 8.  Must not
+ *            overlap q, k or v.
+ *   lse      nullable; fp32 [batch, heads, N]: natural-log softmax
+ *            denominator of each row (max included), for merging partials.
+ *   softmax_scale  0 -> 1/sqrt(head_dim).
+ * Scores are accumulated in fp32 from bf16 inputs (MFMA), softmax statistics
+ * are fp32, probabilities are rounded to bf16 for the value product. */
+dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q,
+                               const uint16_t* k, const uint16_t* v,
+                               int64_t qkv_row_stride, uint16_t* out,
+                               int64_t out_row_stride, float* lse,
+                               float softmax_scale, hipStream_t stream);
+
+/* Linear layer epilogues (the GEMM of "ChunkFlow" Appendix B equations (13)
+ * and (16), with the work around it fused into the store). */
+typedef enum dit_epilogue {
+  DIT_EPI_BF16 = 0,        /* out(bf16) = acc + bias                         */
+  DIT_EPI_GELU_BF16 = 1,   /* out(bf16) = GELU_erf(acc + bias)               */
+  DIT_EPI_SILU_BF16 = 2,   /* out(bf16) = SiLU(acc + bias)                   */
+  DIT_EPI_F32 = 3,         /* out(fp32) = acc + bias                         */
+  DIT_EPI_GATED_RES_F32 = 4 /* out(fp32) += gate[g,:] * (acc + bias)         */
+} dit_epilogue;
+
+/* y = A W^T + bias with an epilogue.
+ *   a     bf16 [m, k]: row r at a + (r / group_rows)*a_group_stride
+ *         + (r % group_rows)*lda.  With group_rows == 0 rows are a + r*lda.
+ *   w     bf16 [n, k], contiguous (k contiguous): PyTorch Linear layout.
+ *   bias  bf16 [n] or NULL.
+ *   out   row r at out + (r / group_rows)*c_group_stride + (r % group_rows)*ldc;
+ *         bf16 or fp32 by epilogue.  With DIT_EPI_GATED_RES_F32 `out` is read
+ *         and written (the residual stream); otherwise it must not overlap a.
+ *   gate  bf16, DIT_EPI_GATED_RES_F32 only: row r uses gate + (r / gate_rows)
+ *         * gate_stride (gate_rows >= 1).
+ * Requires k % 64 == 0 (DIT_EUNSUPPORTED otherwise), lda/ldc/strides multiples
+ * of 8, pointers 16-byte aligned.  m, n >= 1 (m == 0 is a no-op). */
+typedef struct dit_linear_args {
+  const uint16_t* a;
+  int64_t lda;
+  const uint16_t* w;
+  const uint16_t* bias;
+  int64_t m;
+  int32_t n, k;
+  int32_t epilogue;
+  void* out;
+  int64_t ldc;
+  const uint16_t* gate;
+  int64_t gate_stride, gate_rows;
+  int64_t group_rows, a_group_stride, c_group_stride;
+} dit_linear_args;
+
+dit_status dit_linear(const dit_linear_args* args, hipStream_t stream);
+
+/* Adaptive LayerNorm ("Difflet Engineering Report", Terms used in this
+ * report: AdaLN): per row r of x (fp32 [rows, hidden], row stride `hidden`)
+ *   out[r,:] = (x - mean) / sqrt(var + eps) * (1 + scale[b,:]) + shift[b,:]
+ * with biased variance, no learned affine, b = r / rows_per_batch, and
+ * shift/scale bf16 rows at shift + b*mod_stride, scale + b*mod_stride
+ * (mod_stride may be 0 to share one vector).  out is bf16 [rows, hidden].
+ * hidden % 8 == 0 and hidden <= 16384. */
+dit_status dit_adaln_modulate(const float* x, int64_t rows, int32_t hidden,
+                              int64_t rows_per_batch, const uint16_t* shift,
+                              const uint16_t* scale, int64_t mod_stride,
+                              float eps, uint16_t* out, hipStream_t stream);
+
+/* Q/K RMSNorm over the full hidden width followed by axial RoPE, in place
+ * ("Difflet Engineering Report", Wan attention head sharding and global RMS:
+ * one sum of squares over the whole projection).  For every token row r of
+ * qkv (bf16, row stride `row_stride`, q at column 0, k at column `hidden`):
+ *   q <- RoPE(q / sqrt(mean(q^2) + eps) * g_q),  k likewise with g_k.
+ * RoPE: head_dim splits into [rope_t | rope_h | rope_w] dims; pair (2j, 2j+1)
+ * of axis a turns by pos_a * theta^(-2j / rope_a).  Token i of a batch row
+ * (i = r mod (n_vis + n_txt)) is visual when i < n_vis = grid_t*grid_h*grid_w,
+ * at t = i / (grid_h*grid_w), h = (i / grid_w) % grid_h, w = i % grid_w;
+ * text tokens sit at (0,0,0), i.e. are not rotated.  Descriptor fields used:
+ * attn.{batch,n_vis,n_txt,heads,head_dim}, hidden, grid_*, rope_*,
+ * rope_theta, rms_eps. */
+typedef struct dit_block_desc {
+  dit_attn_desc attn;
+  int32_t hidden;  /* == heads * head_dim, multiple of 64 */
+  int32_t mlp;     /* MLP width, multiple of 64            */
+  int32_t grid_t, grid_h, grid_w; /* n_vis == grid_t * grid_h * grid_w     */
+  int32_t rope_t, rope_h, rope_w; /* even, rope_t+rope_h+rope_w == head_dim */
+  float rope_theta, ln_eps, rms_eps;
+  int64_t mod_stride; /* elements between batch rows of `mod`; 0 = shared */
+} dit_block_desc;
+
+dit_status dit_qk_rmsnorm_rope(const dit_block_desc* desc, uint16_t* qkv,
+                               int64_t row_stride, const uint16_t* g_q,
+                               const uint16_t* g_k, hipStream_t stream);
+
+/* Weights of one block, bf16, [out, in] with `in` contiguous. */
+typedef struct dit_block_weights {
+  const uint16_t *w_qkv, *b_qkv; /* [3D, D], [3D] : q, k, v column blocks */
+  const uint16_t *g_q, *g_k;     /* [D] RMSNorm gains                     */
+  const uint16_t *w_o, *b_o;     /* [D, D], [D]                           */
+  const uint16_t *w_up, *b_up;   /* [F, D], [F]                           */
+  const uint16_t *w_dn, *b_dn;   /* [D, F], [D]                           */
+} dit_block_weights;
+
+/* Bytes of device workspace dit_block_forward needs for `desc` (0 on a bad
+ * descriptor). */
+size_t dit_block_workspace_bytes(const dit_block_desc* desc);
+
+/* One DiT block, in place on the residual stream x (fp32 [B, N, D], N =
+ * n_vis + n_txt, visual tokens first):
+ *   h  = adaLN(x; shift1, scale1)
+ *   q,k,v = h W_qkv^T + b_qkv;  q,k <- RoPE(RMSNorm_D(.) * g)
+ *   o  = joint_attention(q, k, v; n_vis + txt_valid[b])
+ *   x  = x + gate1 * (o W_o^T + b_o)
+ *   h2 = adaLN(x; shift2, scale2)
+ *   x  = x + gate2 * (GELU(h2 W_up^T + b_up) W_dn^T + b_dn)
+ * mod: bf16 [B, 6, D] = (shift1, scale1, gate1, shift2, scale2, gate2) per
+ * batch row, row stride desc->mod_stride (0 = one vector for all rows).
+ * Activations h, qkv, o, h2 and the MLP hidden are bf16 in `workspace`
+ * (>= dit_block_workspace_bytes(desc), 256-byte aligned); the residual stream
+ * stays fp32. */
+dit_status dit_block_forward(const dit_block_desc* desc,
+                             const dit_block_weights* w, const uint16_t* mod,
+                             float* x, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Classifier-free guidance and one flow-matching Euler step on the fp32
+ * latent ("Difflet", section 3: the scheduler turns the predicted velocity
+ * into a less noisy latent; "Difflet Engineering Report", Video output
+ * corrections: scheduler state stays fp32):
+ *   v = v_uncond + guidance * (v_cond - v_uncond)   (v = v_cond if v_uncond
+ *                                                    is NULL)
+ *   x = x + (sigma_next - sigma) * v
+ * x fp32 [n]; v_cond, v_uncond bf16 [n]; n >= 0. */
+dit_status dit_euler_step(float* x, const uint16_t* v_cond,
+                          const uint16_t* v_uncond, int64_t n, float guidance,
+                          float sigma, float sigma_next, hipStream_t stream);
+
+/* Sinusoidal timestep features: for t = t_scale * sigma[s] and
+ * f_j = 10000^(-j/(dim/2)), out[s, :] = [cos(t f), sin(t f)] (bf16 [n, dim]).
+ * sigma: fp32 device [n]; dim even, 2..4096. */
+dit_status dit_timestep_features(const float* sigma, int32_t n, int32_t dim,
+                                 float t_scale, uint16_t* out,
+                                 hipStream_t stream);
+
+/* Strided casts used around the block stack (loop glue).
+ * f32 -> bf16: out[r*ld_out + c] = bf16(in[r*ld_in + c]) for r < rows, c < cols
+ * bf16 -> f32: the reverse.  cols % 4 == 0, ld_* % 4 == 0. */
+dit_status dit_cast_f32_bf16(const float* in, int64_t ld_in, int64_t rows,
+                             int32_t cols, uint16_t* out, int64_t ld_out,
+                             hipStream_t stream);
+dit_status dit_cast_bf16_f32(const uint16_t* in, int64_t ld_in, int64_t rows,
+                             int32_t cols, float* out, int64_t ld_out,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * One denoising step of a DiT stack (loop glue + blocks + sampler).
+ *
+ * The denoiser predicts a velocity from the latent, the timestep and the text
+ * conditioning; the scheduler moves the latent to the next noise level
+ * ("Difflet", section 3; "19. Diffusion, Image, Video, and World Models",
+ * Follow the diffusion pipeline).  Steps, in order, all on `stream`:
+ *   f    = sinusoidal(t_scale * sigma, freq_dim)                (bf16 [1, F])
+ *   c    = SiLU(f W_t1^T + b_t1);  s = SiLU(c W_t2^T + b_t2)    (bf16 [1, D])
+ *   x[b, :n_vis]  = bf16(latent[lb]) W_in^T + b_in              (fp32)
+ *   x[b, n_vis:]  = text[b]                                     (fp32)
+ *   for l < depth:  mod_l = s W_mod[l]^T + b_mod[l]  (bf16 [6, D], shared by
+ *                   every batch row);  dit_block_forward(x; mod_l)
+ *   (shift, scale) = s W_fin^T + b_fin;  h = adaLN(x; shift, scale)
+ *   v[b] = h[b, :n_vis] W_out^T + b_out                         (bf16)
+ *   latent += (sigma_next - sigma) * v        (cfg == 0: each row its own
+ *             latent, lb = b), or with cfg == 1 (batch == 2, row 0
+ *             conditional, row 1 unconditional, one latent, lb = 0):
+ *   latent += (sigma_next - sigma) * (v[1] + guidance * (v[0] - v[1])).
+ * Descriptor: block is as for dit_block_forward (block.mod_stride is
+ * ignored); latent_channels % 8 == 0; freq_dim % 64 == 0.
+ * latent: fp32 [cfg ? 1 : batch, n_vis, latent_channels], updated in place.
+ * Workspace: >= dit_denoise_workspace_bytes(desc), 256-byte aligned. */
+typedef struct dit_model_desc {
+  dit_block_desc block;
+  int32_t depth;
+  int32_t latent_channels;
+  int32_t freq_dim;
+  int32_t cfg;
+  float t_scale;
+} dit_model_desc;
+
+typedef struct dit_model_weights {
+  const uint16_t *t_w1, *t_b1;       /* [D, freq_dim], [D]   */
+  const uint16_t *t_w2, *t_b2;       /* [D, D], [D]          */
+  const uint16_t *in_w, *in_b;       /* [D, C], [D]          */
+  const uint16_t *fin_w, *fin_b;     /* [2D, D], [2D]: shift then scale */
+  const uint16_t *out_w, *out_b;     /* [C, D], [C]          */
+  const uint16_t* text;              /* [batch, n_txt, D] conditioning tokens */
+  const dit_block_weights* blocks;   /* HOST array [depth] of device pointers */
+  const uint16_t* const* mod_w;      /* HOST array [depth]: device [6D, D] */
+  const uint16_t* const* mod_b;      /* HOST array [depth]: device [6D]    */
+} dit_model_weights;
+
+size_t dit_denoise_workspace_bytes(const dit_model_desc* desc);
+dit_status dit_denoise_step(const dit_model_desc* desc, const dit_model_weights* w,
+                            float* latent, float sigma, float sigma_next,
+                            float guidance, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Debug: the integer (t, h, w) position of every token of one batch row,
+ * int32 [n_vis + n_txt, 3] (device), from the same device code RoPE uses. */
+dit_status dit_debug_positions(const dit_block_desc* desc, int32_t* out,
+                               hipStream_t stream);
+
+const char* dit_status_string(dit_status s);
+const char* dit_last_error(void); /* thread-local; "" after DIT_OK */
+const char* dit_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_H_ */

@@ -33,11 +33,12 @@ from .dit import (
     sigma_schedule,
     timestep_features,
     silu,
+    denoise_step,
 )
 
 __all__ = [
     "bf16_decode", "round_bf16", "adaln_modulate", "linear", "rms_norm_full",
     "token_positions", "rope_axial", "attention_probs", "joint_attention",
     "gelu_erf", "block_forward", "cfg_combine", "euler_update", "sigma_schedule",
-    "timestep_features", "silu",
+    "timestep_features", "silu", "denoise_step",
 ]

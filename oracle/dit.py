@@ -110,23 +110,26 @@ def rope_axial(x, pos, dims, theta):
     (the pages only name RoPE)."""
     x = np.asarray(x, dtype=np.float64)
     pos = np.asarray(pos)
-    out = x.copy()
-    off = 0
+    d = x.shape[-1]
+    pairs = x.reshape(x.shape[:-1] + (d // 2, 2))  # pair j of the head: dims (2j, 2j+1)
+    out = np.empty_like(pairs)
+    p0 = 0
     for axis, d_a in enumerate(dims):
-        d_a = int(d_a)
-        if d_a == 0:
+        n_a = int(d_a) // 2
+        if n_a == 0:
             continue
-        j = np.arange(d_a // 2, dtype=np.float64)
-        inv_freq = float(theta) ** (-2.0 * j / d_a)
+        j = np.arange(n_a, dtype=np.float64)
+        inv_freq = float(theta) ** (-2.0 * j / int(d_a))
         ang = pos[:, axis].astype(np.float64)[:, None] * inv_freq[None, :]  # [N, d_a/2]
         c = np.cos(ang)[:, None, :]  # [N, 1, d_a/2] broadcast over heads
         s = np.sin(ang)[:, None, :]
-        ev = off + 2 * np.arange(d_a // 2)
-        x0 = x[..., ev]
-        x1 = x[..., ev + 1]
-        out[..., ev] = x0 * c - x1 * s
-        out[..., ev + 1] = x0 * s + x1 * c
-        off += d_a
+        x0 = pairs[..., p0:p0 + n_a, 0]
+        x1 = pairs[..., p0:p0 + n_a, 1]
+        out[..., p0:p0 + n_a, 0] = x0 * c - x1 * s
+        out[..., p0:p0 + n_a, 1] = x0 * s + x1 * c
+        p0 += n_a
+    out[..., p0:, :] = pairs[..., p0:, :]
+    out = out.reshape(x.shape)
     return out
 
 
@@ -293,3 +296,76 @@ def timestep_features(t, dim):
     f = np.exp(-math.log(10000.0) * np.arange(half, dtype=np.float64) / half)
     a = float(t) * f
     return np.concatenate([np.cos(a), np.sin(a)])
+
+
+# ----------------------------------------------------------------------------
+# one denoising step of a DiT stack
+# ----------------------------------------------------------------------------
+
+def denoise_step(model, latent, sigma, sigma_next, guidance, round_points=True, rows=None,
+                 t_scale=1000.0):
+    """One step of the denoising loop ("Difflet", section 3: the denoiser
+    predicts a velocity from the latent, the timestep and the encoder
+    outputs, the scheduler uses it to update the latent; "19. Diffusion,
+    Image, Video, and World Models", Follow the diffusion pipeline).
+
+    ``model`` provides ``shape`` (a LoopShape), the conditioning weights
+    (t_w1, t_b1, t_w2, t_b2, in_w, in_b, fin_mod_w, fin_mod_b, out_w, out_b),
+    ``text`` [B, n_txt, D], ``txt_valid`` [B] and ``layer(l)`` (block weights
+    plus mod_w, mod_b).  ``latent`` is [Bl, n_vis, C] (Bl = 1 with guidance,
+    else B).  The reading taken for the parts the pages leave open:
+
+      f = sinusoidal(t_scale * sigma); c = SiLU(f W_t1 + b_t1);
+      s = SiLU(c W_t2 + b_t2)                       (timestep conditioning)
+      tokens of row b: [bf16(latent) W_in + b_in ; text[b]]
+      per layer: mod = s W_mod + b_mod (one vector for every batch row), block
+      (shift, scale) = s W_fin + b_fin;  v = adaLN(x) W_out + b_out  (visual rows)
+      guidance: v_hat = v_uncond + g (v_cond - v_uncond)  (row 0 cond, row 1 uncond)
+      latent <- latent + (sigma_next - sigma) v_hat     (Euler, see euler_update)
+
+    With ``round_points`` every value the GPU stores in bfloat16 is rounded
+    (features, c, s, modulation vectors, the bf16 copy of the latent, block
+    intermediates, final norm output, v).  ``rows`` restricts the visual
+    tokens whose velocity and update are returned; it is only exact for a
+    single-block model (a later block needs every row of the one before).
+    Returns (new latent rows [Bl, R, C], v [B, R, C])."""
+    R_ = round_bf16 if round_points else (lambda a: a)
+    shp = model.shape
+    blk = shp.block
+    B, nv, N, D = blk.batch, blk.n_vis, blk.n_tok, blk.hidden
+    cfg = shp.cfg
+    sig32 = float(np.float32(sigma))
+    f = R_(timestep_features(float(np.float32(t_scale)) * sig32, shp.freq_dim))
+    c = R_(silu(linear(f, _dec(model.t_w1), _dec(model.t_b1))))
+    s = R_(silu(linear(c, _dec(model.t_w2), _dec(model.t_b2))))
+    lat = np.asarray(latent, dtype=np.float64)
+    xin = linear(R_(lat), _dec(model.in_w), _dec(model.in_b))  # [Bl, n_vis, D]
+    x = np.empty((B, N, D))
+    for b in range(B):
+        x[b, :nv] = xin[0 if cfg else b]
+        x[b, nv:] = _dec(model.text[b])
+    if shp.depth > 1 and rows is not None:
+        raise ValueError("row subsets are only exact for a single block")
+    sel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    for l in range(shp.depth):
+        w = model.layer(l)
+        mod = R_(linear(s, _dec(w["mod_w"]), _dec(w["mod_b"]))).reshape(6, D)
+        inp = dict(w)
+        inp["x"] = x
+        inp["mod"] = np.broadcast_to(mod, (B, 6, D))
+        inp["txt_valid"] = model.txt_valid
+        x = block_forward(inp, blk, round_points=round_points,
+                          rows=None if shp.depth > 1 else rows)
+    fin = R_(linear(s, _dec(model.fin_mod_w), _dec(model.fin_mod_b)))
+    h = R_(adaln_modulate(x, fin[:D], fin[D:], blk.ln_eps))
+    if rows is not None and shp.depth == 1:
+        keep = sel < nv
+        h = h[:, keep]
+        lat_rows = sel[keep]
+    else:
+        h = h[:, :nv]
+        lat_rows = np.arange(nv)
+    v = R_(linear(h, _dec(model.out_w), _dec(model.out_b)))  # [B, R, C]
+    v_hat = cfg_combine(v[0:1], v[1:2], guidance) if cfg else v
+    new = euler_update(lat[:, lat_rows], v_hat, sig32, float(np.float32(sigma_next)))
+    return new, v

@@ -10,6 +10,7 @@ float32, so there is no double rounding).
 import numpy as np
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+_CHUNK = 1 << 16  # elements per pass (cache-sized)
 
 
 def bf16_decode(bits) -> np.ndarray:
@@ -21,14 +22,34 @@ def bf16_decode(bits) -> np.ndarray:
 def round_bf16(x) -> np.ndarray:
     """Round fp64 values to the nearest bfloat16 value (ties to even).
 
-    Write |x| = m * 2**e with m in [0.5, 1).  A normal bfloat16 keeps 8
-    significant bits, so the spacing there is 2**(e - 8); below the smallest
-    normal (2**-126, i.e. e < -125) the spacing stays at 2**-133.  Scaling by a
-    power of two is exact, and ``numpy.round`` rounds halves to even.
+    A normal bfloat16 keeps the sign, the exponent and the top 7 of fp64's 52
+    stored mantissa bits.  Round to nearest even on the fp64 bit pattern:
+    add 2**44 - 1 plus the lowest kept bit, then clear the 45 dropped bits (a
+    carry out of the mantissa correctly bumps the exponent).  Below the
+    smallest normal bfloat16 (2**-126) the spacing stays at 2**-133: there the
+    value is scaled by a power of two (exact) and rounded with numpy.round,
+    which rounds halves to even.  Results above the largest bfloat16 become
+    infinities; NaN and infinities pass through.
     """
-    x = np.asarray(x, dtype=np.float64)
-    m, e = np.frexp(x)
-    q = np.maximum(e, -125) - 8
-    r = np.ldexp(np.round(np.ldexp(x, -q)), q)
-    r = np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, x), r)
-    return np.where(np.isfinite(x), r, x)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    xf, of = x.reshape(-1), out.reshape(-1)
+    keep = np.uint64(45)
+    bias = np.uint64((1 << 44) - 1)
+    for s in range(0, xf.size, _CHUNK):
+        xc = xf[s:s + _CHUNK]
+        t = xc.view(np.uint64) >> keep
+        t &= np.uint64(1)
+        t += bias
+        t += xc.view(np.uint64)
+        t >>= keep
+        t <<= keep
+        r = t.view(np.float64)
+        a = np.abs(xc)
+        if not (np.all(a >= 2.0 ** -126) and np.all(a <= _BF16_MAX)):  # rare: tiny, huge, inf, nan
+            small = a < 2.0 ** -126
+            r = np.where(small, np.ldexp(np.round(np.ldexp(xc, 133)), -133), r)
+            r = np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, xc), r)
+            r = np.where(np.isfinite(xc), r, xc)
+        of[s:s + _CHUNK] = r
+    return out

@@ -17,6 +17,7 @@ from .gen import (
     attention_inputs,
     loop_inputs,
     seed_sequence,
+    normal_bf16,
 )
 
 __all__ = [
@@ -31,4 +32,5 @@ __all__ = [
     "attention_inputs",
     "loop_inputs",
     "seed_sequence",
+    "normal_bf16",
 ]

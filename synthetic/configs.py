@@ -86,6 +86,7 @@ class LoopShape:
     latent_channels: int  # per visual token after patchify (16 ch x 2 x 2)
     freq_dim: int = 256  # sinusoidal timestep features
     seed: int = 0
+    cfg: bool = True  # batch rows (conditional, unconditional) share one latent
 
 
 C1 = BlockShape("c1_tiny", batch=1, grid=(1, 16, 16), n_txt=32, heads=4, head_dim=64,
@@ -101,6 +102,20 @@ C5 = LoopShape("c5_image_loop", block=BlockShape(
     "c5_block", batch=2, grid=(1, 64, 64), n_txt=512, heads=24, head_dim=128, mlp=12288,
     rope=(0, 64, 64), txt_valid=("uniform", 77, 512), seed=5),
     depth=24, steps=30, guidance=5.0, latent_channels=64, seed=5)
+
+# One denoising step of a single-block video DiT at the c3 shape (no guidance):
+# the step the benchmark times.
+C3_STEP = LoopShape("c3_step", block=C3, depth=1, steps=30, guidance=1.0, latent_channels=64,
+                    seed=3, cfg=False)
+# c5 with a single block: row subsets stay exact, so the full-size step can be
+# checked on sampled visual rows.
+C5_DEPTH1 = LoopShape("c5_depth1", block=C5.block, depth=1, steps=30, guidance=5.0,
+                      latent_channels=64, seed=5)
+# A small stack the oracle can run through all 30 steps.
+TINY_LOOP = LoopShape("tiny_loop", block=BlockShape(
+    "tiny_loop_block", batch=2, grid=(1, 8, 8), n_txt=24, heads=2, head_dim=64, mlp=256,
+    rope=(0, 32, 32), txt_valid=("fixed", (10, 3)), seed=6),
+    depth=2, steps=30, guidance=5.0, latent_channels=64, seed=6)
 
 CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
 

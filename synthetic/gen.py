@@ -63,6 +63,11 @@ def _normal_bf16(ss: np.random.SeedSequence, shape, std: float = 1.0,
     return out.reshape(shape)
 
 
+def normal_bf16(seed: int, shape, std: float = 1.0, mean: float = 0.0) -> np.ndarray:
+    """A seeded N(mean, std^2) tensor of bf16 bit patterns (one stream per seed)."""
+    return _normal_bf16(seed_sequence(seed), shape, std, mean)
+
+
 def _valid_lengths(ss: np.random.SeedSequence, spec: tuple, batch: int,
                    n_txt: int) -> np.ndarray:
     kind = spec[0]

@@ -1,0 +1,133 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+symbol include/dit.h declares, and rejects bad arguments on the host with the
+documented status before anything is launched (the pointers passed here are
+never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import diffusion_transformer_denoising_dit_amd as D
+from synthetic import configs as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20  # a 256-byte-aligned address that is never dereferenced
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "dit.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dit_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = D.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 14
+    for name in declared:
+        assert hasattr(L, name), f"libdit.so does not export {name}"
+    assert sorted(declared) == sorted(D.EXPORTED)
+    assert "gfx950" in D.dit_version()
+
+
+def test_status_strings():
+    L = D.lib()
+    for code, name in D._lib.STATUS.items():
+        assert L.dit_status_string(code).decode() == name
+
+
+def _expect(status, fn, *args, **kw):
+    with pytest.raises(D.DitError) as e:
+        fn(*args, **kw)
+    assert e.value.status_name == status, str(e.value)
+    return str(e.value)
+
+
+def _attn(batch=1, n_vis=64, n_txt=16, heads=2, head_dim=64, valid=(4,)):
+    return D.attn_desc(batch, n_vis, n_txt, heads, head_dim, list(valid))
+
+
+def test_attention_argument_errors():
+    f = D.dit_joint_attention
+    hd = 128
+    _expect("DIT_EINVAL", f, _attn(batch=0), FAKE, FAKE, FAKE, hd, FAKE * 2, hd, stream=0)
+    _expect("DIT_EINVAL", f, _attn(batch=9, valid=[0] * 8), FAKE, FAKE, FAKE, hd, FAKE * 2, hd, stream=0)
+    _expect("DIT_EUNSUPPORTED", f, _attn(head_dim=96), FAKE, FAKE, FAKE, 192, FAKE * 2, 192, stream=0)
+    _expect("DIT_EINVAL", f, _attn(valid=(17,)), FAKE, FAKE, FAKE, hd, FAKE * 2, hd, stream=0)
+    _expect("DIT_EINVAL", f, _attn(valid=(-1,)), FAKE, FAKE, FAKE, hd, FAKE * 2, hd, stream=0)
+    _expect("DIT_EINVAL", f, _attn(n_vis=0, valid=(0,)), FAKE, FAKE, FAKE, hd, FAKE * 2, hd, stream=0)
+    _expect("DIT_EINVAL", f, _attn(), None, FAKE, FAKE, hd, FAKE * 2, hd, stream=0)
+    _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE, FAKE, hd - 8, FAKE * 2, hd, stream=0)
+    _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE, FAKE, hd + 4, FAKE * 2, hd, stream=0)
+    _expect("DIT_EINVAL", f, _attn(), FAKE + 2, FAKE, FAKE, hd, FAKE * 2, hd, stream=0)
+    # out aliasing q
+    _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE * 4, FAKE * 4, hd, FAKE + 256, hd, stream=0)
+    _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE, FAKE, hd, FAKE * 2, hd, softmax_scale=-1.0, stream=0)
+
+
+def test_linear_argument_errors():
+    f = D.dit_linear
+    _expect("DIT_EUNSUPPORTED", f, FAKE, 96, FAKE * 2, None, 4, 8, 96, D.EPI_BF16, FAKE * 4, 8, stream=0)
+    _expect("DIT_EUNSUPPORTED", f, FAKE, 64, FAKE * 2, None, 4, 12, 64, D.EPI_BF16, FAKE * 4, 16, stream=0)
+    _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, 9, FAKE * 4, 8, stream=0)
+    _expect("DIT_EINVAL", f, FAKE, 32, FAKE * 2, None, 4, 8, 64, D.EPI_BF16, FAKE * 4, 8, stream=0)
+    _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, D.EPI_GATED_RES_F32, FAKE * 4, 8, stream=0)
+    _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, D.EPI_BF16, FAKE + 64, 8, stream=0)
+    _expect("DIT_EINVAL", f, None, 64, FAKE * 2, None, 4, 8, 64, D.EPI_BF16, FAKE * 4, 8, stream=0)
+    # m == 0 is a no-op that succeeds without touching the GPU
+    f(FAKE, 64, FAKE * 2, None, 0, 8, 64, D.EPI_BF16, FAKE * 4, 8, stream=0)
+
+
+def _block(**over):
+    s = C.C1
+    d = D.block_desc(s, [20])
+    for k, v in over.items():
+        if k in ("batch", "n_vis", "n_txt", "heads", "head_dim"):
+            setattr(d.attn, k, v)
+        else:
+            setattr(d, k, v)
+    return d
+
+
+def test_block_descriptor_errors_and_workspace():
+    ws = D.dit_block_workspace_bytes(_block())
+    s = C.C1
+    M = s.batch * s.n_tok
+    assert ws >= M * s.hidden * 2 + M * max(3 * s.hidden, s.mlp) * 2
+    for over, status in [({"hidden": 320}, "DIT_EINVAL"), ({"mlp": 1000}, "DIT_EUNSUPPORTED"),
+                         ({"grid_w": 15}, "DIT_EINVAL"), ({"rope_h": 31}, "DIT_EINVAL"),
+                         ({"rope_h": 30}, "DIT_EINVAL"), ({"rope_theta": 0.0}, "DIT_EINVAL"),
+                         ({"mod_stride": -4}, "DIT_EINVAL")]:
+        d = _block(**over)
+        with pytest.raises(D.DitError) as e:
+            D.dit_block_workspace_bytes(d)
+        W = {n: FAKE for n in ("w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "w_up", "b_up",
+                               "w_dn", "b_dn")}
+        _expect(status, D.dit_block_forward, d, W, FAKE, FAKE * 64, FAKE * 1024, 1 << 30, stream=0)
+    W = {n: FAKE for n in ("w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "w_up", "b_up", "w_dn",
+                           "b_dn")}
+    _expect("DIT_EWORKSPACE", D.dit_block_forward, _block(), W, FAKE, FAKE * 64, FAKE * 1024, ws - 1,
+            stream=0)
+    W2 = dict(W, w_o=None)
+    _expect("DIT_EINVAL", D.dit_block_forward, _block(), W2, FAKE, FAKE * 64, FAKE * 1024, ws, stream=0)
+    # x overlapping the workspace
+    _expect("DIT_EINVAL", D.dit_block_forward, _block(), W, FAKE, FAKE * 64, FAKE * 64, ws, stream=0)
+
+
+def test_other_entry_points_argument_errors():
+    _expect("DIT_EINVAL", D.dit_euler_step, None, FAKE, None, 16, 5.0, 1.0, 0.9, stream=0)
+    _expect("DIT_EINVAL", D.dit_euler_step, FAKE + 4, FAKE * 2, None, 16, 5.0, 1.0, 0.9, stream=0)
+    _expect("DIT_EINVAL", D.dit_euler_step, FAKE, FAKE * 2, None, 16, float("nan"), 1.0, 0.9, stream=0)
+    _expect("DIT_EINVAL", D.dit_euler_step, FAKE, FAKE + 8, None, 16, 5.0, 1.0, 0.9, stream=0)
+    D.dit_euler_step(FAKE, FAKE * 2, None, 0, 5.0, 1.0, 0.9, stream=0)  # n == 0: no-op
+    _expect("DIT_EUNSUPPORTED", D.dit_adaln_modulate, FAKE, 4, 100, 4, FAKE, FAKE, 0, 1e-6, FAKE * 2,
+            stream=0)
+    _expect("DIT_EINVAL", D.dit_adaln_modulate, FAKE, 4, 256, 0, FAKE, FAKE, 0, 1e-6, FAKE * 2, stream=0)
+    _expect("DIT_EINVAL", D.dit_adaln_modulate, FAKE, 4, 256, 4, FAKE, FAKE, 0, 1e-6, FAKE + 512,
+            stream=0)
+    _expect("DIT_EINVAL", D.dit_timestep_features, FAKE, 30, 255, 1000.0, FAKE * 2, stream=0)
+    _expect("DIT_EINVAL", D.dit_cast_f32_bf16, FAKE, 6, 4, 6, FAKE * 2, 8, stream=0)
+    _expect("DIT_EINVAL", D.dit_qk_rmsnorm_rope, _block(), FAKE, 100, FAKE, FAKE, stream=0)
+    assert D.lib().dit_last_error().decode() != ""

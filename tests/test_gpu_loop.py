@@ -1,0 +1,189 @@
+"""GPU parity of dit_denoise_step (glue + block stack + guidance + Euler)
+against the oracle's denoising step, on the same seeded inputs.
+
+* tiny stack (2 blocks), all 30 steps free-running on both sides;
+* c5 shape with one block: one step at sigma indices 0, 15 and 29, compared
+  on sampled visual rows (exact for a single block);
+* c5 at full depth (24 blocks, 30 steps): with every gate zero each block is
+  exactly the identity, so the whole trajectory equals the oracle's glue-only
+  loop -- checked on every latent element; and one step with a single live
+  layer (the last) equals the oracle's one-block step on sampled rows.
+Composite outputs use: rel-L2 <= 5e-3 and max-abs <= max(2e-2, the oracle's
+own bf16-storage spread on the same elements)."""
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_denoising_dit_amd as D
+import oracle as O
+from synthetic import configs as C
+from synthetic import gen as G
+from tests.gpu_util import assert_composite, dev_bf16, host
+from tests.sampling import sample_rows
+
+pytestmark = pytest.mark.gpu
+
+BLOCK_NAMES = ("w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "w_up", "b_up", "w_dn", "b_dn")
+
+
+def zero_gates(w, D_):
+    w = dict(w)
+    for k in ("mod_w", "mod_b"):
+        w[k] = w[k].copy()
+        w[k][2 * D_:3 * D_] = 0
+        w[k][5 * D_:6 * D_] = 0
+    return w
+
+
+class Model:
+    """Seeded model with per-layer weights chosen by ``plan``: layer l uses
+    the weights of seed layer plan[l] (so layers may share device buffers),
+    with gates zeroed where dead[l]."""
+
+    def __init__(self, shape, plan=None, dead=None):
+        self.shape = shape
+        self.inp = G.loop_inputs(shape)
+        for n in ("t_w1", "t_b1", "t_w2", "t_b2", "in_w", "in_b", "fin_mod_w", "fin_mod_b",
+                  "out_w", "out_b", "text", "txt_valid"):
+            setattr(self, n, getattr(self.inp, n))
+        self.plan = list(range(shape.depth)) if plan is None else list(plan)
+        self.dead = [False] * shape.depth if dead is None else list(dead)
+        self._cache = {}
+
+    def layer(self, l):
+        key = (self.plan[l], self.dead[l])
+        if key not in self._cache:
+            w = self.inp.layer(self.plan[l])
+            self._cache[key] = zero_gates(w, self.shape.block.hidden) if self.dead[l] else w
+        return self._cache[key]
+
+    def upload(self):
+        glue = {"t_w1": self.t_w1, "t_b1": self.t_b1, "t_w2": self.t_w2, "t_b2": self.t_b2,
+                "in_w": self.in_w, "in_b": self.in_b, "fin_w": self.fin_mod_w,
+                "fin_b": self.fin_mod_b, "out_w": self.out_w, "out_b": self.out_b,
+                "text": self.text}
+        self.dev_glue = {k: dev_bf16(v) for k, v in glue.items()}
+        dev_layers = {}
+        blocks, mw, mb = [], [], []
+        for l in range(self.shape.depth):
+            key = (self.plan[l], self.dead[l])
+            if key not in dev_layers:
+                dev_layers[key] = {k: dev_bf16(v) for k, v in self.layer(l).items()}
+            d = dev_layers[key]
+            blocks.append({n: d[n] for n in BLOCK_NAMES})
+            mw.append(d["mod_w"])
+            mb.append(d["mod_b"])
+        self.dev_layers = dev_layers
+        self.weights = D.model_weights(self.dev_glue, blocks, mw, mb)
+        self.desc = D.model_desc(self.shape, self.txt_valid)
+        self.ws_bytes = D.dit_denoise_workspace_bytes(self.desc)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device="cuda")
+        return self
+
+    def gpu_step(self, latent, sigma, sigma_next):
+        D.dit_denoise_step(self.desc, self.weights, latent, sigma, sigma_next, self.shape.guidance,
+                           self.ws, self.ws_bytes)
+
+
+def _latent(shape, seed):
+    Bl = 1 if shape.cfg else shape.block.batch
+    return G.normal_bf16(seed, (Bl, shape.block.n_vis, shape.latent_channels))
+
+
+def test_tiny_loop_free_running_30_steps():
+    shape = C.TINY_LOOP
+    m = Model(shape).upload()
+    lat0 = O.bf16_decode(_latent(shape, 70))
+    x = torch.from_numpy(lat0.astype(np.float32)).cuda()
+    sig = O.sigma_schedule(shape.steps)
+    for i in range(shape.steps):
+        m.gpu_step(x, float(sig[i]), float(sig[i + 1]))
+    torch.cuda.synchronize()
+    ref, exact = lat0, lat0
+    for i in range(shape.steps):
+        ref, _ = O.denoise_step(m, ref, sig[i], sig[i + 1], shape.guidance)
+        exact, _ = O.denoise_step(m, exact, sig[i], sig[i + 1], shape.guidance, round_points=False)
+    assert_composite(host(x), ref, exact, "tiny loop, 30 steps")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("step", [0, 15, 29])
+def test_c5_one_block_step_sampled(step):
+    shape = C.C5_DEPTH1
+    m = Model(shape).upload()
+    lat0 = O.bf16_decode(_latent(shape, 80 + step))
+    sig = O.sigma_schedule(shape.steps)
+    x = torch.from_numpy(lat0.astype(np.float32)).cuda()
+    m.gpu_step(x, float(sig[step]), float(sig[step + 1]))
+    torch.cuda.synchronize()
+    b = shape.block
+    rows = sample_rows(b.n_vis, b.n_txt, m.txt_valid, n_random=48, seed=step)
+    vis = rows[rows < b.n_vis]
+    ref, _ = O.denoise_step(m, lat0, sig[step], sig[step + 1], shape.guidance, rows=rows)
+    exact, _ = O.denoise_step(m, lat0, sig[step], sig[step + 1], shape.guidance, rows=rows,
+                              round_points=False)
+    assert_composite(host(x)[:, vis], ref, exact, f"c5 one-block step {step} (sampled)")
+
+
+def _c5_full(dead_all_but_last):
+    shape = C.C5
+    if dead_all_but_last:
+        plan = [0] * (shape.depth - 1) + [1]
+        dead = [True] * (shape.depth - 1) + [False]
+    else:
+        plan = [0] * shape.depth
+        dead = [True] * shape.depth
+    return Model(shape, plan, dead).upload()
+
+
+@pytest.mark.slow
+def test_c5_full_depth_zero_gates_trajectory():
+    m = _c5_full(False)
+    shape = m.shape
+    lat0 = O.bf16_decode(_latent(shape, 90))
+    sig = O.sigma_schedule(shape.steps)
+    x = torch.from_numpy(lat0.astype(np.float32)).cuda()
+    m.gpu_step(x, float(sig[0]), float(sig[1]))  # warm-up, then restart from lat0
+    x.copy_(torch.from_numpy(lat0.astype(np.float32)))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(shape.steps):
+        m.gpu_step(x, float(sig[i]), float(sig[i + 1]))
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / shape.steps
+    print(f"c5 (24 blocks, CFG batch 2): {dt * 1e3:.2f} ms/step over {shape.steps} steps", flush=True)
+    glue = Model(C.LoopShape("c5_glue", block=shape.block, depth=0, steps=shape.steps,
+                             guidance=shape.guidance, latent_channels=shape.latent_channels,
+                             seed=shape.seed))
+    ref, exact = lat0, lat0
+    for i in range(shape.steps):
+        ref, _ = O.denoise_step(glue, ref, sig[i], sig[i + 1], shape.guidance)
+        exact, _ = O.denoise_step(glue, exact, sig[i], sig[i + 1], shape.guidance, round_points=False)
+    assert_composite(host(x), ref, exact, "c5 24 blocks x 30 steps, zero gates")
+
+
+@pytest.mark.slow
+def test_c5_full_depth_last_layer_live_step():
+    m = _c5_full(True)
+    shape = m.shape
+    lat0 = O.bf16_decode(_latent(shape, 91))
+    sig = O.sigma_schedule(shape.steps)
+    x = torch.from_numpy(lat0.astype(np.float32)).cuda()
+    m.gpu_step(x, float(sig[0]), float(sig[1]))
+    x2 = torch.from_numpy(lat0.astype(np.float32)).cuda()
+    m.gpu_step(x2, float(sig[0]), float(sig[1]))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(x.cpu().numpy(), x2.cpu().numpy())  # deterministic
+    one = Model(C.LoopShape("c5_last_live", block=shape.block, depth=1, steps=shape.steps,
+                            guidance=shape.guidance, latent_channels=shape.latent_channels,
+                            seed=shape.seed), plan=[1], dead=[False])
+    b = shape.block
+    rows = sample_rows(b.n_vis, b.n_txt, m.txt_valid, n_random=48, seed=7)
+    vis = rows[rows < b.n_vis]
+    ref, _ = O.denoise_step(one, lat0, sig[0], sig[1], shape.guidance, rows=rows)
+    exact, _ = O.denoise_step(one, lat0, sig[0], sig[1], shape.guidance, rows=rows,
+                              round_points=False)
+    assert_composite(host(x)[:, vis], ref, exact, "c5 24 blocks, last layer live (sampled)")
