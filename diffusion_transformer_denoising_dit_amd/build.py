@@ -34,6 +34,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-file device flags.  attention.hip keeps its MFMA accumulators in VGPRs:
+# its softmax phase reads the scores with VALU instructions, and the AGPR form
+# would copy every accumulator register across the register files each tile.
+FILE_FLAGS = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -62,7 +70,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
     def compile_one(pair):
         src, obj = pair
-        return _run([hipcc, *COMMON_FLAGS, "-c", src, "-o", obj])
+        return _run([hipcc, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src,
+                     "-o", obj])
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         logs = list(ex.map(compile_one, zip(srcs, objs)))

@@ -117,6 +117,10 @@ dit::RopeParams rope_params(const dit_block_desc* d, uint16_t* qkv, int64_t row_
   return p;
 }
 
+// The attention kernel addresses the 64 rows of a key tile with 32-bit byte
+// offsets from the tile's first row.
+constexpr int64_t kMaxQkvRowStride = int64_t{1} << 24;
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct WsLayout {
@@ -349,6 +353,10 @@ dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q, con
   if (qkv_row_stride < hd || qkv_row_stride % 8 != 0)
     return fail(DIT_EINVAL, "qkv_row_stride %lld must be >= heads*head_dim and a multiple of 8",
                 static_cast<long long>(qkv_row_stride));
+  if (qkv_row_stride > kMaxQkvRowStride)
+    return fail(DIT_EUNSUPPORTED, "qkv_row_stride %lld above %lld (key tiles are addressed with "
+                "32-bit byte offsets)", static_cast<long long>(qkv_row_stride),
+                static_cast<long long>(kMaxQkvRowStride));
   if (out_row_stride < hd || out_row_stride % 8 != 0)
     return fail(DIT_EINVAL, "out_row_stride %lld must be >= heads*head_dim and a multiple of 8",
                 static_cast<long long>(out_row_stride));

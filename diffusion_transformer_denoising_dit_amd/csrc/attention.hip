@@ -2,227 +2,443 @@
 //
 // Each query attends to the visual and the valid text keys of its batch row
 // under one softmax ("Difflet", section 4).  Padded text keys sit after the
-// valid ones, so the valid keys are the interval [0, n_vis + L_b) and only two
-// numbers per row decide the mask ("Difflet", section 4.2 Representing
-// Attention Mask): key tiles past the bound are never visited, and only the
-// one tile that straddles it is masked.
+// valid ones, so the valid keys are the interval [0, n_vis + L_b) and one
+// integer per row decides the mask ("Difflet", section 4.2, Representing
+// Attention Mask): key tiles past the bound are never visited and only the one
+// tile that straddles it is masked.  Key and value rows past the bound are
+// never read at all (their loads are clamped to the last valid row), so
+// whatever the padded slots hold cannot reach the output.
 //
-// The design point of the Trainium kernel the pages describe (128-query tiles,
-// scores kept on chip, probabilities transposed before the value product) is
-// kept; its mechanics are re-done for CDNA4:
-//  * a workgroup of 4 waves owns 128 queries of one (batch row, head); each
-//    wave owns 32 queries whose Q fragments stay in registers;
-//  * scores are produced transposed, S^T = K Q^T, with K as the MFMA A operand
-//    (32x32x16, bf16 in, fp32 out).  Every lane then holds 16 scores of ONE
-//    query, so the softmax row statistics need a single cross-lane exchange
-//    (lane l <-> l^32) and no transpose of P is needed: the fp32 scores, once
-//    exponentiated and rounded to bf16, are already laid out as the B operand
-//    of O^T = V^T P^T.  The key order inside each 16-key MFMA step is permuted
-//    identically in both operands, which leaves the sum unchanged;
-//  * K tiles are staged row-major and V tiles transposed (V^T, d-major) in LDS,
-//    64 keys at a time, with the next tile prefetched into registers while the
-//    current one is multiplied;
-//  * the softmax runs in the log2 domain: scores are scaled by
-//    scale*log2(e) and exponentiated with v_exp_f32; the running max and sum
-//    are fp32; the output is divided by the sum once at the end.
+// The Trainium kernel on the pages (128-query tiles, scores kept on chip, a
+// transpose of the probabilities before the value product) is prior art; the
+// mechanics here are CDNA4's, chosen from measurements on gfx950:
+//  * a workgroup is 8 waves of 32 queries (256 queries), two waves per SIMD.
+//    The waves form two groups that alternate between an MFMA phase and a
+//    softmax phase, one phase apart, with a workgroup barrier at every phase
+//    boundary: while one wave of a SIMD multiplies, the other exponentiates.
+//    (VALU work in another wave hides behind MFMAs; in the same wave it
+//    mostly does not.)
+//  * K and V tiles (64 keys) stream from HBM/L2 straight into LDS with
+//    global_load_lds_dwordx4 (no VGPR staging) through a 4-stage ring, two
+//    tiles ahead of the math.  Rows are stored unpadded with their 16-byte
+//    chunks XOR-swizzled by row so the K fragment reads and the transposing V
+//    reads hit distinct bank groups.  The loads are issued from inline
+//    assembly so the compiler does not guard each LDS read with a wait for
+//    every load in flight (an explicit vmcnt wait + barrier per tile is the
+//    synchronisation);
+//  * scores are produced transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16, K
+//    as the A operand): each lane then holds the scores of ONE query against 32
+//    keys, so the row max needs one exchange between lane halves, and the
+//    exponentiated scores are already laid out as the B operand of
+//    O^T = V^T P^T (the key order inside each 16-key step is permuted the same
+//    way in both operands, which leaves the sum unchanged);
+//  * V^T fragments come from row-major V with ds_read_b64_tr_b16 (gfx950's
+//    transposing LDS read): in each 16-lane group, output lane 4r+e takes
+//    element e of the 8-byte reads of source lanes r, r+4, r+8, r+12, so
+//    source lane s points at key k0 + s/4, columns d0 + 4(s%4) .. +3 and
+//    output lane i receives keys k0..k0+3 of column d0 + i;
+//  * softmax runs in the log2 domain: p = exp2(s*c - m) with c = scale*log2(e)
+//    folded into one FMA before v_exp_f32; the running max and sum are fp32
+//    and O is divided by the sum once at the end.  The MFMA accumulators are
+//    VGPRs (the file is built with the VGPR form of MFMA) so the softmax
+//    phase reads the scores without AGPR copies.
 #include "common.h"
 #include "kernels.h"
 
 namespace dit {
 namespace {
 
-constexpr int kBM = 128;  // queries per workgroup (32 per wave)
-constexpr int kBN = 64;   // keys per tile
-constexpr int kThreads = 256;
-constexpr int kVtLd = kBN + 4;  // V^T row (keys) padded: 136 B rows -> conflict-free 8 B reads
+constexpr int kWaves = 8;      // two groups of 4 waves, one wave of each per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBN = 64;        // keys per tile
+constexpr int kStages = 4;     // LDS ring depth
+constexpr int kBM = kWaves * 32;  // queries per workgroup (32 per wave)
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnParams p) {
-  constexpr int kKLd = D + 8;        // K row padded by 16 B
-  constexpr int kCpr = D / 8;        // 16-byte chunks per K/V row
-  constexpr int kRowsPerPass = kThreads / kCpr;
-  constexpr int kKPasses = kBN / kRowsPerPass;
-  constexpr int kVPasses = kCpr * kBN / kThreads;
-  constexpr int kDB = D / 32;        // 32-wide d blocks of O^T
-  constexpr int kKS = D / 16;        // 16-wide k steps of Q K^T
+struct Tile {
+  static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kBytes = kBN * kRowBytes;         // one K or V tile
+  static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows per wave-wide 16 B/lane load
+  static constexpr int kLoads = kBN / kRowsPerLoad / kWaves;  // loads per tensor per wave per tile
+  static constexpr int kStageBytes = 2 * kBytes;         // K tile then V tile
+};
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBN * kKLd];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * kVtLd];
+// 16-byte chunk c of tile row r is stored at chunk position c ^ swz(r).
+// Measured on gfx950, LDS serves a 16-byte K fragment read in ~5.8 clocks
+// and an 8-byte transposing read in ~3.0 when every group of lanes served
+// together touches distinct 16-byte bank groups (16 of them, 256 bytes):
+//  * K reads: lanes 0..15 read the same chunk of rows 0..15, so swz must be
+//    a permutation over 16 consecutive rows (bank group = (row*kChunks + pos)
+//    mod 16);
+//  * V reads: lanes 0..31 read 4 consecutive chunks (one aligned group of 4)
+//    of 4 consecutive rows, so those rows must move the group to 4 distinct
+//    places.
+// With 16 chunks per row (D = 128) swz = 4*(r&3) + ((r>>2)&3) meets both;
+// with 8 chunks (D = 64, two rows per bank cycle) swz = 4*((r>>1)&1) +
+// ((r>>2)&3) does.  swz depends on row % 16 only.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128)
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  else
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+// s_waitcnt with only vmcnt constrained (expcnt, lgkmcnt left at their max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_ptr;
+typedef __attribute__((address_space(3))) char* lds_char_ptr;
+
+// One wave-wide 16-byte-per-lane load from global memory into LDS: lane i's
+// 16 bytes at gbase + voff land at LDS byte lds_addr + 16*i.  gbase and
+// lds_addr are wave-uniform.  M0 (the LDS base register) is saved and
+// restored around the load.
+__device__ __forceinline__ void lds_dma16(const char* gbase, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gbase), "s"(lds_addr)
+      : "memory");
+}
+
+// Per-lane byte offsets (from the tile's first key row) of the chunks this
+// wave loads: wave w loads rows [(w*kLoads + n) * kRowsPerLoad, +kRowsPerLoad);
+// lane i of a load lands at row i / kChunks, chunk position i % kChunks, so it
+// fetches the chunk that swizzles there.  Rows past `last_row` (the last
+// valid key, relative to the tile) are clamped to it.
+template <int D>
+__device__ __forceinline__ void dma_offsets(uint32_t (&voff)[Tile<D>::kLoads], int wave, int lane,
+                                            int64_t stride_bytes, int last_row) {
+  using T = Tile<D>;
+#pragma unroll
+  for (int n = 0; n < T::kLoads; ++n) {
+    const int r = (wave * T::kLoads + n) * T::kRowsPerLoad + lane / T::kChunks;
+    const int c = (lane % T::kChunks) ^ swz<D>(r);
+    voff[n] = static_cast<uint32_t>(min(r, last_row) * stride_bytes + c * 16);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void dma_tile(const char* kg, const char* vg,
+                                         const uint32_t (&voff)[Tile<D>::kLoads],
+                                         uint32_t lds_stage, int wave) {
+  using T = Tile<D>;
+#pragma unroll
+  for (int n = 0; n < T::kLoads; ++n) {
+    const uint32_t dst = lds_stage + (wave * T::kLoads + n) * 1024;
+    lds_dma16(kg, voff[n], dst);
+    lds_dma16(vg, voff[n], dst + T::kBytes);
+  }
+}
+
+template <int D>
+struct WaveState {
+  static constexpr int kKS = D / 16;  // 16-wide k steps of K Q^T
+  static constexpr int kDB = D / 32;  // 32-row blocks of O^T
+  bf16x8 qf[kKS];     // Q fragments: Q[q][16*ks + 8*hi .. +7], q = lane%32
+  f32x16 o[kDB];      // O^T accumulators: o[db][4g + e] = O[q][32db + 8g + 4*hi + e]
+  f32x16 s[2];        // S^T of one tile: s[t][4g + e] = score of key 32t + 8g + 4*hi + e
+  bf16x8 pf[4];       // p of one tile as the B operand of four 16-key value steps
+  float m_run;        // running max of the scaled scores (log2 domain)
+  float alpha;        // rescale of O still owed for the last raise of m_run
+  float l_run;        // this lane's partial sum of p
+  int k_off[kKS];     // K fragment byte offsets within a stage (row lane%32)
+  int v_off[2][kDB];  // V^T transposing-read byte offsets (rows 8g + 4*hi + s16/4)
+};
+
+// max / sum of a value with the one in the other half of the wave (lane^32),
+// without an LDS round trip: v_permlane32_swap of (x, x) leaves
+// (x[l], x[l+32]) in lanes l < 32 and (x[l-32], x[l]) in lanes l >= 32.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// MFMA phase: S^T of key tile j+1 (sK = its K stage; absent after the last
+// tile), then O^T = alpha O^T + V^T P^T for tile j (sV = its V stage; absent
+// before the first tile).  LDS reads and MFMAs, plus the O rescale owed by
+// the softmax phase, woven into the score MFMAs (this wave's VALU is idle
+// here while the other wave of the SIMD runs its softmax).  Fragment reads run a fixed number of
+// steps ahead of their MFMA (scheduling fences keep the compiler from hoisting
+// all 32 of them, which would cost 128 VGPRs).
+template <int D, bool kPVPart, bool kQKPart>
+__device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, const char* sV) {
+  using T = Tile<D>;
+  using W = WaveState<D>;
+  constexpr int kPV = 4 * W::kDB;  // value steps: (u, db)
+  constexpr int kQK = 2 * W::kKS;  // score steps: (ks, t), t fastest: two accumulator chains
+  constexpr int kAhead = 2;  // fragment reads in flight ahead of their MFMA
+  if constexpr (kQKPart) {
+    auto kread = [&](int i) {
+      const int t = i % 2, ks = i / 2;
+      return *reinterpret_cast<const bf16x8*>(sK + 32 * t * T::kRowBytes + st.k_off[ks]);
+    };
+    bf16x8 kf[kQK];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) kf[i] = kread(i);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.s[t][e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kQK; ++i) {
+      if (i + kAhead < kQK) kf[i + kAhead] = kread(i + kAhead);
+      // the O rescale owed by the last softmax phase rides along (VALU)
+      if constexpr (kPVPart) {
+        if (i < W::kDB * 4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.o[i / 4][4 * (i % 4) + e] *= st.alpha;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      st.s[i % 2] = mfma32x32x16(kf[i], st.qf[i / 2], st.s[i % 2]);
+    }
+  } else if constexpr (kPVPart) {
+#pragma unroll
+    for (int i = 0; i < W::kDB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.o[i][e] *= st.alpha;
+  }
+  if constexpr (kPVPart) {
+    auto vread = [&](int i) {
+      const int u = i / W::kDB, db = i % W::kDB;
+      const char* vrow = sV + 16 * u * T::kRowBytes;
+      const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(vrow + st.v_off[0][db]));
+      const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_ptr)(vrow + st.v_off[1][db]));
+      return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 vf[kPV];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) vf[i] = vread(i);
+#pragma unroll
+    for (int i = 0; i < kPV; ++i) {
+      if (i + kAhead < kPV) vf[i + kAhead] = vread(i + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+      st.o[i % W::kDB] = mfma32x32x16(vf[i], st.pf[i / W::kDB], st.o[i % W::kDB]);
+    }
+  }
+}
+
+// Softmax phase for key tile j (keys j0 .. j0+63): mask past the bound (only
+// the tile that holds it), tile max, online update of the running max with
+// the rescale of O and l, p = exp2(s*c - m) into the running sum and, rounded
+// to bf16, into pf.  VALU only.
+template <int D>
+__device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_valid, int hi, float c) {
+  using W = WaveState<D>;
+  if (j0 + kBN > n_valid) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (j0 + 32 * t + 8 * (r / 4) + 4 * hi + (r % 4) >= n_valid) st.s[t][r] = -INFINITY;
+  }
+  // 32 scores -> 1 in 16 v_max3 (four independent chains)
+  float m[4];
+#pragma unroll
+  for (int c4 = 0; c4 < 4; ++c4) {
+    const int t = c4 / 2, r0 = 8 * (c4 % 2);
+    float x = max3f(st.s[t][r0], st.s[t][r0 + 1], st.s[t][r0 + 2]);
+    x = max3f(x, st.s[t][r0 + 3], st.s[t][r0 + 4]);
+    x = max3f(x, st.s[t][r0 + 5], st.s[t][r0 + 6]);
+    m[c4] = fmaxf(x, st.s[t][r0 + 7]);
+  }
+  const float m0 = fmaxf(m[0], m[1]), m1 = fmaxf(m[2], m[3]);
+  // running max; l is rescaled here, O in the next MFMA phase (alpha)
+  const float m_new = fmaxf(st.m_run, max_halves(fmaxf(m0, m1)) * c);  // c > 0 keeps the order
+  st.alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+  st.m_run = m_new;
+  st.l_run *= st.alpha;
+  const float nm = -st.m_run;
+  float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(st.s[u / 2][8 * (u % 2) + i], c, nm));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(st.s[u / 2][8 * (u % 2) + i + 1], c, nm));
+      l0 += e0;
+      l1 += e1;
+      w[i / 2] = pack_bf16x2(e0, e1);
+    }
+    st.pf[u] = __builtin_bit_cast(bf16x8, w);
+  }
+  st.l_run += l0 + l1;
+}
+
+// Wait (each wave for its own loads) until tile `need` has landed, knowing
+// how many tiles were issued after it.
+template <int L>
+__device__ __forceinline__ void wait_tile(int later_tiles) {
+  if (later_tiles >= 2)
+    wait_vmcnt<2 * L>();
+  else if (later_tiles == 1)
+    wait_vmcnt<L>();
+  else
+    wait_vmcnt<0>();
+}
+
+// Issue the loads of tile j into its ring slot (clamping rows past the last
+// valid key in the tile that holds the bound).
+template <int D>
+__device__ __forceinline__ void issue_tile(const char* kg0, const char* vg0, int64_t stride_bytes,
+                                           int j, int n_valid, uint32_t lds_base, int wave,
+                                           int lane, const uint32_t (&voff)[Tile<D>::kLoads]) {
+  using T = Tile<D>;
+  const int64_t adv = static_cast<int64_t>(j) * kBN * stride_bytes;
+  const uint32_t stage = lds_base + (j % kStages) * T::kStageBytes;
+  if ((j + 1) * kBN <= n_valid) {
+    dma_tile<D>(kg0 + adv, vg0 + adv, voff, stage, wave);
+  } else {
+    uint32_t vc[T::kLoads];
+    dma_offsets<D>(vc, wave, lane, stride_bytes, n_valid - 1 - j * kBN);
+    dma_tile<D>(kg0 + adv, vg0 + adv, vc, stage, wave);
+  }
+}
+
+// The workgroup's 8 waves form two groups (waves 0-3 and 4-7; each SIMD runs
+// one wave of each) that alternate between an MFMA phase and a softmax phase,
+// the second group one phase behind the first, with a workgroup barrier at
+// every phase boundary.  While one wave of a SIMD multiplies, the other
+// exponentiates, so the matrix core and the vector ALU work at the same time
+// (measured on gfx950: VALU work in another wave hides behind MFMAs almost
+// completely, VALU work in the same wave does not).
+//
+// Each wave runs the same sequence -- S of tile 0; softmax of tile 0; then
+// for each tile k: {O += P V of tile k and S of tile k+1; softmax of tile
+// k+1}; finally O += P V of the last tile -- with a barrier before every
+// step.  The second group takes one extra barrier first (and the first group
+// one at the end), which puts it exactly one phase behind.
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
+  using T = Tile<D>;
+  using W = WaveState<D>;
+  constexpr int L = 2 * T::kLoads;  // loads per wave per tile
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * T::kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int grp = wave / 4;
   const int hi = lane / 32;
   const int b = blockIdx.z;
   const int h = blockIdx.y;
   const int n_tok = p.n_tok;
   const int n_valid = p.n_valid[b];
-  const int64_t base = static_cast<int64_t>(b) * n_tok * p.qkv_stride + h * D;
-
-  // Q fragments: lane holds Q[q][16*ks + 8*hi .. +7] for its query q.
-  const int q_row = blockIdx.x * kBM + wave * 32 + lane % 32;
-  const int q_ld = q_row < n_tok ? q_row : n_tok - 1;
-  bf16x8 qf[kKS];
-  {
-    const uint16_t* src = p.q + base + static_cast<int64_t>(q_ld) * p.qkv_stride + 8 * hi;
-#pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
-  }
-
-  // K load mapping: consecutive threads read consecutive chunks of one row.
-  const int kc = tid % kCpr;
-  const int kr = tid / kCpr;
-  // V load mapping: a wave covers 64 keys of one chunk, so the transposed
-  // 2-byte LDS writes of a wave land on one contiguous V^T row segment.
-  const int vk = tid % kBN;
-  const int vc = tid / kBN;
-
-  u32x4 rk[kKPasses], rv[kVPasses];
-  auto fetch = [&](int j0) {
-#pragma unroll
-    for (int i = 0; i < kKPasses; ++i) {
-      int key = j0 + kr + i * kRowsPerPass;
-      key = key < n_tok ? key : n_tok - 1;
-      rk[i] = *reinterpret_cast<const u32x4*>(p.k + base + static_cast<int64_t>(key) * p.qkv_stride + kc * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < kVPasses; ++i) {
-      int key = j0 + vk;
-      key = key < n_tok ? key : n_tok - 1;
-      rv[i] = *reinterpret_cast<const u32x4*>(p.v + base + static_cast<int64_t>(key) * p.qkv_stride + (vc + i * (kThreads / kBN)) * 8);
-    }
-  };
-
-  f32x16 o[kDB];
-#pragma unroll
-  for (int i = 0; i < kDB; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-  float m_run = -INFINITY;  // running max of scaled (log2-domain) scores
-  float l_run = 0.f;        // this lane's partial sum of exponentials
-
   const int n_tiles = (n_valid + kBN - 1) / kBN;  // fully padded tiles are skipped
+  const int64_t base = static_cast<int64_t>(b) * n_tok * p.qkv_stride + h * D;
+  const char* kg0 = reinterpret_cast<const char*>(p.k + base);
+  const char* vg0 = reinterpret_cast<const char*>(p.v + base);
+  const int64_t stride_bytes = p.qkv_stride * 2;
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_ptr)smem));
   const float c = p.scale_log2;
-  fetch(0);
 
-  for (int jt = 0; jt < n_tiles; ++jt) {
-    const int j0 = jt * kBN;
-    __syncthreads();
+  uint32_t voff[T::kLoads];
+  dma_offsets<D>(voff, wave, lane, stride_bytes, kBN - 1);
 #pragma unroll
-    for (int i = 0; i < kKPasses; ++i)
-      *reinterpret_cast<u32x4*>(&sK[(kr + i * kRowsPerPass) * kKLd + kc * 8]) = rk[i];
-    {
-      // V rows past the valid bound are written as zeros, so whatever the
-      // padded slots hold (even Inf/NaN) cannot reach the output.
-      const bool vvalid = j0 + vk < n_valid;
-#pragma unroll
-      for (int i = 0; i < kVPasses; ++i) {
-        const int d0 = (vc + i * (kThreads / kBN)) * 8;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = vvalid ? rv[i][e] : 0u;
-          sVt[(d0 + 2 * e) * kVtLd + vk] = static_cast<uint16_t>(w & 0xffffu);
-          sVt[(d0 + 2 * e + 1) * kVtLd + vk] = static_cast<uint16_t>(w >> 16);
-        }
-      }
-    }
-    __syncthreads();
-    if (jt + 1 < n_tiles) fetch(j0 + kBN);
+  for (int j = 0; j < kStages - 1; ++j)
+    if (j < n_tiles) issue_tile<D>(kg0, vg0, stride_bytes, j, n_valid, lds_base, wave, lane, voff);
 
-    // S^T for two 32-key halves: s[t][4*g + e] is the score of
-    // key j0 + 32*t + 8*g + 4*hi + e against this lane's query.
-    f32x16 s[2];
+  W st;
+  // Q fragments.  The wait for them also covers the first tiles' loads;
+  // waiting once here keeps the compiler from guarding later instructions
+  // with waits on loads it cannot see complete.
+  const int q_first = blockIdx.x * kBM + wave * 32;
+  {
+    const int q = min(q_first + lane % 32, n_tok - 1);
+    const uint16_t* src = p.q + base + static_cast<int64_t>(q) * p.qkv_stride + 8 * hi;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int ks = 0; ks < W::kKS; ++ks) st.qf[ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
+  }
+  wait_vmcnt<0>();
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
+  for (int i = 0; i < W::kDB; ++i)
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            &sK[(32 * t + lane % 32) * kKLd + 16 * ks + 8 * hi]);
-        s[t] = mfma32x32x16(kf, qf[ks], s[t]);
-      }
-    }
-
-    // scale into the log2 domain; mask the tile that straddles the bound
-    const bool boundary = j0 + kBN > n_valid;
-    float mt = -INFINITY;
+    for (int e = 0; e < 16; ++e) st.o[i][e] = 0.f;
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+  st.alpha = 1.f;
+  // LDS read offsets.  A K fragment row is lane%32 (+32t) and a V^T read row
+  // is 16u + 8g + 4*hi + s16/4; the swizzle depends only on row % 16, so t
+  // and u only add immediate row offsets.
+  {
+    const int r = lane % 32;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int ks = 0; ks < W::kKS; ++ks) st.k_off[ks] = r * T::kRowBytes + (((2 * ks + hi) ^ swz<D>(r)) * 16);
+    const int g16 = lane / 16, s16 = lane % 16;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[t][r] * c;
-        if (boundary) {
-          const int key = j0 + 32 * t + 8 * (r / 4) + 4 * hi + (r % 4);
-          v = key < n_valid ? v : -INFINITY;
-        }
-        s[t][r] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-
-    float ls = 0.f;
+    for (int g = 0; g < 2; ++g) {
+      const int rv = 8 * g + 4 * hi + s16 / 4;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(s[t][r] - m_new);
-        s[t][r] = e;
-        ls += e;
-      }
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int i = 0; i < kDB; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-
-    // O^T += V^T P^T over four 16-key steps.  Step u covers keys
-    // j0 + 16*u + [0, 16); its 16 k-slots are, for lane half hi,
-    // keys 4*hi + {0..3} then 8 + 4*hi + {0..3} -- the order in which the
-    // score accumulator already holds them.
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = u / 2;
-      const int g0 = 2 * (u % 2);
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pf[e] = static_cast<__bf16>(s[t][4 * g0 + e]);
-        pf[4 + e] = static_cast<__bf16>(s[t][4 * (g0 + 1) + e]);
-      }
-      const int kb = 16 * u + 4 * hi;
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const uint16_t* vrow = &sVt[(32 * db + lane % 32) * kVtLd];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kb);
-        const u32x2 hi8 = *reinterpret_cast<const u32x2*>(vrow + kb + 8);
-        u32x4 vv;
-        vv[0] = lo[0]; vv[1] = lo[1]; vv[2] = hi8[0]; vv[3] = hi8[1];
-        o[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, vv), pf, o[db]);
+      for (int db = 0; db < W::kDB; ++db) {
+        const int col = 32 * db + 16 * (g16 % 2) + 4 * (s16 % 4);
+        st.v_off[g][db] = rv * T::kRowBytes + (((col / 8) ^ swz<D>(rv)) * 16) + (col % 8) * 2;
       }
     }
   }
+
+  // Global phase 2m opens with "tile m has landed, ring slot of tile m-2 is
+  // free": every wave waits for its own loads of tile m, then after the
+  // barrier issues its share of tile m+2 (tiles 0..2 were issued above).  The
+  // first group meets phase 2m before the MFMA phase of tile m-1, the second
+  // (one phase behind) before the softmax phase of tile m-1.
+  auto phase_barrier = [&](bool duty, int m) {
+    if (duty && m < n_tiles) wait_tile<L>(min(m == 0 ? 2 : m + 1, n_tiles - 1) - m);
+    __builtin_amdgcn_s_barrier();
+    if (duty && m >= 1 && m + 2 < n_tiles)
+      issue_tile<D>(kg0, vg0, stride_bytes, m + 2, n_valid, lds_base, wave, lane, voff);
+  };
+  auto stage = [&](int j) { return smem + (j % kStages) * T::kStageBytes; };
+  const bool a_grp = grp == 0;
+  if (!a_grp) phase_barrier(true, 0);
+  phase_barrier(a_grp, 0);
+  mfma_phase<D, false, true>(st, stage(0), nullptr);
+  phase_barrier(!a_grp, 1);
+  softmax_phase<D>(st, 0, n_valid, hi, c);
+  for (int k = 0; k + 1 < n_tiles; ++k) {
+    phase_barrier(a_grp, k + 1);
+    mfma_phase<D, true, true>(st, stage(k + 1), stage(k) + T::kBytes);
+    phase_barrier(!a_grp, k + 2);
+    softmax_phase<D>(st, (k + 1) * kBN, n_valid, hi, c);
+  }
+  phase_barrier(a_grp, n_tiles);
+  mfma_phase<D, true, false>(st, nullptr, stage(n_tiles - 1) + T::kBytes);
+  if (a_grp) phase_barrier(false, 0);
 
   // Combine the two lane halves' partial sums, normalise, store.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
-  if (q_row < n_tok) {
+  const int q = q_first + lane % 32;
+  const float l_tot = sum_halves(st.l_run);
+  if (q < n_tok) {
     const float inv = 1.f / l_tot;
-    uint16_t* dst = p.out + (static_cast<int64_t>(b) * n_tok + q_row) * p.out_stride + h * D;
+    uint16_t* dst = p.out + (static_cast<int64_t>(b) * n_tok + q) * p.out_stride + h * D;
 #pragma unroll
-    for (int db = 0; db < kDB; ++db)
+    for (int db = 0; db < W::kDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         u32x2 w;
-        w[0] = pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-        w[1] = pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        w[0] = pack_bf16x2(st.o[db][4 * g] * inv, st.o[db][4 * g + 1] * inv);
+        w[1] = pack_bf16x2(st.o[db][4 * g + 2] * inv, st.o[db][4 * g + 3] * inv);
         *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * g + 4 * hi) = w;
       }
     if (p.lse && hi == 0)
-      p.lse[(static_cast<int64_t>(b) * p.heads + h) * n_tok + q_row] =
-          m_run * 0.69314718055994531f + logf(l_tot);
+      p.lse[(static_cast<int64_t>(b) * p.heads + h) * n_tok + q] =
+          st.m_run * 0.69314718055994531f + logf(l_tot);
   }
 }
 

@@ -78,7 +78,8 @@ typedef struct dit_attn_desc {
  *   q, k, v  bf16, element [b, i, h, e] at  ptr + (b*N + i)*qkv_row_stride
  *            + h*head_dim + e   (e.g. three column blocks of one [B,N,3*H*d]
  *            buffer with qkv_row_stride = 3*H*d).  Must be 16-byte aligned
- *            and qkv_row_stride a multiple of 8.
+ *            and qkv_row_stride a multiple of 8, at most 2^24
+ *            (DIT_EUNSUPPORTED above).
  *   out      bf16 [b, i, h, e] at  out + (b*N + i)*out_row_stride + h*head_dim
  *            + e;  out_row_stride >= heads*head_dim, multiple of 8.  Must not
  *            overlap q, k or v.

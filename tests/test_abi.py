@@ -61,6 +61,7 @@ def test_attention_argument_errors():
     _expect("DIT_EINVAL", f, _attn(), None, FAKE, FAKE, hd, FAKE * 2, hd, stream=0)
     _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE, FAKE, hd - 8, FAKE * 2, hd, stream=0)
     _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE, FAKE, hd + 4, FAKE * 2, hd, stream=0)
+    _expect("DIT_EUNSUPPORTED", f, _attn(), FAKE, FAKE, FAKE, (1 << 24) + 8, FAKE * 2, hd, stream=0)
     _expect("DIT_EINVAL", f, _attn(), FAKE + 2, FAKE, FAKE, hd, FAKE * 2, hd, stream=0)
     # out aliasing q
     _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE * 4, FAKE * 4, hd, FAKE + 256, hd, stream=0)
