@@ -3,14 +3,29 @@
 // gated residual x += gate * y on the fp32 residual stream.  These are the
 // projection and MLP terms of "ChunkFlow" Appendix B, equations (13) and (16).
 //
-// Tiling: a workgroup of 4 waves computes a 128 (W rows, n) x 256 (A rows, m)
-// tile of C^T; each wave owns 64 x 128 = 2 x 4 MFMA 32x32 tiles.  The MFMA is
-// fed W as its A operand and the activations as its B operand, so each lane
-// ends up holding 4 consecutive output features of one token row: bias, gate
-// and residual loads and the stores are 8- or 16-byte vectors.  K is staged
-// through LDS 64 at a time (rows padded by 16 bytes so the 16-byte operand
-// reads of a wave fall in distinct banks); the next K slice is fetched into
-// registers while the current one is multiplied.
+// In both kernels the MFMA is fed W as its A operand and the activations as
+// its B operand, so each lane ends up holding 4 consecutive output features
+// of one token row: bias, gate and residual loads and the stores are 8- or
+// 16-byte vectors.
+//
+// Large GEMMs (the block's projections and MLP): a workgroup of 8 waves (two
+// per SIMD) computes a 256 (tokens) x 256 (features) tile, each wave 128 x 64
+// = 4 x 2 MFMA 32x32 tiles with the accumulators in AGPRs.  A 256 x 256 tile
+// moves 64 bytes of operands from L2 per 2 x 256 x 256 flops, half of what a
+// 128 x 256 tile needs, which keeps L2 below its bandwidth at full MFMA
+// rate.  K slices of 32 stream from HBM/L2 straight into LDS with
+// global_load_lds_dwordx4 through a 4-stage ring (three slices ahead, one
+// barrier per slice); rows are stored unpadded with their 16-byte chunks
+// XOR-swizzled by row so the operand reads of a wave hit distinct bank
+// groups.  Workgroups are ordered XCD by XCD (the dispatcher deals workgroup
+// ids round-robin over the 8 XCDs, each with its own L2) and, inside an XCD,
+// in groups of 8 token tiles that sweep all feature tiles, so the
+// workgroups running together on one XCD share operand slices in its L2.
+//
+// Small GEMMs (loop glue: timestep MLP, modulation, input/output projection):
+// a workgroup of 4 waves computes a 128 (features) x 256 (tokens) tile, each
+// wave 64 x 128; K is staged through padded LDS 64 at a time, the next slice
+// fetched into registers while the current one is multiplied.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,6 +49,49 @@ __device__ __forceinline__ int64_t a_row_offset(const GemmParams& p, int64_t r) 
 __device__ __forceinline__ int64_t c_row_offset(const GemmParams& p, int64_t r) {
   return p.group_rows > 0 ? (r / p.group_rows) * p.c_group_stride + (r % p.group_rows) * p.ldc
                           : r * p.ldc;
+}
+
+// y[0..3] = acc for output features n..n+3 of token row m: add the bias, apply
+// the epilogue and store (8-byte bf16 or 16-byte fp32 accesses).
+template <int EPI>
+__device__ __forceinline__ void store_epilogue(const GemmParams& p, int64_t m, int n, float (&y)[4]) {
+  const int64_t crow = c_row_offset(p, m);
+  if (p.bias) {
+    const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
+    y[0] += __uint_as_float(bb[0] << 16);
+    y[1] += __uint_as_float(bb[0] & 0xffff0000u);
+    y[2] += __uint_as_float(bb[1] << 16);
+    y[3] += __uint_as_float(bb[1] & 0xffff0000u);
+  }
+  if (EPI == EPI_GELU) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = 0.5f * y[e] * (1.f + erff(y[e] * 0.70710678118654752f));
+  } else if (EPI == EPI_SILU) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = y[e] / (1.f + expf(-y[e]));
+  }
+  if (EPI == EPI_F32 || EPI == EPI_GATED) {
+    float* dst = static_cast<float*>(p.out) + crow + n;
+    f32x4 o;
+    if (EPI == EPI_GATED) {
+      const uint16_t* grow = p.gate + (m / p.gate_rows) * p.gate_stride;
+      o = *reinterpret_cast<const f32x4*>(dst);
+      const u32x2 gg = *reinterpret_cast<const u32x2*>(grow + n);
+      o[0] += __uint_as_float(gg[0] << 16) * y[0];
+      o[1] += __uint_as_float(gg[0] & 0xffff0000u) * y[1];
+      o[2] += __uint_as_float(gg[1] << 16) * y[2];
+      o[3] += __uint_as_float(gg[1] & 0xffff0000u) * y[3];
+    } else {
+      o[0] = y[0]; o[1] = y[1]; o[2] = y[2]; o[3] = y[3];
+    }
+    *reinterpret_cast<f32x4*>(dst) = o;
+  } else {
+    uint16_t* dst = static_cast<uint16_t*>(p.out) + crow + n;
+    u32x2 o;
+    o[0] = pack_bf16x2(y[0], y[1]);
+    o[1] = pack_bf16x2(y[2], y[3]);
+    *reinterpret_cast<u32x2*>(dst) = o;
+  }
 }
 
 template <int EPI>
@@ -125,9 +183,6 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmParams p) {
   for (int j = 0; j < 4; ++j) {
     const int64_t m = m0 + wm * 128 + j * 32 + (lane % 32);
     if (m >= p.m) continue;
-    const int64_t crow = c_row_offset(p, m);
-    const uint16_t* grow = nullptr;
-    if (EPI == EPI_GATED) grow = p.gate + (m / p.gate_rows) * p.gate_stride;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -137,50 +192,240 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmParams p) {
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * g + e];
-        if (p.bias) {
-          const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
-          y[0] += __uint_as_float(bb[0] << 16);
-          y[1] += __uint_as_float(bb[0] & 0xffff0000u);
-          y[2] += __uint_as_float(bb[1] << 16);
-          y[3] += __uint_as_float(bb[1] & 0xffff0000u);
-        }
-        if (EPI == EPI_GELU) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = 0.5f * y[e] * (1.f + erff(y[e] * 0.70710678118654752f));
-        } else if (EPI == EPI_SILU) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = y[e] / (1.f + expf(-y[e]));
-        }
-        if (EPI == EPI_F32 || EPI == EPI_GATED) {
-          float* dst = static_cast<float*>(p.out) + crow + n;
-          f32x4 o;
-          if (EPI == EPI_GATED) {
-            o = *reinterpret_cast<const f32x4*>(dst);
-            const u32x2 gg = *reinterpret_cast<const u32x2*>(grow + n);
-            o[0] += __uint_as_float(gg[0] << 16) * y[0];
-            o[1] += __uint_as_float(gg[0] & 0xffff0000u) * y[1];
-            o[2] += __uint_as_float(gg[1] << 16) * y[2];
-            o[3] += __uint_as_float(gg[1] & 0xffff0000u) * y[3];
-          } else {
-            o[0] = y[0]; o[1] = y[1]; o[2] = y[2]; o[3] = y[3];
-          }
-          *reinterpret_cast<f32x4*>(dst) = o;
-        } else {
-          uint16_t* dst = static_cast<uint16_t*>(p.out) + crow + n;
-          u32x2 o;
-          o[0] = pack_bf16x2(y[0], y[1]);
-          o[1] = pack_bf16x2(y[2], y[3]);
-          *reinterpret_cast<u32x2*>(dst) = o;
-        }
+        store_epilogue<EPI>(p, m, n, y);
       }
     }
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-GEMM kernel.
+namespace big {
+
+constexpr int kTM = 256;                          // token rows per workgroup
+constexpr int kTN = 256;                          // output features per workgroup
+constexpr int kBK = 32;                           // k per ring stage
+constexpr int kStages = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowBytes = 2 * kBK;                // 64
+constexpr int kChunks = kRowBytes / 16;           // 4 chunks of 16 bytes per row
+constexpr int kRowsPerLoad = 1024 / kRowBytes;    // rows per wave-wide 16 B/lane load
+constexpr int kLoadsA = kTM / kRowsPerLoad / kWaves;
+constexpr int kLoadsW = kTN / kRowsPerLoad / kWaves;
+constexpr int kTileA = kTM * kRowBytes;
+constexpr int kTileW = kTN * kRowBytes;
+constexpr int kStageBytes = kTileA + kTileW;
+constexpr int kGroupM = 8;
+
+// 16-byte chunk c of a 64-byte row r sits at chunk position c ^ swz(r).  LDS
+// serves 16 bank groups of 16 bytes per clock and a 16-byte operand read
+// serves 16 lanes (16 consecutive rows, one chunk) per clock; rows r, r+4,
+// r+8, r+12 start in the same bank group, and swz separates them.
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wave-wide 16-byte-per-lane load into LDS: lane i's 16 bytes at src land at
+// LDS byte lds_addr + 16*i (lds_addr wave-uniform).  Issued from inline
+// assembly so the compiler does not guard LDS reads with waits on it; M0 is
+// saved and restored.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_addr)
+      : "memory");
+}
+
+typedef __attribute__((address_space(3))) char* lds_char_ptr;
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int hi = lane / 32;
+
+  // tile of this workgroup: XCD-contiguous ids, then groups of kGroupM token tiles
+  int tm, tn;
+  {
+    const int total = tiles_m * tiles_n;
+    const int id = blockIdx.x;
+    const int xcd = id % 8, slot = id / 8;
+    const int q = total / 8, r = total % 8;
+    const int nid = xcd * q + min(xcd, r) + slot;
+    const int per_group = kGroupM * tiles_n;
+    const int g = nid / per_group;
+    const int first_m = g * kGroupM;
+    const int gsize = min(tiles_m - first_m, kGroupM);
+    const int in_g = nid - g * per_group;
+    tm = first_m + in_g % gsize;
+    tn = in_g / gsize;
+  }
+  const int64_t m0 = static_cast<int64_t>(tm) * kTM;
+  const int n0 = tn * kTN;
+
+  // Loads: wave w fills rows [(w*kLoads + n) * kRowsPerLoad, +kRowsPerLoad) of
+  // the A and W tiles; lane i lands at row i / kChunks, chunk position
+  // i % kChunks and fetches the chunk that swizzles there.  Rows past m or n
+  // are clamped (computed, never stored).
+  const char* a_src[kLoadsA];
+  const char* w_src[kLoadsW];
+#pragma unroll
+  for (int n = 0; n < kLoadsA; ++n) {
+    const int rr = (wave * kLoadsA + n) * kRowsPerLoad + lane / kChunks;
+    const int c = (lane % kChunks) ^ swz(rr);
+    int64_t m = m0 + rr;
+    if (m > p.m - 1) m = p.m - 1;
+    a_src[n] = reinterpret_cast<const char*>(p.a + a_row_offset(p, m)) + c * 16;
+  }
+#pragma unroll
+  for (int n = 0; n < kLoadsW; ++n) {
+    const int rr = (wave * kLoadsW + n) * kRowsPerLoad + lane / kChunks;
+    const int c = (lane % kChunks) ^ swz(rr);
+    const int nr = min(n0 + rr, p.n - 1);
+    w_src[n] = reinterpret_cast<const char*>(p.w + static_cast<int64_t>(nr) * p.k) + c * 16;
+  }
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_ptr)smem));
+  auto issue = [&](int kt) {
+    const uint32_t st = lds_base + (kt % kStages) * kStageBytes;
+    const int64_t ko = static_cast<int64_t>(kt) * kRowBytes;
+#pragma unroll
+    for (int n = 0; n < kLoadsA; ++n) lds_dma16(a_src[n] + ko, st + (wave * kLoadsA + n) * 1024);
+#pragma unroll
+    for (int n = 0; n < kLoadsW; ++n) lds_dma16(w_src[n] + ko, st + kTileA + (wave * kLoadsW + n) * 1024);
+  };
+  constexpr int L = kLoadsA + kLoadsW;  // loads per wave per k slice
+
+  const int k_tiles = p.k / kBK;
+#pragma unroll
+  for (int kt = 0; kt < kStages - 1; ++kt)
+    if (kt < k_tiles) issue(kt);
+
+  // wave tile: 128 token rows (wm) x 64 features (wn)
+  const int wm = wave / 4, wn = wave % 4;
+  // operand read offsets within a stage: row = base row + lane%32 (+32 per
+  // MFMA tile, an immediate); the swizzle depends on the row's bits 2..3,
+  // which the tile offsets do not change
+  int a_off[kBK / 16], w_off[kBK / 16];
+  {
+    const int r = lane % 32;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      a_off[ks] = (wm * 128 + r) * kRowBytes + (((2 * ks + hi) ^ swz(r)) * 16);
+      w_off[ks] = kTileA + (wn * 64 + r) * kRowBytes + (((2 * ks + hi) ^ swz(r)) * 16);
+    }
+  }
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // Software pipeline over k steps of 16: the fragments of the next step are
+  // read from LDS while the MFMAs of the current one run.  The barrier that
+  // publishes slice kt+1 sits in the middle of slice kt (after its first k
+  // step), so the first reads of slice kt+1 overlap the last MFMAs of slice
+  // kt; at that barrier every wave is also done with slice kt-1, whose ring
+  // slot then receives slice kt+3.
+  constexpr int kSteps = kBK / 16;
+  auto read_frags = [&](int kt, int ks, bf16x8 (&wf)[2], bf16x8 (&af)[4]) {
+    const char* st = smem + (kt % kStages) * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wf[i] = *reinterpret_cast<const bf16x8*>(st + w_off[ks] + i * 32 * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) af[j] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + j * 32 * kRowBytes);
+  };
+  auto mfmas = [&](const bf16x8 (&wf)[2], const bf16x8 (&af)[4]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(wf[i], af[j], acc[i][j]);
+  };
+  // Slice `need` has landed once at most the loads of the slices issued after
+  // it are in flight; `issued` is the last slice issued so far.
+  auto wait_slice = [&](int need, int issued) {
+    const int later = min(issued, k_tiles - 1) - need;
+    if (later >= 2)
+      wait_vmcnt<2 * L>();
+    else if (later == 1)
+      wait_vmcnt<L>();
+    else
+      wait_vmcnt<0>();
+  };
+
+  static_assert(kSteps == 2, "the pipeline below is written for two k steps per slice");
+  bf16x8 wf0[2], af0[4], wf1[2], af1[4];
+  wait_slice(0, kStages - 2);  // slices 0 .. kStages-2 were issued above
+  __builtin_amdgcn_s_barrier();
+  read_frags(0, 0, wf0, af0);
+  for (int kt = 0; kt < k_tiles; ++kt) {
+    read_frags(kt, 1, wf1, af1);
+    mfmas(wf0, af0);
+    if (kt + 1 < k_tiles) {
+      wait_slice(kt + 1, kt + kStages - 2);  // slice kt+3 is issued only after this barrier
+      __builtin_amdgcn_s_barrier();
+      if (kt + kStages - 1 < k_tiles) issue(kt + kStages - 1);
+      read_frags(kt + 1, 0, wf0, af0);
+    }
+    mfmas(wf1, af1);
+  }
+
+  // acc[i][j][4*g + e] is C[m, n] with
+  //   m = m0 + wm*128 + j*32 + lane%32,  n = n0 + wn*64 + i*32 + 8*g + 4*(lane/32) + e.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t m = m0 + wm * 128 + j * 32 + (lane % 32);
+    if (m >= p.m) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 64 + i * 32 + 8 * g + 4 * hi;
+        if (n >= p.n) continue;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * g + e];
+        store_epilogue<EPI>(p, m, n, y);
+      }
+  }
+}
+
+}  // namespace big
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s) {
   if (p.m == 0) return hipSuccess;
+  if (p.m >= 4 * big::kTM && p.n >= big::kTN) {
+    const int tiles_m = static_cast<int>((p.m + big::kTM - 1) / big::kTM);
+    const int tiles_n = (p.n + big::kTN - 1) / big::kTN;
+    dim3 grid(tiles_m * tiles_n);
+    dim3 block(big::kThreads);
+    switch (epilogue) {
+      case EPI_BF16: hipLaunchKernelGGL(big::gemm_kernel<EPI_BF16>, grid, block, 0, s, p, tiles_m, tiles_n); break;
+      case EPI_GELU: hipLaunchKernelGGL(big::gemm_kernel<EPI_GELU>, grid, block, 0, s, p, tiles_m, tiles_n); break;
+      case EPI_SILU: hipLaunchKernelGGL(big::gemm_kernel<EPI_SILU>, grid, block, 0, s, p, tiles_m, tiles_n); break;
+      case EPI_F32: hipLaunchKernelGGL(big::gemm_kernel<EPI_F32>, grid, block, 0, s, p, tiles_m, tiles_n); break;
+      case EPI_GATED: hipLaunchKernelGGL(big::gemm_kernel<EPI_GATED>, grid, block, 0, s, p, tiles_m, tiles_n); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   dim3 grid((p.n + kTN - 1) / kTN, static_cast<unsigned>((p.m + kTM - 1) / kTM));
   dim3 block(kThreads);
   switch (epilogue) {

@@ -52,6 +52,48 @@ def test_linear_epilogues(M, N, K, epi):
         assert_bf16_ulp(got, ref, f"linear {epi} {M}x{N}x{K}")
 
 
+# Shapes with M >= 1024 and N >= 256 run the large-tile kernel (256 x 256
+# workgroup tiles, K slices streamed into an LDS ring): ragged M and N, one
+# and several K slices, every epilogue, bitwise-equal reruns.
+@pytest.mark.parametrize("M,N,K", [(1100, 520, 128), (1031, 264, 64), (2304, 512, 320)])
+@pytest.mark.parametrize("epi", ["bf16", "gelu", "f32", "gated"])
+def test_linear_large_tiles(M, N, K, epi):
+    a, w, b = _gemm_case(200 + M + K, M, N, K)
+    y = O.linear(_dec(a), _dec(w), _dec(b))
+    da, dw, db = dev_bf16(a), dev_bf16(w), dev_bf16(b)
+    if epi == "gated":
+        rows_g = M // 2 + 1
+        gate = G.normal_bf16(11, (2, N))
+        x0 = G.normal_bf16(12, (M, N))
+        want = _dec(x0) + _dec(gate)[np.arange(M) // rows_g] * y
+        outs = []
+        for _ in range(2):
+            x = dev_f32_from_bf16(x0)
+            D.dit_linear(da, K, dw, db, M, N, K, D.EPI_GATED_RES_F32, x, N, gate=dev_bf16(gate),
+                         gate_stride=N, gate_rows=rows_g)
+            outs.append(x)
+        torch.cuda.synchronize()
+        assert_parity(host(outs[0]), want, f"large gated {M}x{N}x{K}",
+                      max_abs=1e-4 * np.abs(want).max(), rel_l2=1e-5)
+    else:
+        code = {"bf16": D.EPI_BF16, "gelu": D.EPI_GELU_BF16, "f32": D.EPI_F32}[epi]
+        outs = []
+        for _ in range(2):
+            out = torch.empty((M, N), dtype=torch.float32 if epi == "f32" else torch.bfloat16,
+                              device="cuda")
+            D.dit_linear(da, K, dw, db, M, N, K, code, out, N)
+            outs.append(out)
+        torch.cuda.synchronize()
+        got = host(outs[0])
+        if epi == "f32":
+            assert_parity(got, y, f"large f32 {M}x{N}x{K}", max_abs=1e-4 * np.abs(y).max(),
+                          rel_l2=1e-5)
+        else:
+            ref = {"bf16": y, "gelu": O.gelu_erf(y)}[epi]
+            assert_bf16_ulp(got, ref, f"large {epi} {M}x{N}x{K}")
+    assert torch.equal(outs[0], outs[1]), "large-tile GEMM rerun differs"
+
+
 def test_linear_gated_residual_and_row_groups():
     M, N, K, rows_g = 300, 128, 128, 150
     a, w, b = _gemm_case(7, M, N, K)
@@ -77,6 +119,21 @@ def test_linear_gated_residual_and_row_groups():
     assert np.isnan(got[:, G_rows:]).all(), "rows outside the groups were written"
     assert_parity(got[:, :G_rows].reshape(2 * G_rows, N), y[:2 * G_rows], "grouped rows",
                   max_abs=1e-4 * np.abs(y).max(), rel_l2=1e-5)
+
+    # the same grouped addressing through the large-tile kernel (M >= 1024, N >= 256)
+    M2, N2, G2 = 1200, 256, 600
+    a2, w2, b2 = _gemm_case(17, M2, N2, K)
+    y2 = O.linear(_dec(a2), _dec(w2), _dec(b2))
+    a2_pad = np.zeros((2, G2 + 3, K), np.uint16)
+    a2_pad[:, :G2] = a2.reshape(2, G2, K)
+    out2 = torch.full((2, G2 + 5, N2), float("nan"), dtype=torch.float32, device="cuda")
+    D.dit_linear(dev_bf16(a2_pad), K, dev_bf16(w2), dev_bf16(b2), M2, N2, K, D.EPI_F32, out2, N2,
+                 group_rows=G2, a_group_stride=(G2 + 3) * K, c_group_stride=(G2 + 5) * N2)
+    torch.cuda.synchronize()
+    got2 = host(out2)
+    assert np.isnan(got2[:, G2:]).all(), "rows outside the groups were written (large tiles)"
+    assert_parity(got2[:, :G2].reshape(M2, N2), y2, "grouped rows (large tiles)",
+                  max_abs=1e-4 * np.abs(y2).max(), rel_l2=1e-5)
 
 
 def test_linear_rejects_bad_k_without_launch():
