@@ -26,6 +26,8 @@ from .dit import (
     rope_axial,
     attention_probs,
     joint_attention,
+    attention_partial,
+    merge_partials,
     gelu_erf,
     block_forward,
     cfg_combine,
@@ -38,7 +40,7 @@ from .dit import (
 
 __all__ = [
     "bf16_decode", "round_bf16", "adaln_modulate", "linear", "rms_norm_full",
-    "token_positions", "rope_axial", "attention_probs", "joint_attention",
+    "token_positions", "rope_axial", "attention_probs", "attention_partial", "merge_partials", "joint_attention",
     "gelu_erf", "block_forward", "cfg_combine", "euler_update", "sigma_schedule",
     "timestep_features", "silu", "denoise_step",
 ]

@@ -190,6 +190,60 @@ def joint_attention(q, k, v, n_vis, txt_valid, scale=None, chunk=1024):
     return o, lse
 
 
+def attention_partial(q, k, v, k_valid, scale):
+    """One partial of split joint attention ("Difflet", section 4.3, Ring for
+    joint attention): queries q [B, R, heads, d] against one key/value
+    partition k, v [B, Nk, heads, d] whose valid keys of batch row b are the
+    interval [0, k_valid[b]) in the partition's own coordinates (a text
+    partial passes [0, L_text); a visual partition passes all its keys).
+
+    Per query it returns what each partial call hands to the merge: the
+    unnormalised weighted value sum  acc = sum_j exp(s_j - m) v_j,  the
+    maximum score  m = max_j s_j  and the sum of exponentials relative to it
+    l = sum_j exp(s_j - m), all over valid keys only, with s_j = scale q.k_j.
+    A partition with no valid key returns acc = 0, m = -inf, l = 0.
+    Shapes: acc [B, R, heads, d], m and l [B, heads, R]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, R, Hh, d = q.shape
+    acc = np.zeros((B, R, Hh, d), dtype=np.float64)
+    m = np.full((B, Hh, R), -np.inf, dtype=np.float64)
+    l = np.zeros((B, Hh, R), dtype=np.float64)
+    for b in range(B):
+        nv = int(k_valid[b])
+        if nv == 0:
+            continue
+        for h in range(Hh):
+            s = (q[b, :, h, :] @ k[b, :nv, h, :].T) * scale
+            mb = s.max(axis=1)
+            e = np.exp(s - mb[:, None])
+            acc[b, :, h, :] = e @ v[b, :nv, h, :]
+            m[b, h] = mb
+            l[b, h] = e.sum(axis=1)
+    return acc, m, l
+
+
+def merge_partials(parts):
+    """Joint normalisation from independently computed partials ("Difflet",
+    section 4.3): each partial (acc, m, l) of attention_partial uses its own
+    maximum, so both sums are first rescaled to the common maximum
+    M = max_p m_p, i.e. multiplied by exp(m_p - M), then added over the
+    partials; the merged output is the combined weighted sum divided by the
+    combined exponential sum.  Returns (o [B, R, heads, d], lse [B, heads, R])
+    with lse = M + log(sum_p exp(m_p - M) l_p), the natural log of the joint
+    softmax denominator."""
+    M = np.max(np.stack([m for _, m, _ in parts]), axis=0)
+    num = 0.0
+    den = 0.0
+    for acc, m, l in parts:
+        w = np.where(np.isfinite(m), np.exp(m - M), 0.0)  # [B, heads, R]
+        num = num + acc * np.transpose(w, (0, 2, 1))[..., None]
+        den = den + w * l
+    o = num / np.transpose(den, (0, 2, 1))[..., None]
+    return o, M + np.log(den)
+
+
 # ----------------------------------------------------------------------------
 # the block
 # ----------------------------------------------------------------------------
