@@ -20,7 +20,7 @@ STATUS = {0: "DIT_OK", 1: "DIT_EINVAL", 2: "DIT_EUNSUPPORTED", 3: "DIT_EWORKSPAC
 EPI_BF16, EPI_GELU_BF16, EPI_SILU_BF16, EPI_F32, EPI_GATED_RES_F32 = range(5)
 
 EXPORTED = (
-    "dit_joint_attention", "dit_linear", "dit_adaln_modulate", "dit_qk_rmsnorm_rope",
+    "dit_joint_attention", "dit_attention_partial", "dit_attention_merge", "dit_linear", "dit_adaln_modulate", "dit_qk_rmsnorm_rope",
     "dit_block_workspace_bytes", "dit_block_forward", "dit_euler_step",
     "dit_timestep_features", "dit_cast_f32_bf16", "dit_cast_bf16_f32", "dit_debug_positions",
     "dit_denoise_workspace_bytes", "dit_denoise_step",
@@ -39,6 +39,17 @@ class AttnDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_vis", ctypes.c_int32), ("n_txt", ctypes.c_int32),
                 ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("txt_valid", ctypes.c_int32 * DIT_MAX_BATCH)]
+
+
+class PartialDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_k", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("k_valid", ctypes.c_int32 * DIT_MAX_BATCH)]
+
+
+class MergeDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("parts", ctypes.c_int32)]
 
 
 class BlockDesc(ctypes.Structure):
@@ -96,6 +107,10 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, f32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_int
         sig = {
             "dit_joint_attention": (st, [ctypes.POINTER(AttnDesc), vp, vp, vp, i64, vp, i64, vp, f32, vp]),
+            "dit_attention_partial": (st, [ctypes.POINTER(PartialDesc), vp, i64, vp, vp, i64, vp, i64,
+                                           vp, f32, vp]),
+            "dit_attention_merge": (st, [ctypes.POINTER(MergeDesc), ctypes.POINTER(vp), i64,
+                                         ctypes.POINTER(vp), vp, i64, vp, vp]),
             "dit_linear": (st, [ctypes.POINTER(LinearArgs), vp]),
             "dit_adaln_modulate": (st, [vp, i64, i32, i64, vp, vp, i64, f32, vp, vp]),
             "dit_qk_rmsnorm_rope": (st, [ctypes.POINTER(BlockDesc), vp, i64, vp, vp, vp]),
@@ -169,6 +184,31 @@ def dit_joint_attention(desc: AttnDesc, q, k, v, qkv_row_stride, out, out_row_st
     _check(lib().dit_joint_attention(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), qkv_row_stride,
                                      _ptr(out), out_row_stride, _ptr(lse), softmax_scale,
                                      _stream(stream)))
+
+
+def partial_desc(batch, n_q, n_k, heads, head_dim, k_valid) -> PartialDesc:
+    d = PartialDesc()
+    d.batch, d.n_q, d.n_k, d.heads, d.head_dim = batch, n_q, n_k, heads, head_dim
+    for i, L in enumerate(list(k_valid)[:DIT_MAX_BATCH]):
+        d.k_valid[i] = int(L)
+    return d
+
+
+def dit_attention_partial(desc: PartialDesc, q, q_row_stride, k, v, kv_row_stride, out,
+                          out_row_stride, lse, softmax_scale=0.0, stream=None):
+    _check(lib().dit_attention_partial(ctypes.byref(desc), _ptr(q), q_row_stride, _ptr(k), _ptr(v),
+                                       kv_row_stride, _ptr(out), out_row_stride, _ptr(lse),
+                                       softmax_scale, _stream(stream)))
+
+
+def dit_attention_merge(batch, n_q, heads, head_dim, outs, part_row_stride, lses, out,
+                        out_row_stride, lse_out=None, stream=None):
+    d = MergeDesc()
+    d.batch, d.n_q, d.heads, d.head_dim, d.parts = batch, n_q, heads, head_dim, len(outs)
+    po = (ctypes.c_void_p * max(1, len(outs)))(*[_ptr(t) for t in outs])
+    pl = (ctypes.c_void_p * max(1, len(lses)))(*[_ptr(t) for t in lses])
+    _check(lib().dit_attention_merge(ctypes.byref(d), po, part_row_stride, pl, _ptr(out),
+                                     out_row_stride, _ptr(lse_out), _stream(stream)))
 
 
 def dit_linear(a, lda, w, bias, m, n, k, epilogue, out, ldc, gate=None, gate_stride=0, gate_rows=1,

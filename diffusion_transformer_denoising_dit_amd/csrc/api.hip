@@ -225,9 +225,11 @@ hipError_t block_launch(const dit_block_desc* desc, const dit_block_weights* w, 
   if (e != hipSuccess) { *what = "block: rmsnorm/rope"; return e; }
   // 4. o = joint attention
   dit::AttnParams ap{};
-  ap.q = big; ap.k = big + D; ap.v = big + 2 * D; ap.qkv_stride = 3 * D;
-  ap.out = hbuf; ap.out_stride = D; ap.lse = nullptr;
-  ap.n_tok = static_cast<int>(N); ap.heads = desc->attn.heads; ap.head_dim = desc->attn.head_dim;
+  ap.q = big; ap.k = big + D; ap.v = big + 2 * D;
+  ap.q_stride = ap.kv_stride = 3 * D;
+  ap.q_batch = ap.kv_batch = N * 3 * D;
+  ap.out = hbuf; ap.out_stride = D; ap.out_f32 = 0; ap.lse = nullptr;
+  ap.n_q = ap.n_k = static_cast<int>(N); ap.heads = desc->attn.heads; ap.head_dim = desc->attn.head_dim;
   ap.batch = B;
   for (int b = 0; b < DIT_MAX_BATCH; ++b)
     ap.n_valid[b] = b < B ? desc->attn.n_vis + desc->attn.txt_valid[b] : 0;
@@ -381,11 +383,13 @@ dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q, con
   p.q = q;
   p.k = k;
   p.v = v;
-  p.qkv_stride = qkv_row_stride;
+  p.q_stride = p.kv_stride = qkv_row_stride;
+  p.q_batch = p.kv_batch = n_tok * qkv_row_stride;
   p.out = out;
   p.out_stride = out_row_stride;
   p.lse = lse;
-  p.n_tok = static_cast<int>(n_tok);
+  p.n_q = p.n_k = static_cast<int>(n_tok);
+  p.out_f32 = 0;
   p.heads = desc->heads;
   p.head_dim = desc->head_dim;
   p.batch = desc->batch;
@@ -394,6 +398,116 @@ dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q, con
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt(static_cast<float>(desc->head_dim));
   p.scale_log2 = scale * 1.4426950408889634f;
   return hip_status(dit::launch_attention(p, stream), "attention launch");
+}
+
+dit_status dit_attention_partial(const dit_partial_desc* desc, const uint16_t* q,
+                                 int64_t q_row_stride, const uint16_t* k, const uint16_t* v,
+                                 int64_t kv_row_stride, float* out, int64_t out_row_stride,
+                                 float* lse, float softmax_scale, hipStream_t stream) {
+  if (!desc) return fail(DIT_EINVAL, "partial-attention descriptor is NULL");
+  const dit_partial_desc& d = *desc;
+  if (d.batch < 1 || d.batch > DIT_MAX_BATCH)
+    return fail(DIT_EINVAL, "batch %d outside [1, %d]", d.batch, DIT_MAX_BATCH);
+  if (d.n_q < 1 || d.n_k < 1 || d.n_q > (1 << 30) || d.n_k > (1 << 30))
+    return fail(DIT_EINVAL, "n_q %d and n_k %d must be in [1, 2^30]", d.n_q, d.n_k);
+  if (d.heads < 1 || d.heads > 65535) return fail(DIT_EINVAL, "heads %d outside [1, 65535]", d.heads);
+  if (d.head_dim != 64 && d.head_dim != 128)
+    return fail(DIT_EUNSUPPORTED, "head_dim %d: only 64 and 128 are implemented", d.head_dim);
+  for (int b = 0; b < d.batch; ++b)
+    if (d.k_valid[b] < 0 || d.k_valid[b] > d.n_k)
+      return fail(DIT_EINVAL, "k_valid[%d] = %d outside [0, n_k = %d]", b, d.k_valid[b], d.n_k);
+  if (!q || !k || !v || !out || !lse) return fail(DIT_EINVAL, "NULL q, k, v, out or lse");
+  const int64_t hd = static_cast<int64_t>(d.heads) * d.head_dim;
+  if (q_row_stride < hd || q_row_stride % 8 != 0 || kv_row_stride < hd || kv_row_stride % 8 != 0)
+    return fail(DIT_EINVAL, "q/kv row strides must be >= heads*head_dim and multiples of 8");
+  if (kv_row_stride > kMaxQkvRowStride)
+    return fail(DIT_EUNSUPPORTED, "kv_row_stride %lld above %lld",
+                static_cast<long long>(kv_row_stride), static_cast<long long>(kMaxQkvRowStride));
+  if (out_row_stride < hd || out_row_stride % 4 != 0)
+    return fail(DIT_EINVAL, "out_row_stride %lld must be >= heads*head_dim and a multiple of 4",
+                static_cast<long long>(out_row_stride));
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4))
+    return fail(DIT_EINVAL, "q, k, v and out must be 16-byte aligned, lse 4-byte");
+  if (!(softmax_scale >= 0.f) || !std::isfinite(softmax_scale))
+    return fail(DIT_EINVAL, "softmax_scale must be finite and >= 0");
+  const size_t q_bytes = static_cast<size_t>((static_cast<int64_t>(d.batch) * d.n_q - 1) * q_row_stride + hd) * 2;
+  const size_t kv_bytes = static_cast<size_t>((static_cast<int64_t>(d.batch) * d.n_k - 1) * kv_row_stride + hd) * 2;
+  const size_t out_bytes = static_cast<size_t>((static_cast<int64_t>(d.batch) * d.n_q - 1) * out_row_stride + hd) * 4;
+  const size_t lse_bytes = static_cast<size_t>(d.batch) * d.heads * d.n_q * 4;
+  if (overlap(out, out_bytes, q, q_bytes) || overlap(out, out_bytes, k, kv_bytes) ||
+      overlap(out, out_bytes, v, kv_bytes) || overlap(lse, lse_bytes, q, q_bytes) ||
+      overlap(lse, lse_bytes, k, kv_bytes) || overlap(lse, lse_bytes, v, kv_bytes) ||
+      overlap(lse, lse_bytes, out, out_bytes))
+    return fail(DIT_EINVAL, "out or lse overlaps an input or each other");
+  dit::AttnParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.q_stride = q_row_stride;
+  p.kv_stride = kv_row_stride;
+  p.q_batch = static_cast<int64_t>(d.n_q) * q_row_stride;
+  p.kv_batch = static_cast<int64_t>(d.n_k) * kv_row_stride;
+  p.out = out;
+  p.out_stride = out_row_stride;
+  p.out_f32 = 1;
+  p.lse = lse;
+  p.n_q = d.n_q;
+  p.n_k = d.n_k;
+  p.heads = d.heads;
+  p.head_dim = d.head_dim;
+  p.batch = d.batch;
+  for (int b = 0; b < DIT_MAX_BATCH; ++b) p.n_valid[b] = b < d.batch ? d.k_valid[b] : 0;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt(static_cast<float>(d.head_dim));
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(dit::launch_attention(p, stream), "partial attention launch");
+}
+
+dit_status dit_attention_merge(const dit_merge_desc* desc, const float* const* outs,
+                               int64_t part_row_stride, const float* const* lses, uint16_t* out,
+                               int64_t out_row_stride, float* lse_out, hipStream_t stream) {
+  if (!desc) return fail(DIT_EINVAL, "merge descriptor is NULL");
+  const dit_merge_desc& d = *desc;
+  if (d.parts < 1 || d.parts > DIT_MAX_PARTS)
+    return fail(DIT_EINVAL, "parts %d outside [1, %d]", d.parts, DIT_MAX_PARTS);
+  if (d.batch < 1 || d.batch > DIT_MAX_BATCH || d.n_q < 1 || d.heads < 1 || d.heads > 65535)
+    return fail(DIT_EINVAL, "bad merge shape (batch %d, n_q %d, heads %d)", d.batch, d.n_q, d.heads);
+  if (d.head_dim != 64 && d.head_dim != 128)
+    return fail(DIT_EUNSUPPORTED, "head_dim %d: only 64 and 128 are implemented", d.head_dim);
+  if (!outs || !lses || !out) return fail(DIT_EINVAL, "NULL outs, lses or out");
+  const int64_t hd = static_cast<int64_t>(d.heads) * d.head_dim;
+  if (part_row_stride < hd || part_row_stride % 4 != 0 || out_row_stride < hd || out_row_stride % 8 != 0)
+    return fail(DIT_EINVAL, "part_row_stride (multiple of 4) and out_row_stride (multiple of 8) "
+                            "must be >= heads*head_dim");
+  const int64_t rows = static_cast<int64_t>(d.batch) * d.n_q;
+  const size_t part_bytes = static_cast<size_t>((rows - 1) * part_row_stride + hd) * 4;
+  const size_t lse_bytes = static_cast<size_t>(d.batch) * d.heads * d.n_q * 4;
+  const size_t out_bytes = static_cast<size_t>((rows - 1) * out_row_stride + hd) * 2;
+  if (!aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
+    return fail(DIT_EINVAL, "out must be 16-byte aligned, lse_out 4-byte");
+  dit::MergeParams p{};
+  for (int i = 0; i < d.parts; ++i) {
+    if (!outs[i] || !lses[i]) return fail(DIT_EINVAL, "NULL partial %d", i);
+    if (!aligned(outs[i], 16) || !aligned(lses[i], 4))
+      return fail(DIT_EINVAL, "partial %d: out must be 16-byte aligned, lse 4-byte", i);
+    if (overlap(out, out_bytes, outs[i], part_bytes) || overlap(out, out_bytes, lses[i], lse_bytes) ||
+        (lse_out && (overlap(lse_out, lse_bytes, outs[i], part_bytes) ||
+                     overlap(lse_out, lse_bytes, lses[i], lse_bytes))))
+      return fail(DIT_EINVAL, "an output overlaps partial %d", i);
+    p.outs[i] = outs[i];
+    p.lses[i] = lses[i];
+  }
+  if (lse_out && overlap(lse_out, lse_bytes, out, out_bytes))
+    return fail(DIT_EINVAL, "lse_out overlaps out");
+  p.parts = d.parts;
+  p.part_stride = part_row_stride;
+  p.out = out;
+  p.out_stride = out_row_stride;
+  p.lse_out = lse_out;
+  p.batch = d.batch;
+  p.n_q = d.n_q;
+  p.heads = d.heads;
+  p.head_dim = d.head_dim;
+  return hip_status(dit::launch_attention_merge(p, stream), "attention merge launch");
 }
 
 dit_status dit_linear(const dit_linear_args* args, hipStream_t stream) {

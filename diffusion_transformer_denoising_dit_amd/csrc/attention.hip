@@ -339,13 +339,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   const int hi = lane / 32;
   const int b = blockIdx.z;
   const int h = blockIdx.y;
-  const int n_tok = p.n_tok;
+  const int n_q = p.n_q;
   const int n_valid = p.n_valid[b];
   const int n_tiles = (n_valid + kBN - 1) / kBN;  // fully padded tiles are skipped
-  const int64_t base = static_cast<int64_t>(b) * n_tok * p.qkv_stride + h * D;
-  const char* kg0 = reinterpret_cast<const char*>(p.k + base);
-  const char* vg0 = reinterpret_cast<const char*>(p.v + base);
-  const int64_t stride_bytes = p.qkv_stride * 2;
+  const int64_t q_base = static_cast<int64_t>(b) * p.q_batch + h * D;
+  const int64_t kv_base = static_cast<int64_t>(b) * p.kv_batch + h * D;
+  const char* kg0 = reinterpret_cast<const char*>(p.k + kv_base);
+  const char* vg0 = reinterpret_cast<const char*>(p.v + kv_base);
+  const int64_t stride_bytes = p.kv_stride * 2;
+  const int q_first = blockIdx.x * kBM + wave * 32;
+
+  if (n_tiles == 0) {
+    // an empty key range (a partial of split attention whose partition holds
+    // no valid key): the weighted sum is 0 and the log-denominator -inf, the
+    // neutral element of the merge
+    const int q = q_first + lane % 32;
+    if (q < n_q) {
+      const int64_t row = (static_cast<int64_t>(b) * n_q + q) * p.out_stride + h * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = 32 * db + 8 * g + 4 * hi;
+          if (p.out_f32) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + row + col) = z;
+          } else {
+            const u32x2 z = {0u, 0u};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row + col) = z;
+          }
+        }
+      if (p.lse && hi == 0) p.lse[(static_cast<int64_t>(b) * p.heads + h) * n_q + q] = -INFINITY;
+    }
+    return;
+  }
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_ptr)smem));
   const float c = p.scale_log2;
 
@@ -359,10 +386,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // Q fragments.  The wait for them also covers the first tiles' loads;
   // waiting once here keeps the compiler from guarding later instructions
   // with waits on loads it cannot see complete.
-  const int q_first = blockIdx.x * kBM + wave * 32;
   {
-    const int q = min(q_first + lane % 32, n_tok - 1);
-    const uint16_t* src = p.q + base + static_cast<int64_t>(q) * p.qkv_stride + 8 * hi;
+    const int q = min(q_first + lane % 32, n_q - 1);
+    const uint16_t* src = p.q + q_base + static_cast<int64_t>(q) * p.q_stride + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < W::kKS; ++ks) st.qf[ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
   }
@@ -424,20 +450,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // Combine the two lane halves' partial sums, normalise, store.
   const int q = q_first + lane % 32;
   const float l_tot = sum_halves(st.l_run);
-  if (q < n_tok) {
+  if (q < n_q) {
     const float inv = 1.f / l_tot;
-    uint16_t* dst = p.out + (static_cast<int64_t>(b) * n_tok + q) * p.out_stride + h * D;
+    const int64_t row = (static_cast<int64_t>(b) * n_q + q) * p.out_stride + h * D;
 #pragma unroll
     for (int db = 0; db < W::kDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = pack_bf16x2(st.o[db][4 * g] * inv, st.o[db][4 * g + 1] * inv);
-        w[1] = pack_bf16x2(st.o[db][4 * g + 2] * inv, st.o[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(dst + 32 * db + 8 * g + 4 * hi) = w;
+        const int col = 32 * db + 8 * g + 4 * hi;
+        if (p.out_f32) {
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = st.o[db][4 * g + e] * inv;
+          *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + row + col) = w;
+        } else {
+          u32x2 w;
+          w[0] = pack_bf16x2(st.o[db][4 * g] * inv, st.o[db][4 * g + 1] * inv);
+          w[1] = pack_bf16x2(st.o[db][4 * g + 2] * inv, st.o[db][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + row + col) = w;
+        }
       }
     if (p.lse && hi == 0)
-      p.lse[(static_cast<int64_t>(b) * p.heads + h) * n_tok + q] =
+      p.lse[(static_cast<int64_t>(b) * p.heads + h) * n_q + q] =
           st.m_run * 0.69314718055994531f + logf(l_tot);
   }
 }
@@ -445,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
-  dim3 grid((p.n_tok + kBM - 1) / kBM, p.heads, p.batch);
+  dim3 grid((p.n_q + kBM - 1) / kBM, p.heads, p.batch);
   dim3 block(kThreads);
   if (p.head_dim == 128)
     hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, s, p);

@@ -26,15 +26,31 @@ struct AttnParams {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  int64_t qkv_stride;
-  uint16_t* out;
+  int64_t q_stride;   // elements between query tokens
+  int64_t kv_stride;  // elements between key / value tokens
+  int64_t q_batch;    // elements between batch rows of q
+  int64_t kv_batch;   // elements between batch rows of k and v
+  void* out;          // bf16, or fp32 if out_f32: row (b, i) at out + (b*n_q + i)*out_stride
   int64_t out_stride;
-  float* lse;
-  int n_tok, heads, head_dim, batch;
-  int n_valid[8];  // n_vis + txt_valid[b]
-  float scale_log2;  // softmax scale * log2(e)
+  int out_f32;
+  float* lse;         // nullable, fp32 [batch, heads, n_q]
+  int n_q, n_k, heads, head_dim, batch;
+  int n_valid[8];     // valid keys of batch row b: [0, n_valid[b]), n_valid[b] <= n_k
+  float scale_log2;   // softmax scale * log2(e)
 };
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
+
+struct MergeParams {
+  const float* outs[32];
+  const float* lses[32];
+  int parts;
+  int64_t part_stride;  // fp32 elements between rows of a partial output
+  uint16_t* out;
+  int64_t out_stride;
+  float* lse_out;       // nullable
+  int batch, n_q, heads, head_dim;
+};
+hipError_t launch_attention_merge(const MergeParams& p, hipStream_t s);
 
 hipError_t launch_adaln(const float* x, int64_t rows, int hidden, int64_t rows_per_batch,
                         const uint16_t* shift, const uint16_t* scale, int64_t mod_stride,

@@ -94,6 +94,67 @@ dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q,
                                int64_t out_row_stride, float* lse,
                                float softmax_scale, hipStream_t stream);
 
+/* Split joint attention ("Difflet", section 4.3, Ring for joint attention):
+ * the key set of each query is cut into partitions -- the text keys with
+ * bounds [0, L_text) and one partition per chunk of visual keys -- and each
+ * partition is attended separately; partials are merged afterwards by
+ * rescaling to a common maximum.  This is the building block of sequence-
+ * parallel attention; on one GPU it lets a caller split a long key sequence.
+ *
+ * dit_attention_partial: for every batch row b, head h and query row i
+ * (i < n_q), attention of q over the valid keys [0, k_valid[b]) of the
+ * partition (k_valid[b] in [0, n_k]; 0 is an empty partition):
+ *   out[b,i,h,:] = sum_j softmax_j(scale * q.k_j) v_j      (fp32, normalised)
+ *   lse[b,h,i]   = log sum_j exp(scale * q.k_j)            (natural log)
+ * An empty partition writes out = 0 and lse = -inf (the neutral element of
+ * the merge).
+ *   q    bf16, element (b, i, h, e) at q + (b*n_q + i)*q_row_stride + h*head_dim + e
+ *   k, v bf16, element (b, j, h, e) at k + (b*n_k + j)*kv_row_stride + h*head_dim + e
+ *   out  fp32, element (b, i, h, e) at out + (b*n_q + i)*out_row_stride + h*head_dim + e
+ *   lse  fp32 [batch, heads, n_q], required.
+ * Strides are multiples of 8 (q, k, v; kv_row_stride at most 2^24) and of 4
+ * (out) and at least heads*head_dim; pointers 16-byte aligned (lse 4-byte).
+ * out and lse must not overlap q, k, v or each other.  head_dim 64 or 128. */
+#define DIT_MAX_PARTS 32
+typedef struct dit_partial_desc {
+  int32_t batch;      /* 1..DIT_MAX_BATCH */
+  int32_t n_q;        /* query rows per batch row (>= 1) */
+  int32_t n_k;        /* key rows of this partition per batch row (>= 1) */
+  int32_t heads;
+  int32_t head_dim;   /* 64 or 128 */
+  int32_t k_valid[DIT_MAX_BATCH];  /* valid keys of batch row b: [0, k_valid[b]) */
+} dit_partial_desc;
+
+dit_status dit_attention_partial(const dit_partial_desc* desc, const uint16_t* q,
+                                 int64_t q_row_stride, const uint16_t* k,
+                                 const uint16_t* v, int64_t kv_row_stride, float* out,
+                                 int64_t out_row_stride, float* lse, float softmax_scale,
+                                 hipStream_t stream);
+
+/* dit_attention_merge: joint normalisation of `parts` partials of the same
+ * queries ("Difflet", section 4.3: rescale to a common maximum, add, divide):
+ *   M        = max_p lse_p[b,h,i]
+ *   w_p      = exp(lse_p[b,h,i] - M)
+ *   out      = sum_p w_p out_p[b,i,h,:] / sum_p w_p     (bf16, RNE)
+ *   lse_out  = M + log(sum_p w_p)                        (nullable, fp32)
+ * (With out_p = acc_p / l_p and lse_p = m_p + log l_p this is the page's
+ * (sum_p e^(m_p - M) acc_p) / (sum_p e^(m_p - M) l_p).)
+ *   outs, lses  host arrays of `parts` device pointers laid out as the out
+ *               and lse of dit_attention_partial (part_row_stride for all)
+ *   out         bf16 (b, i, h, e) at out + (b*n_q + i)*out_row_stride + h*head_dim + e
+ * parts in [1, DIT_MAX_PARTS]; every (b, h, i) needs at least one partial
+ * with a valid key (else its row is NaN).  Strides: part_row_stride a
+ * multiple of 4, out_row_stride a multiple of 8, both >= heads*head_dim.
+ * out must not overlap any input. */
+typedef struct dit_merge_desc {
+  int32_t batch, n_q, heads, head_dim, parts;
+} dit_merge_desc;
+
+dit_status dit_attention_merge(const dit_merge_desc* desc, const float* const* outs,
+                               int64_t part_row_stride, const float* const* lses,
+                               uint16_t* out, int64_t out_row_stride, float* lse_out,
+                               hipStream_t stream);
+
 /* Linear layer epilogues (the GEMM of "ChunkFlow" Appendix B equations (13)
  * and (16), with the work around it fused into the store). */
 typedef enum dit_epilogue {

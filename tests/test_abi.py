@@ -68,6 +68,40 @@ def test_attention_argument_errors():
     _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE, FAKE, hd, FAKE * 2, hd, softmax_scale=-1.0, stream=0)
 
 
+def test_partial_attention_and_merge_argument_errors():
+    f = D.dit_attention_partial
+    hd = 128
+    ok = dict(batch=1, n_q=16, n_k=8, heads=1, head_dim=128, k_valid=[8])
+
+    def pd(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return D.partial_desc(a["batch"], a["n_q"], a["n_k"], a["heads"], a["head_dim"], a["k_valid"])
+
+    args = (FAKE, hd, FAKE * 2, FAKE * 3, hd, FAKE * 4, hd, FAKE * 5)
+    _expect("DIT_EINVAL", f, pd(batch=0), *args, stream=0)
+    _expect("DIT_EINVAL", f, pd(n_k=0, k_valid=[0]), *args, stream=0)
+    _expect("DIT_EINVAL", f, pd(k_valid=[9]), *args, stream=0)
+    _expect("DIT_EINVAL", f, pd(k_valid=[-1]), *args, stream=0)
+    _expect("DIT_EUNSUPPORTED", f, pd(head_dim=96), FAKE, 96, FAKE * 2, FAKE * 3, 96, FAKE * 4, 96,
+            FAKE * 5, stream=0)
+    _expect("DIT_EINVAL", f, pd(), FAKE, hd, FAKE * 2, FAKE * 3, hd, FAKE * 4, hd, None, stream=0)
+    _expect("DIT_EINVAL", f, pd(), FAKE, hd, FAKE * 2, FAKE * 3, hd, FAKE * 4, hd - 4, FAKE * 5,
+            stream=0)
+    _expect("DIT_EINVAL", f, pd(), FAKE, hd, FAKE * 2, FAKE * 3, hd, FAKE + 64, hd, FAKE * 5,
+            stream=0)  # out overlaps q
+    _expect("DIT_EUNSUPPORTED", f, pd(), FAKE, hd, FAKE * 2, FAKE * 3, (1 << 24) + 8, FAKE * 4, hd,
+            FAKE * 5, stream=0)
+    m = D.dit_attention_merge
+    _expect("DIT_EINVAL", m, 1, 16, 1, 128, [], hd, [], FAKE, hd, stream=0)
+    _expect("DIT_EINVAL", m, 1, 16, 1, 128, [FAKE] * 33, hd, [FAKE * 2] * 33, FAKE * 3, hd,
+            stream=0)
+    _expect("DIT_EUNSUPPORTED", m, 1, 16, 1, 96, [FAKE], 96, [FAKE * 2], FAKE * 3, 96, stream=0)
+    _expect("DIT_EINVAL", m, 1, 16, 1, 128, [FAKE], hd, [None], FAKE * 3, hd, stream=0)
+    _expect("DIT_EINVAL", m, 1, 16, 1, 128, [FAKE], hd, [FAKE * 2], FAKE + 16, hd, stream=0)
+    _expect("DIT_EINVAL", m, 1, 16, 1, 128, [FAKE], hd - 4, [FAKE * 2], FAKE * 3, hd, stream=0)
+
+
 def test_linear_argument_errors():
     f = D.dit_linear
     _expect("DIT_EUNSUPPORTED", f, FAKE, 96, FAKE * 2, None, 4, 8, 96, D.EPI_BF16, FAKE * 4, 8, stream=0)
