@@ -4,7 +4,10 @@ A plain, slow, fp64 NumPy statement of what one denoising step computes:
 adaLN modulation, QKV projection, Q/K RMSNorm over the full hidden width,
 axial RoPE, joint attention over [visual; valid text] keys with a materialised
 softmax, output projection with a gated residual, a GELU MLP with a gated
-residual, classifier-free guidance and the flow-matching Euler update.
+residual, classifier-free guidance and the flow-matching Euler update; split
+attention with a statistic merge; and step caching (``stepcache``: the skip
+controller, the relative L1 change score, the output estimator and the
+block-0 probe).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
 leg may import this package.  It shares no code with the HIP path and never
@@ -36,7 +39,9 @@ from .dit import (
     timestep_features,
     silu,
     denoise_step,
+    step_tokens,
 )
+from . import stepcache
 
 __all__ = [
     "bf16_decode", "round_bf16", "adaln_modulate", "linear", "rms_norm_full",

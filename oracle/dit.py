@@ -356,6 +356,29 @@ def timestep_features(t, dim):
 # one denoising step of a DiT stack
 # ----------------------------------------------------------------------------
 
+def step_tokens(model, latent, sigma, round_points=True, t_scale=1000.0):
+    """Timestep conditioning and the token sequence a step feeds to its first
+    block (the reading of the parts the pages leave open is stated under
+    ``denoise_step``): s = SiLU(SiLU(sinusoidal(t_scale * sigma) W_t1 + b_t1)
+    W_t2 + b_t2) and, per batch row b, x[b] = [bf16(latent) W_in + b_in;
+    text[b]].  Returns (s [D], x [B, N, D])."""
+    R_ = round_bf16 if round_points else (lambda a: a)
+    shp = model.shape
+    blk = shp.block
+    B, nv, N, D = blk.batch, blk.n_vis, blk.n_tok, blk.hidden
+    sig32 = float(np.float32(sigma))
+    f = R_(timestep_features(float(np.float32(t_scale)) * sig32, shp.freq_dim))
+    c = R_(silu(linear(f, _dec(model.t_w1), _dec(model.t_b1))))
+    s = R_(silu(linear(c, _dec(model.t_w2), _dec(model.t_b2))))
+    lat = np.asarray(latent, dtype=np.float64)
+    xin = linear(R_(lat), _dec(model.in_w), _dec(model.in_b))  # [Bl, n_vis, D]
+    x = np.empty((B, N, D))
+    for b in range(B):
+        x[b, :nv] = xin[0 if shp.cfg else b]
+        x[b, nv:] = _dec(model.text[b])
+    return s, x
+
+
 def denoise_step(model, latent, sigma, sigma_next, guidance, round_points=True, rows=None,
                  t_scale=1000.0):
     """One step of the denoising loop ("Difflet", section 3: the denoiser
@@ -389,15 +412,8 @@ def denoise_step(model, latent, sigma, sigma_next, guidance, round_points=True, 
     B, nv, N, D = blk.batch, blk.n_vis, blk.n_tok, blk.hidden
     cfg = shp.cfg
     sig32 = float(np.float32(sigma))
-    f = R_(timestep_features(float(np.float32(t_scale)) * sig32, shp.freq_dim))
-    c = R_(silu(linear(f, _dec(model.t_w1), _dec(model.t_b1))))
-    s = R_(silu(linear(c, _dec(model.t_w2), _dec(model.t_b2))))
     lat = np.asarray(latent, dtype=np.float64)
-    xin = linear(R_(lat), _dec(model.in_w), _dec(model.in_b))  # [Bl, n_vis, D]
-    x = np.empty((B, N, D))
-    for b in range(B):
-        x[b, :nv] = xin[0 if cfg else b]
-        x[b, nv:] = _dec(model.text[b])
+    s, x = step_tokens(model, lat, sigma, round_points, t_scale)
     if shp.depth > 1 and rows is not None:
         raise ValueError("row subsets are only exact for a single block")
     sel = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
