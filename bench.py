@@ -8,9 +8,10 @@ with gated residual, GELU MLP with gated residual), final adaLN + projection
 and the Euler update -- one call of dit_denoise_step.  Inputs are seeded
 synthetic tensors already resident in HBM.
 
-Prints ONE JSON line: ms/step (the value), the block alone, and joint
+Prints ONE JSON line: ms/step (the value), the block alone, joint
 attention's TFLOP/s against the bf16 dense MFMA peak (the roofline object),
-plus the CPU oracle timed on a bounded sample of the same step.
+split joint attention (a text partial plus 4 visual partials, merged), plus
+the CPU oracle timed on a bounded sample of the same step.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -29,6 +30,35 @@ if ROOT not in sys.path:
 
 METRIC = "DiT block ms/step + joint-attn TFLOP/s (% bf16 MFMA peak) @32760+512 tok"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
+
+# HBM traffic of one c3 joint-attention launch from two rocprofv3 counter
+# passes (FETCH_SIZE, then WRITE_SIZE, of `bench.py --traffic-probe`), scaled
+# by what the same counters read for a plain 1 GiB device copy (FETCH x2.0,
+# WRITE x1.0); summary and commands in profiles/attn_c3_hbm_traffic.md.  Valid
+# only for the kernel source they were taken on.
+ATTN_TRAFFIC = {
+    "source_sha256": "5829bfd7cd02ceadc24e0f0d2f0a45b332671cd728d375c1492812143896b0ba",
+    "fetch_bytes": 3.7187e9,
+    "write_bytes": 0.3434e9,
+    "fetch_scale": 2.0,
+    "write_scale": 1.0,
+    "profile": "profiles/attn_c3_hbm_traffic.md",
+}
+ATTN_SOURCES = ("diffusion_transformer_denoising_dit_amd/csrc/attention.hip",
+                "diffusion_transformer_denoising_dit_amd/csrc/common.h")
+
+
+def attn_traffic():
+    """Counter-measured bytes per attention launch, or None once the kernel
+    source differs from the one the counters were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != ATTN_TRAFFIC["source_sha256"]:
+        return None
+    return ATTN_TRAFFIC
 BLOCK_NAMES = ("w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "w_up", "b_up", "w_dn", "b_dn")
 
 
@@ -38,6 +68,9 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="only launch c3 joint attention --steps times and a plain 1 GiB copy "
+                        "--steps times (for hardware-counter runs), print nothing else")
     p.add_argument("--cpu-rows", type=int, default=64,
                    help="query rows in the CPU oracle's bounded sample")
     return p.parse_args()
@@ -117,6 +150,33 @@ def cpu_baseline(shape, model, n_rows):
             "affinity_cores": len(os.sched_getaffinity(0))}
 
 
+def traffic_probe(steps):
+    """The kernels a hardware-counter pass needs and nothing else: joint
+    attention at the c3 shape (q/k/v as column blocks of one [N, 3*H*d]
+    buffer, as in the block), then a plain device copy of exactly 1 GiB read +
+    1 GiB written, whose FETCH_SIZE / WRITE_SIZE calibrate the counters."""
+    import torch
+
+    import diffusion_transformer_denoising_dit_amd as D
+    from synthetic import configs as C
+    blk = C.C3_STEP.block
+    HD = blk.hidden
+    g = torch.Generator("cuda").manual_seed(5)
+    qkv = torch.randn((blk.batch, blk.n_tok, 3 * HD), generator=g, device="cuda").to(torch.bfloat16)
+    o = torch.empty((blk.batch, blk.n_tok, HD), dtype=torch.bfloat16, device="cuda")
+    adesc = D.attn_desc(blk.batch, blk.n_vis, blk.n_txt, blk.heads, blk.head_dim, [226])
+    for _ in range(steps):
+        D.dit_joint_attention(adesc, qkv, qkv[..., HD:], qkv[..., 2 * HD:], 3 * HD, o, HD)
+    torch.cuda.synchronize()
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[traffic-probe] {steps} attention launches + {steps} copies of 1 GiB done",
+          file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -132,6 +192,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.traffic_probe:
+        traffic_probe(args.steps)
+        return
     shape = C.C3_STEP
     blk = shape.block
     t_gen = time.perf_counter()
@@ -201,6 +264,41 @@ def main():
     a_tflops = a_flop / (ms_attn * 1e-3) / 1e12
     b_flop = block_flops(blk, valid)
 
+    # split joint attention (Difflet, section 4.3): the text keys [0, L) as one
+    # partial plus the visual keys in 4 partitions, each attended by every
+    # query row into fp32 (out, LSE) buffers, then merged to bf16
+    cuts = [round(i * blk.n_vis / 4) for i in range(5)]
+    segs = [(blk.n_vis, blk.n_tok, valid)] + [(a, b, [b - a] * blk.batch)
+                                               for a, b in zip(cuts[:-1], cuts[1:])]
+    p_out = [torch.empty((blk.batch, blk.n_tok, HD), dtype=torch.float32, device="cuda")
+             for _ in segs]
+    p_lse = [torch.empty((blk.batch, blk.heads, blk.n_tok), dtype=torch.float32, device="cuda")
+             for _ in segs]
+    p_desc = [D.partial_desc(blk.batch, blk.n_tok, b - a, blk.heads, blk.head_dim, kv)
+              for a, b, kv in segs]
+    o_split = torch.empty_like(o)
+
+    def split_partials():
+        for (a, b, _), pd, po, pl in zip(segs, p_desc, p_out, p_lse):
+            D.dit_attention_partial(pd, qkv, 3 * HD, qkv[:, a:, HD:], qkv[:, a:, 2 * HD:], 3 * HD,
+                                    po, HD, pl)
+
+    def split_merge():
+        D.dit_attention_merge(blk.batch, blk.n_tok, blk.heads, blk.head_dim, p_out, HD, p_lse,
+                              o_split, HD)
+
+    def split():
+        split_partials()
+        split_merge()
+
+    split()
+    torch.cuda.synchronize()
+    split_err = (o_split.float() - o.float()).abs().max().item()
+    ms_split = timed(split, max(3, args.steps // 2), stream)
+    ms_merge = timed(split_merge, max(5, args.steps), stream)
+    del p_out, p_lse, o_split
+
+    traffic = attn_traffic()
     result = {
         "metric": METRIC,
         "value": round(ms_step, 3),
@@ -230,14 +328,28 @@ def main():
             "algorithmic_tflop": round(a_flop / 1e12, 3),
             "dense_tflop": round(a_dense / 1e12, 3),
         },
+        "split_attention": {
+            "partials": len(segs),
+            "ms": round(ms_split, 3),
+            "merge_ms": round(ms_merge, 3),
+            "tflops": round(a_flop / (ms_split * 1e-3) / 1e12, 1),
+            "max_abs_vs_unsplit": round(split_err, 5),
+        },
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_kernel<128> (joint attention)",
+            "kernel": "attn_kernel<128, false> (joint attention)",
             "achieved": round(a_tflops, 1),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(a_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": (None if traffic is None
+                        else round(traffic["fetch_bytes"] + traffic["write_bytes"])),
+            "traffic_unit": "bytes per launch (L2-to-fabric, counter-measured)",
+            "traffic_detail": None if traffic is None else {
+                "fetch_bytes": traffic["fetch_bytes"], "write_bytes": traffic["write_bytes"],
+                "algorithmic_bytes": 4 * blk.batch * blk.n_tok * HD * 2,
+                "fetch_scale": traffic["fetch_scale"], "write_scale": traffic["write_scale"],
+                "profile": traffic["profile"]},
         },
     }
     if not args.no_cpu_baseline:

@@ -39,6 +39,16 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
+// The attention kernel runs one 512-thread workgroup per (batch row, head,
+// 256-query tile) on a 1-D grid whose size in threads must fit 32 bits.
+dit_status check_attn_grid(int64_t n_q, int32_t heads, int32_t batch) {
+  const int64_t n_wg = (n_q + 255) / 256 * heads * batch;
+  if (n_wg * 512 > 0xffffffffLL)
+    return fail(DIT_EUNSUPPORTED, "%lld attention workgroups (query tiles x heads x batch) exceed "
+                "the 1-D grid limit of %lld", static_cast<long long>(n_wg), 0xffffffffLL / 512);
+  return DIT_OK;
+}
+
 dit_status check_attn_desc(const dit_attn_desc* d) {
   if (!d) return fail(DIT_EINVAL, "attention descriptor is NULL");
   if (d->batch < 1 || d->batch > DIT_MAX_BATCH)
@@ -59,7 +69,7 @@ dit_status check_attn_desc(const dit_attn_desc* d) {
     if (d->n_vis + d->txt_valid[b] < 1)
       return fail(DIT_EINVAL, "batch row %d has no valid key (n_vis 0, txt_valid 0)", b);
   }
-  return DIT_OK;
+  return check_attn_grid(static_cast<int64_t>(d->n_vis) + d->n_txt, d->heads, d->batch);
 }
 
 dit_status check_block_desc(const dit_block_desc* d) {
@@ -416,6 +426,7 @@ dit_status dit_attention_partial(const dit_partial_desc* desc, const uint16_t* q
   for (int b = 0; b < d.batch; ++b)
     if (d.k_valid[b] < 0 || d.k_valid[b] > d.n_k)
       return fail(DIT_EINVAL, "k_valid[%d] = %d outside [0, n_k = %d]", b, d.k_valid[b], d.n_k);
+  if (dit_status st = check_attn_grid(d.n_q, d.heads, d.batch)) return st;
   if (!q || !k || !v || !out || !lse) return fail(DIT_EINVAL, "NULL q, k, v, out or lse");
   const int64_t hd = static_cast<int64_t>(d.heads) * d.head_dim;
   if (q_row_stride < hd || q_row_stride % 8 != 0 || kv_row_stride < hd || kv_row_stride % 8 != 0)

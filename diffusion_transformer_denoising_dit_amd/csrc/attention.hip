@@ -325,7 +325,7 @@ __device__ __forceinline__ void issue_tile(const char* kg0, const char* vg0, int
 // k+1}; finally O += P V of the last tile -- with a barrier before every
 // step.  The second group takes one extra barrier first (and the first group
 // one at the end), which puts it exactly one phase behind.
-template <int D>
+template <int D, bool kOutF32>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   using T = Tile<D>;
   using W = WaveState<D>;
@@ -337,8 +337,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int grp = wave / 4;
   const int hi = lane / 32;
-  const int b = blockIdx.z;
-  const int h = blockIdx.y;
+  // Workgroup -> (batch row, head, query tile).  The dispatcher deals
+  // workgroup ids round-robin over the 8 XCDs, each with its own L2; the ids
+  // are renumbered so that every XCD owns a contiguous run of (row, head)
+  // pairs, query tile fastest.  The workgroups resident on one XCD then share
+  // one head's K/V stream through that L2 (at c3 this halves the L2-miss
+  // bytes of a launch) instead of every XCD streaming every head.
+  int b, h, qt;
+  {
+    const int n_qt = (p.n_q + kBM - 1) / kBM;
+    const int total = n_qt * p.heads * p.batch;
+    const int id = blockIdx.x;
+    const int xcd = id % 8, slot = id / 8;
+    const int per = total / 8, extra = total % 8;
+    const int nid = xcd * per + min(xcd, extra) + slot;
+    qt = nid % n_qt;
+    h = (nid / n_qt) % p.heads;
+    b = nid / (n_qt * p.heads);
+  }
   const int n_q = p.n_q;
   const int n_valid = p.n_valid[b];
   const int n_tiles = (n_valid + kBN - 1) / kBN;  // fully padded tiles are skipped
@@ -347,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   const char* kg0 = reinterpret_cast<const char*>(p.k + kv_base);
   const char* vg0 = reinterpret_cast<const char*>(p.v + kv_base);
   const int64_t stride_bytes = p.kv_stride * 2;
-  const int q_first = blockIdx.x * kBM + wave * 32;
+  const int q_first = qt * kBM + wave * 32;
 
   if (n_tiles == 0) {
     // an empty key range (a partial of split attention whose partition holds
@@ -361,7 +377,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int col = 32 * db + 8 * g + 4 * hi;
-          if (p.out_f32) {
+          if constexpr (kOutF32) {
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
             *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + row + col) = z;
           } else {
@@ -458,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * db + 8 * g + 4 * hi;
-        if (p.out_f32) {
+        if constexpr (kOutF32) {
           f32x4 w;
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[e] = st.o[db][4 * g + e] * inv;
@@ -479,12 +495,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
-  dim3 grid((p.n_q + kBM - 1) / kBM, p.heads, p.batch);
+  const int64_t n_wg = static_cast<int64_t>((p.n_q + kBM - 1) / kBM) * p.heads * p.batch;
+  if (n_wg * kThreads > 0xffffffffLL) return hipErrorInvalidValue;  // grid size in threads is 32-bit
+  dim3 grid(static_cast<unsigned>(n_wg));
   dim3 block(kThreads);
-  if (p.head_dim == 128)
-    hipLaunchKernelGGL(attn_kernel<128>, grid, block, 0, s, p);
+  if (p.head_dim == 128 && !p.out_f32)
+    hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, 0, s, p);
+  else if (p.head_dim == 128)
+    hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, 0, s, p);
+  else if (p.head_dim == 64 && !p.out_f32)
+    hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, 0, s, p);
   else if (p.head_dim == 64)
-    hipLaunchKernelGGL(attn_kernel<64>, grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

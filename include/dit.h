@@ -58,7 +58,9 @@ typedef enum dit_status {
  * routing and mask representation).
  *   batch      1 .. DIT_MAX_BATCH
  *   n_vis      >= 0 visual tokens; n_txt >= 0 text slots; n_vis + n_txt >= 1
- *   heads      >= 1
+ *   heads      >= 1, with ceil((n_vis + n_txt) / 256) * heads * batch at most
+ *              8388607 (one 512-thread workgroup per 256-query tile, head and
+ *              batch row on a 1-D grid; more is DIT_EUNSUPPORTED)
  *   head_dim   64 or 128
  *   txt_valid  host values in [0, n_txt] (entries past `batch` are ignored);
  *              n_vis + txt_valid[b] must be >= 1 so no row is empty. */
@@ -114,7 +116,8 @@ dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q,
  *   lse  fp32 [batch, heads, n_q], required.
  * Strides are multiples of 8 (q, k, v; kv_row_stride at most 2^24) and of 4
  * (out) and at least heads*head_dim; pointers 16-byte aligned (lse 4-byte).
- * out and lse must not overlap q, k, v or each other.  head_dim 64 or 128. */
+ * out and lse must not overlap q, k, v or each other.  head_dim 64 or 128;
+ * ceil(n_q / 256) * heads * batch at most 8388607 (else DIT_EUNSUPPORTED). */
 #define DIT_MAX_PARTS 32
 typedef struct dit_partial_desc {
   int32_t batch;      /* 1..DIT_MAX_BATCH */

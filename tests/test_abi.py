@@ -66,6 +66,9 @@ def test_attention_argument_errors():
     # out aliasing q
     _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE * 4, FAKE * 4, hd, FAKE + 256, hd, stream=0)
     _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE, FAKE, hd, FAKE * 2, hd, softmax_scale=-1.0, stream=0)
+    # query tiles x heads x batch beyond the kernel's 1-D grid (2^30 tokens, 8 heads, 8 rows)
+    _expect("DIT_EUNSUPPORTED", f, _attn(batch=8, n_vis=(1 << 30) - 16, heads=8, valid=[4] * 8),
+            FAKE, FAKE, FAKE, 1024, FAKE * 2, 1024, stream=0)
 
 
 def test_partial_attention_and_merge_argument_errors():
@@ -92,6 +95,9 @@ def test_partial_attention_and_merge_argument_errors():
             stream=0)  # out overlaps q
     _expect("DIT_EUNSUPPORTED", f, pd(), FAKE, hd, FAKE * 2, FAKE * 3, (1 << 24) + 8, FAKE * 4, hd,
             FAKE * 5, stream=0)
+    # query tiles x heads x batch beyond the kernel's 1-D grid
+    _expect("DIT_EUNSUPPORTED", f, pd(batch=8, n_q=1 << 30, heads=2, k_valid=[8] * 8), *args,
+            stream=0)
     m = D.dit_attention_merge
     _expect("DIT_EINVAL", m, 1, 16, 1, 128, [], hd, [], FAKE, hd, stream=0)
     _expect("DIT_EINVAL", m, 1, 16, 1, 128, [FAKE] * 33, hd, [FAKE * 2] * 33, FAKE * 3, hd,
