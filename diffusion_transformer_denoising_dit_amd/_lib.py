@@ -24,8 +24,15 @@ EXPORTED = (
     "dit_block_workspace_bytes", "dit_block_forward", "dit_euler_step",
     "dit_timestep_features", "dit_cast_f32_bf16", "dit_cast_bf16_f32", "dit_debug_positions",
     "dit_denoise_workspace_bytes", "dit_denoise_step",
+    "dit_change_score_workspace_bytes", "dit_change_score", "dit_cache_probe",
+    "dit_denoise_step_cached", "dit_cache_ctrl_init", "dit_cache_ctrl_decide",
+    "dit_cache_ctrl_observe",
     "dit_status_string", "dit_last_error", "dit_version",
 )
+DTYPE_BF16, DTYPE_F32 = 0, 1
+STEP_FULL, STEP_SKIP = 0, 1
+CACHE_OFF, CACHE_CADENCE, CACHE_ONLINE_DELTA, CACHE_TEACACHE = range(4)
+CACHE_MAX_COEF = 8
 
 
 class DitError(RuntimeError):
@@ -92,6 +99,20 @@ class ModelWeights(ctypes.Structure):
         ("mod_b", ctypes.POINTER(ctypes.c_void_p))]
 
 
+class CachePolicy(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("n_steps", ctypes.c_int32), ("warmup", ctypes.c_int32),
+                ("cooldown", ctypes.c_int32), ("cadence", ctypes.c_int32), ("n_coef", ctypes.c_int32),
+                ("alpha", ctypes.c_double), ("threshold", ctypes.c_double),
+                ("coef", ctypes.c_double * CACHE_MAX_COEF)]
+
+
+class CacheCtrl(ctypes.Structure):
+    _fields_ = [("policy", CachePolicy), ("next_step", ctypes.c_int32), ("n_full", ctypes.c_int32),
+                ("last_skipped", ctypes.c_int32), ("skip_next", ctypes.c_int32),
+                ("have_first", ctypes.c_int32), ("first_change", ctypes.c_double),
+                ("acc", ctypes.c_double)]
+
+
 _lib = None
 
 
@@ -125,6 +146,17 @@ def lib() -> ctypes.CDLL:
             "dit_denoise_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(ModelDesc)]),
             "dit_denoise_step": (st, [ctypes.POINTER(ModelDesc), ctypes.POINTER(ModelWeights), vp, f32,
                                       f32, f32, vp, ctypes.c_size_t, vp]),
+            "dit_change_score_workspace_bytes": (ctypes.c_size_t, []),
+            "dit_change_score": (st, [vp, vp, i32, i64, i32, vp, vp, ctypes.c_size_t, vp]),
+            "dit_cache_probe": (st, [ctypes.POINTER(ModelDesc), ctypes.POINTER(ModelWeights), vp, f32,
+                                     vp, i32, vp, vp, ctypes.c_size_t, vp]),
+            "dit_denoise_step_cached": (st, [ctypes.POINTER(ModelDesc), ctypes.POINTER(ModelWeights), vp,
+                                             f32, f32, f32, i32, i32, vp, vp, vp, vp, ctypes.c_size_t,
+                                             vp]),
+            "dit_cache_ctrl_init": (st, [ctypes.POINTER(CacheCtrl), ctypes.POINTER(CachePolicy)]),
+            "dit_cache_ctrl_decide": (st, [ctypes.POINTER(CacheCtrl), i32, f32,
+                                           ctypes.POINTER(ctypes.c_int32)]),
+            "dit_cache_ctrl_observe": (st, [ctypes.POINTER(CacheCtrl), f32]),
             "dit_status_string": (ctypes.c_char_p, [st]),
             "dit_last_error": (ctypes.c_char_p, []),
             "dit_version": (ctypes.c_char_p, []),
@@ -310,3 +342,58 @@ def dit_denoise_step(desc: ModelDesc, weights: ModelWeights, latent, sigma, sigm
     _check(lib().dit_denoise_step(ctypes.byref(desc), ctypes.byref(weights), _ptr(latent), sigma,
                                   sigma_next, guidance, _ptr(workspace), workspace_bytes,
                                   _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# step caching
+
+def dit_change_score_workspace_bytes() -> int:
+    return int(lib().dit_change_score_workspace_bytes())
+
+
+def dit_change_score(cur, prev, dtype, n, update, score, workspace, workspace_bytes, stream=None):
+    _check(lib().dit_change_score(_ptr(cur), _ptr(prev), dtype, n, int(update), _ptr(score),
+                                  _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def dit_cache_probe(desc, weights, latent, sigma, saved, have_saved, score, workspace,
+                    workspace_bytes, stream=None):
+    _check(lib().dit_cache_probe(ctypes.byref(desc), ctypes.byref(weights), _ptr(latent), sigma,
+                                 _ptr(saved), int(have_saved), _ptr(score), _ptr(workspace),
+                                 workspace_bytes, _stream(stream)))
+
+
+def dit_denoise_step_cached(desc, weights, latent, sigma, sigma_next, guidance, action, have_prev,
+                            prev_v, delta_v, score, workspace, workspace_bytes, stream=None):
+    _check(lib().dit_denoise_step_cached(ctypes.byref(desc), ctypes.byref(weights), _ptr(latent),
+                                         sigma, sigma_next, guidance, action, int(have_prev),
+                                         _ptr(prev_v), _ptr(delta_v), _ptr(score), _ptr(workspace),
+                                         workspace_bytes, _stream(stream)))
+
+
+def cache_policy(mode, n_steps, warmup=0, cooldown=0, cadence=2, alpha=0.6, threshold=0.0,
+                 coef=(1.0, 0.0)) -> CachePolicy:
+    p = CachePolicy()
+    p.mode, p.n_steps, p.warmup, p.cooldown, p.cadence = mode, n_steps, warmup, cooldown, cadence
+    p.alpha, p.threshold = alpha, threshold
+    p.n_coef = len(coef)
+    for i, c in enumerate(list(coef)[:CACHE_MAX_COEF]):
+        p.coef[i] = c
+    return p
+
+
+class CacheController:
+    """The library's host-side step-cache controller (dit_cache_ctrl_*)."""
+
+    def __init__(self, policy: CachePolicy):
+        self.state = CacheCtrl()
+        _check(lib().dit_cache_ctrl_init(ctypes.byref(self.state), ctypes.byref(policy)))
+
+    def decide(self, step, probe_score=float("inf")) -> int:
+        a = ctypes.c_int32()
+        _check(lib().dit_cache_ctrl_decide(ctypes.byref(self.state), step, probe_score,
+                                           ctypes.byref(a)))
+        return a.value
+
+    def observe(self, output_change):
+        _check(lib().dit_cache_ctrl_observe(ctypes.byref(self.state), output_change))

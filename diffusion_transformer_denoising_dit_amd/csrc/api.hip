@@ -275,7 +275,7 @@ hipError_t block_launch(const dit_block_desc* desc, const dit_block_weights* w, 
 // residual stream x, the final-norm output, the velocity and the block's own
 // workspace.
 struct StepLayout {
-  size_t feat, c, s, mod, fin, lat, x, hf, v, blk, total;
+  size_t feat, c, s, mod, fin, lat, x, hf, v, part, blk, total;
 };
 
 StepLayout step_layout(const dit_model_desc* m) {
@@ -294,6 +294,7 @@ StepLayout step_layout(const dit_model_desc* m) {
   L.x = o; o += align256(B * N * D * 4);
   L.hf = o; o += align256(B * N * D * 2);
   L.v = o; o += align256(B * nv * C * 2);
+  L.part = o; o += align256(dit::kScorePartialBytes);
   L.blk = o; o += ws_layout(&b).total;
   L.total = o;
   return L;
@@ -657,9 +658,21 @@ size_t dit_denoise_workspace_bytes(const dit_model_desc* desc) {
   return step_layout(desc).total;
 }
 
-dit_status dit_denoise_step(const dit_model_desc* desc, const dit_model_weights* w, float* latent,
-                            float sigma, float sigma_next, float guidance, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+#define DIT_TRY(expr, what)                            \
+  do {                                                 \
+    const hipError_t e_ = (expr);                      \
+    if (e_ != hipSuccess) return hip_status(e_, what); \
+  } while (0)
+
+// Argument checks shared by the denoising-step entry points: descriptor,
+// weights, latent, scalars and workspace.
+dit_status check_step_args(const dit_model_desc* desc, const dit_model_weights* w,
+                           const float* latent, float sigma, float sigma_next, float guidance,
+                           void* workspace, size_t workspace_bytes, StepLayout* L) {
   dit_status st = check_model_desc(desc);
   if (st != DIT_OK) return st;
   if (!w) return fail(DIT_EINVAL, "model weights are NULL");
@@ -678,43 +691,38 @@ dit_status dit_denoise_step(const dit_model_desc* desc, const dit_model_weights*
   if (!std::isfinite(sigma) || !std::isfinite(sigma_next) || !std::isfinite(guidance))
     return fail(DIT_EINVAL, "sigma, sigma_next and guidance must be finite");
   if (!workspace || !aligned(workspace, 256)) return fail(DIT_EINVAL, "workspace is NULL or not 256-byte aligned");
-  const StepLayout L = step_layout(desc);
-  if (workspace_bytes < L.total)
-    return fail(DIT_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, L.total);
+  *L = step_layout(desc);
+  if (workspace_bytes < L->total)
+    return fail(DIT_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, L->total);
+  const dit_block_desc& bd = desc->block;
+  const size_t lat_bytes = static_cast<size_t>(desc->cfg ? 1 : bd.attn.batch) * bd.attn.n_vis *
+                           desc->latent_channels * 4;
+  if (overlap(latent, lat_bytes, workspace, L->total))
+    return fail(DIT_EINVAL, "latent overlaps the workspace");
+  return DIT_OK;
+}
 
-  dit_block_desc bd = desc->block;
-  bd.mod_stride = 0;  // one modulation vector per step, shared by every batch row
+// Timestep conditioning s and the first block's input tokens x:
+//   f = sinusoidal(t_scale * sigma);  c = SiLU(f W1 + b1);  s = SiLU(c W2 + b2)
+//   x[b] = [bf16(latent) W_in + b_in ; text[b]]
+dit_status step_prologue(const dit_model_desc* desc, const dit_model_weights* w,
+                         const float* latent, float sigma, const StepLayout& L, char* ws,
+                         hipStream_t stream) {
+  const dit_block_desc& bd = desc->block;
   const int B = bd.attn.batch, nv = bd.attn.n_vis;
   const int64_t N = static_cast<int64_t>(nv) + bd.attn.n_txt;
   const int D = bd.hidden, C = desc->latent_channels, Fq = desc->freq_dim;
   const int Bl = desc->cfg ? 1 : B;
-  if (overlap(latent, static_cast<size_t>(Bl) * nv * C * 4, workspace, L.total))
-    return fail(DIT_EINVAL, "latent overlaps the workspace");
-  char* ws = static_cast<char*>(workspace);
   uint16_t* feat = reinterpret_cast<uint16_t*>(ws + L.feat);
   uint16_t* cbuf = reinterpret_cast<uint16_t*>(ws + L.c);
   uint16_t* sbuf = reinterpret_cast<uint16_t*>(ws + L.s);
-  uint16_t* mod = reinterpret_cast<uint16_t*>(ws + L.mod);
-  uint16_t* fin = reinterpret_cast<uint16_t*>(ws + L.fin);
   uint16_t* lat = reinterpret_cast<uint16_t*>(ws + L.lat);
   float* x = reinterpret_cast<float*>(ws + L.x);
-  uint16_t* hf = reinterpret_cast<uint16_t*>(ws + L.hf);
-  uint16_t* v = reinterpret_cast<uint16_t*>(ws + L.v);
-  char* blk = ws + L.blk;
-
-#define DIT_TRY(expr, what)                            \
-  do {                                                 \
-    const hipError_t e_ = (expr);                      \
-    if (e_ != hipSuccess) return hip_status(e_, what); \
-  } while (0)
-
-  // timestep conditioning: f -> c = SiLU(f W1 + b1) -> s = SiLU(c W2 + b2)
   DIT_TRY(dit::launch_timestep_features(nullptr, sigma, 1, Fq, desc->t_scale, feat, stream), "step: timestep");
   DIT_TRY(dit::launch_gemm(gemm(feat, Fq, w->t_w1, w->t_b1, 1, D, Fq, cbuf, D), DIT_EPI_SILU_BF16, stream),
           "step: t-mlp 1");
   DIT_TRY(dit::launch_gemm(gemm(cbuf, D, w->t_w2, w->t_b2, 1, D, D, sbuf, D), DIT_EPI_SILU_BF16, stream),
           "step: t-mlp 2");
-  // tokens: projected latent rows, then the text rows of each batch row
   DIT_TRY(dit::launch_cast_f32_bf16(latent, C, static_cast<int64_t>(Bl) * nv, C, lat, C, stream),
           "step: latent cast");
   {
@@ -728,7 +736,25 @@ dit_status dit_denoise_step(const dit_model_desc* desc, const dit_model_weights*
     DIT_TRY(dit::launch_cast_bf16_f32(w->text + static_cast<int64_t>(b) * bd.attn.n_txt * D, D,
                                       bd.attn.n_txt, D, x + (b * N + nv) * D, D, stream),
             "step: text rows");
-  // the block stack
+  return DIT_OK;
+}
+
+// The block stack on x, the final adaLN and the projection of the visual rows
+// to the latent channels: v bf16 [batch, n_vis, C] in the workspace.
+dit_status step_denoiser(const dit_model_desc* desc, const dit_model_weights* w,
+                         const StepLayout& L, char* ws, hipStream_t stream) {
+  dit_block_desc bd = desc->block;
+  bd.mod_stride = 0;  // one modulation vector per step, shared by every batch row
+  const int B = bd.attn.batch, nv = bd.attn.n_vis;
+  const int64_t N = static_cast<int64_t>(nv) + bd.attn.n_txt;
+  const int D = bd.hidden, C = desc->latent_channels;
+  uint16_t* sbuf = reinterpret_cast<uint16_t*>(ws + L.s);
+  uint16_t* mod = reinterpret_cast<uint16_t*>(ws + L.mod);
+  uint16_t* fin = reinterpret_cast<uint16_t*>(ws + L.fin);
+  float* x = reinterpret_cast<float*>(ws + L.x);
+  uint16_t* hf = reinterpret_cast<uint16_t*>(ws + L.hf);
+  uint16_t* v = reinterpret_cast<uint16_t*>(ws + L.v);
+  char* blk = ws + L.blk;
   for (int l = 0; l < desc->depth; ++l) {
     DIT_TRY(dit::launch_gemm(gemm(sbuf, D, w->mod_w[l], w->mod_b[l], 1, 6 * D, D, mod, 6 * D),
                              DIT_EPI_BF16, stream),
@@ -737,26 +763,234 @@ dit_status dit_denoise_step(const dit_model_desc* desc, const dit_model_weights*
     const hipError_t e = block_launch(&bd, &w->blocks[l], mod, 0, x, blk, stream, &what);
     if (e != hipSuccess) return hip_status(e, what);
   }
-  // final adaLN and projection of the visual rows to the latent channels
   DIT_TRY(dit::launch_gemm(gemm(sbuf, D, w->fin_w, w->fin_b, 1, 2 * D, D, fin, 2 * D), DIT_EPI_BF16, stream),
           "step: final modulation");
   DIT_TRY(dit::launch_adaln(x, B * N, D, N, fin, fin + D, 0, bd.ln_eps, hf, stream), "step: final adaln");
-  {
-    dit::GemmParams g = gemm(hf, D, w->out_w, w->out_b, static_cast<int64_t>(B) * nv, C, D, v, C);
-    g.group_rows = nv;
-    g.a_group_stride = N * D;
-    g.c_group_stride = static_cast<int64_t>(nv) * C;
-    DIT_TRY(dit::launch_gemm(g, DIT_EPI_BF16, stream), "step: output projection");
-  }
+  dit::GemmParams g = gemm(hf, D, w->out_w, w->out_b, static_cast<int64_t>(B) * nv, C, D, v, C);
+  g.group_rows = nv;
+  g.a_group_stride = N * D;
+  g.c_group_stride = static_cast<int64_t>(nv) * C;
+  DIT_TRY(dit::launch_gemm(g, DIT_EPI_BF16, stream), "step: output projection");
+  return DIT_OK;
+}
+
+// Elements of the velocity the sampler uses (and of the latent).
+int64_t step_velocity_elems(const dit_model_desc* desc) {
+  const dit_block_desc& bd = desc->block;
+  return static_cast<int64_t>(desc->cfg ? 1 : bd.attn.batch) * bd.attn.n_vis * desc->latent_channels;
+}
+
+// Host-side skip decision of a step-caching controller.  Every quantity is
+// double and evaluated without contraction so that the decision does not
+// depend on the compiler's choice of fused multiply-adds.
+double cache_rescale(const dit_cache_policy& p, double r) {
+#pragma clang fp contract(off)
+  double y = 0.0;
+  for (int i = 0; i < p.n_coef; ++i) y = y * r + p.coef[i];
+  return y;
+}
+
+}  // namespace
+
+extern "C" {
+
+dit_status dit_denoise_step(const dit_model_desc* desc, const dit_model_weights* w, float* latent,
+                            float sigma, float sigma_next, float guidance, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  StepLayout L;
+  dit_status st = check_step_args(desc, w, latent, sigma, sigma_next, guidance, workspace,
+                                  workspace_bytes, &L);
+  if (st != DIT_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  if ((st = step_prologue(desc, w, latent, sigma, L, ws, stream)) != DIT_OK) return st;
+  if ((st = step_denoiser(desc, w, L, ws, stream)) != DIT_OK) return st;
   // guidance + Euler on the fp32 latent
-  const int64_t n_lat = static_cast<int64_t>(nv) * C;
+  const uint16_t* v = reinterpret_cast<const uint16_t*>(ws + L.v);
+  const int64_t n = step_velocity_elems(desc);
   if (desc->cfg)
-    DIT_TRY(dit::launch_euler(latent, v, v + n_lat, n_lat, guidance, sigma_next - sigma, stream), "step: euler");
+    DIT_TRY(dit::launch_euler(latent, v, v + n, n, guidance, sigma_next - sigma, stream), "step: euler");
   else
-    DIT_TRY(dit::launch_euler(latent, v, nullptr, static_cast<int64_t>(B) * n_lat, 1.f, sigma_next - sigma, stream),
-            "step: euler");
-#undef DIT_TRY
+    DIT_TRY(dit::launch_euler(latent, v, nullptr, n, 1.f, sigma_next - sigma, stream), "step: euler");
   return ok();
 }
+
+size_t dit_change_score_workspace_bytes(void) { return dit::kScorePartialBytes; }
+
+dit_status dit_change_score(const void* cur, void* prev, int32_t dtype, int64_t n, int32_t update,
+                            float* score, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  if (dtype != DIT_DTYPE_BF16 && dtype != DIT_DTYPE_F32)
+    return fail(DIT_EINVAL, "dtype %d is neither DIT_DTYPE_BF16 nor DIT_DTYPE_F32", dtype);
+  if (n < 1) return fail(DIT_EINVAL, "n %lld < 1", static_cast<long long>(n));
+  if (update != 0 && update != 1) return fail(DIT_EINVAL, "update must be 0 or 1");
+  if (!cur || !prev || !score || !workspace) return fail(DIT_EINVAL, "NULL cur, prev, score or workspace");
+  if (!aligned(cur, 16) || !aligned(prev, 16) || !aligned(score, 4) || !aligned(workspace, 16))
+    return fail(DIT_EINVAL, "cur, prev and workspace must be 16-byte aligned, score 4-byte");
+  if (workspace_bytes < dit::kScorePartialBytes)
+    return fail(DIT_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, dit::kScorePartialBytes);
+  const size_t bytes = static_cast<size_t>(n) * (dtype == DIT_DTYPE_BF16 ? 2 : 4);
+  if (update && overlap(cur, bytes, prev, bytes))
+    return fail(DIT_EINVAL, "cur and prev overlap (prev is overwritten)");
+  if (overlap(score, 4, cur, bytes) || overlap(score, 4, prev, bytes) ||
+      overlap(workspace, dit::kScorePartialBytes, cur, bytes) ||
+      overlap(workspace, dit::kScorePartialBytes, prev, bytes) ||
+      overlap(workspace, dit::kScorePartialBytes, score, 4))
+    return fail(DIT_EINVAL, "score or workspace overlaps an array");
+  return hip_status(dit::launch_change_score(cur, prev, dtype == DIT_DTYPE_BF16, n, update != 0,
+                                             static_cast<float*>(workspace), score, stream),
+                    "change-score launch");
+}
+
+dit_status dit_cache_probe(const dit_model_desc* desc, const dit_model_weights* w,
+                           const float* latent, float sigma, uint16_t* saved, int32_t have_saved,
+                           float* score, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  StepLayout L;
+  dit_status st = check_step_args(desc, w, latent, sigma, sigma, 1.f, workspace, workspace_bytes, &L);
+  if (st != DIT_OK) return st;
+  if (have_saved != 0 && have_saved != 1) return fail(DIT_EINVAL, "have_saved must be 0 or 1");
+  if (!saved || !score || !aligned(saved, 16) || !aligned(score, 4))
+    return fail(DIT_EINVAL, "saved (16-byte aligned) and score must not be NULL");
+  const dit_block_desc& bd = desc->block;
+  const int64_t rows = static_cast<int64_t>(bd.attn.batch) * (static_cast<int64_t>(bd.attn.n_vis) + bd.attn.n_txt);
+  const int D = bd.hidden;
+  const size_t feat_bytes = static_cast<size_t>(rows) * D * 2;
+  if (overlap(saved, feat_bytes, workspace, L.total) || overlap(score, 4, workspace, L.total) ||
+      overlap(score, 4, saved, feat_bytes))
+    return fail(DIT_EINVAL, "saved or score overlaps the workspace or each other");
+  char* ws = static_cast<char*>(workspace);
+  if ((st = step_prologue(desc, w, latent, sigma, L, ws, stream)) != DIT_OK) return st;
+  uint16_t* sbuf = reinterpret_cast<uint16_t*>(ws + L.s);
+  uint16_t* mod = reinterpret_cast<uint16_t*>(ws + L.mod);
+  const float* x = reinterpret_cast<const float*>(ws + L.x);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.hf);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  const int64_t N = static_cast<int64_t>(bd.attn.n_vis) + bd.attn.n_txt;
+  // block 0's modulation and its first adaLN: h = LN(x) (1 + scale1) + shift1
+  DIT_TRY(dit::launch_gemm(gemm(sbuf, D, w->mod_w[0], w->mod_b[0], 1, 6 * D, D, mod, 6 * D),
+                           DIT_EPI_BF16, stream),
+          "probe: modulation");
+  DIT_TRY(dit::launch_adaln(x, rows, D, N, mod, mod + D, 0, bd.ln_eps, h, stream), "probe: adaln");
+  if (have_saved)
+    DIT_TRY(dit::launch_change_score(h, saved, true, rows * D, true, part, score, stream), "probe: score");
+  else {
+    DIT_TRY(hipMemcpyAsync(saved, h, feat_bytes, hipMemcpyDeviceToDevice, stream), "probe: save");
+    DIT_TRY(dit::launch_score_invalid(part, score, stream), "probe: score");
+  }
+  return ok();
+}
+
+dit_status dit_denoise_step_cached(const dit_model_desc* desc, const dit_model_weights* w,
+                                   float* latent, float sigma, float sigma_next, float guidance,
+                                   int32_t action, int32_t have_prev, float* prev_v,
+                                   float* delta_v, float* score, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  StepLayout L;
+  dit_status st = check_step_args(desc, w, latent, sigma, sigma_next, guidance, workspace,
+                                  workspace_bytes, &L);
+  if (st != DIT_OK) return st;
+  if (action != DIT_STEP_FULL && action != DIT_STEP_SKIP)
+    return fail(DIT_EINVAL, "action %d is neither DIT_STEP_FULL nor DIT_STEP_SKIP", action);
+  if (have_prev != 0 && have_prev != 1) return fail(DIT_EINVAL, "have_prev must be 0 or 1");
+  if (action == DIT_STEP_SKIP && !have_prev)
+    return fail(DIT_EINVAL, "a cached step needs a previous output and a measured change");
+  if (!prev_v || !delta_v || !aligned(prev_v, 16) || !aligned(delta_v, 16))
+    return fail(DIT_EINVAL, "prev_v and delta_v must be non-NULL and 16-byte aligned");
+  if (score && !aligned(score, 4)) return fail(DIT_EINVAL, "score must be 4-byte aligned");
+  const int64_t n = step_velocity_elems(desc);
+  const size_t vb = static_cast<size_t>(n) * 4;
+  if (overlap(prev_v, vb, delta_v, vb) || overlap(prev_v, vb, latent, vb) ||
+      overlap(delta_v, vb, latent, vb) || overlap(prev_v, vb, workspace, L.total) ||
+      overlap(delta_v, vb, workspace, L.total) ||
+      (score && (overlap(score, 4, workspace, L.total) || overlap(score, 4, prev_v, vb) ||
+                 overlap(score, 4, delta_v, vb) || overlap(score, 4, latent, vb))))
+    return fail(DIT_EINVAL, "latent, prev_v, delta_v, score and workspace must not overlap");
+  char* ws = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  const float dt = sigma_next - sigma;
+  if (action == DIT_STEP_SKIP) {
+    DIT_TRY(dit::launch_cached_velocity(latent, nullptr, nullptr, n, 1.f, dt, prev_v, delta_v, true,
+                                        true, part, nullptr, stream),
+            "cached step: estimate");
+    return ok();
+  }
+  if ((st = step_prologue(desc, w, latent, sigma, L, ws, stream)) != DIT_OK) return st;
+  if ((st = step_denoiser(desc, w, L, ws, stream)) != DIT_OK) return st;
+  const uint16_t* v = reinterpret_cast<const uint16_t*>(ws + L.v);
+  DIT_TRY(dit::launch_cached_velocity(latent, v, desc->cfg ? v + n : nullptr, n,
+                                      desc->cfg ? guidance : 1.f, dt, prev_v, delta_v, false,
+                                      have_prev != 0, part, score, stream),
+          "cached step: full");
+  return ok();
+}
+
+dit_status dit_cache_ctrl_init(dit_cache_ctrl* c, const dit_cache_policy* p) {
+  if (!c || !p) return fail(DIT_EINVAL, "NULL controller or policy");
+  if (p->mode < DIT_CACHE_OFF || p->mode > DIT_CACHE_TEACACHE)
+    return fail(DIT_EINVAL, "unknown cache mode %d", p->mode);
+  if (p->n_steps < 1) return fail(DIT_EINVAL, "n_steps %d < 1", p->n_steps);
+  if (p->warmup < 0 || p->cooldown < 0) return fail(DIT_EINVAL, "negative warmup or cooldown");
+  if (p->mode == DIT_CACHE_CADENCE && p->cadence < 1) return fail(DIT_EINVAL, "cadence %d < 1", p->cadence);
+  if (p->mode == DIT_CACHE_ONLINE_DELTA && !(p->alpha >= 0.0 && std::isfinite(p->alpha)))
+    return fail(DIT_EINVAL, "alpha must be finite and >= 0");
+  if (p->mode == DIT_CACHE_TEACACHE) {
+    if (!std::isfinite(p->threshold)) return fail(DIT_EINVAL, "threshold must be finite");
+    if (p->n_coef < 1 || p->n_coef > DIT_CACHE_MAX_COEF)
+      return fail(DIT_EINVAL, "n_coef %d outside [1, %d]", p->n_coef, DIT_CACHE_MAX_COEF);
+    for (int i = 0; i < p->n_coef; ++i)
+      if (!std::isfinite(p->coef[i])) return fail(DIT_EINVAL, "coefficient %d is not finite", i);
+  }
+  std::memset(c, 0, sizeof(*c));
+  c->policy = *p;
+  return ok();
+}
+
+dit_status dit_cache_ctrl_decide(dit_cache_ctrl* c, int32_t step, float probe_score, int32_t* action) {
+  if (!c || !action) return fail(DIT_EINVAL, "NULL controller or action");
+  if (step != c->next_step)
+    return fail(DIT_EINVAL, "steps must be decided in order: expected %d, got %d", c->next_step, step);
+  if (step >= c->policy.n_steps) return fail(DIT_EINVAL, "step %d past n_steps %d", step, c->policy.n_steps);
+  const dit_cache_policy& p = c->policy;
+  c->next_step = step + 1;
+  const bool boundary = step < p.warmup || step >= p.n_steps - p.cooldown;
+  const bool allowed = !boundary && c->n_full >= 2;
+  bool skip = false;
+  switch (p.mode) {
+    case DIT_CACHE_OFF: break;
+    case DIT_CACHE_CADENCE: skip = allowed && (step - p.warmup) % p.cadence != 0; break;
+    case DIT_CACHE_ONLINE_DELTA: skip = allowed && !c->last_skipped && c->skip_next; break;
+    case DIT_CACHE_TEACACHE:
+      if (std::isfinite(probe_score)) {
+        c->acc = c->acc + cache_rescale(p, static_cast<double>(probe_score));
+        skip = allowed && c->acc < p.threshold;
+      }
+      break;
+  }
+  if (skip) {
+    c->last_skipped = 1;
+    c->skip_next = 0;
+    *action = DIT_STEP_SKIP;
+  } else {
+    c->last_skipped = 0;
+    c->acc = 0.0;
+    ++c->n_full;
+    *action = DIT_STEP_FULL;
+  }
+  return ok();
+}
+
+dit_status dit_cache_ctrl_observe(dit_cache_ctrl* c, float output_change) {
+  if (!c) return fail(DIT_EINVAL, "NULL controller");
+  if (c->policy.mode != DIT_CACHE_ONLINE_DELTA || !std::isfinite(output_change)) return ok();
+  const double v = static_cast<double>(output_change);
+  if (!c->have_first) {
+    c->first_change = v;
+    c->have_first = 1;
+  }
+  c->skip_next = v < c->policy.alpha * c->first_change;
+  return ok();
+}
+
+#undef DIT_TRY
 
 }  // extern "C"

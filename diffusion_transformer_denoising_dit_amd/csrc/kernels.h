@@ -72,6 +72,23 @@ hipError_t launch_positions(const RopeParams& p, int32_t* out, hipStream_t s);
 
 hipError_t launch_euler(float* x, const uint16_t* vc, const uint16_t* vu, int64_t n, float g,
                         float dt, hipStream_t s);
+
+// Step caching.  Streaming passes use at most kScoreBlocks workgroups, each
+// leaving two fp32 partial sums in `partials` (kScorePartialBytes).
+constexpr int kScoreBlocks = 1024;
+constexpr size_t kScorePartialBytes = 2 * kScoreBlocks * sizeof(float);
+// score = sum|cur - prev| / sum|prev| (bf16 or fp32 arrays of n elements);
+// with update, prev <- cur in the same pass.
+hipError_t launch_change_score(const void* cur, void* prev, bool bf16, int64_t n, bool update,
+                               float* partials, float* score, hipStream_t s);
+// score = +inf (nothing to compare with).
+hipError_t launch_score_invalid(float* partials, float* score, hipStream_t s);
+// Full step (skip false): v = guided velocity, delta = v - prev and the change
+// score when have_prev, prev = v, x += dt v.  Skip: v = prev + delta,
+// prev = v, x += dt v.  score may be null (not computed).
+hipError_t launch_cached_velocity(float* x, const uint16_t* vc, const uint16_t* vu, int64_t n,
+                                  float g, float dt, float* prev, float* delta, bool skip,
+                                  bool have_prev, float* partials, float* score, hipStream_t s);
 hipError_t launch_timestep_features(const float* sigma, float sigma0, int n, int dim,
                                     float t_scale, uint16_t* out, hipStream_t s);
 hipError_t launch_cast_f32_bf16(const float* in, int64_t ld_in, int64_t rows, int cols,

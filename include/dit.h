@@ -345,6 +345,109 @@ dit_status dit_denoise_step(const dit_model_desc* desc, const dit_model_weights*
                             float guidance, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Step caching ("Difflet", section 5 Adaptive Step Caching on Trainium;
+ * "Difflet Engineering Report", DiT caching: adaptive TeaCache, online delta,
+ * and fixed cadence; "19. Diffusion, Image, Video, and World Models", Inside
+ * TeaCache's skip decision).
+ *
+ * Nearby steps give similar denoiser outputs, so some full denoiser calls are
+ * replaced by an estimate.  The device side keeps two fp32 arrays the size of
+ * the velocity -- prev_v (the previously used velocity, possibly an estimate)
+ * and delta_v (the most recently measured change) -- and reports one fp32
+ * change score per call; the decision to skip is taken on the host by a
+ * controller (dit_cache_ctrl_*) from those scores.  The relative L1 change of
+ * cur against prev is sum|cur - prev| / sum|prev| (0 if both sums are 0,
+ * +inf if only the reference sum is 0). */
+
+typedef enum dit_dtype { DIT_DTYPE_BF16 = 0, DIT_DTYPE_F32 = 1 } dit_dtype;
+
+/* Relative L1 change of cur against prev (n >= 1 elements of `dtype`),
+ * written to *score (fp32, device).  With update = 1, prev <- cur in the same
+ * pass (cur and prev must not overlap then).  The sum is deterministic: a
+ * fixed partition of the elements that depends on n alone, fp32 partial sums,
+ * a final sum in double.  cur, prev and workspace 16-byte aligned; workspace
+ * >= dit_change_score_workspace_bytes() (partial sums; caller-owned). */
+size_t dit_change_score_workspace_bytes(void);
+dit_status dit_change_score(const void* cur, void* prev, int32_t dtype, int64_t n,
+                            int32_t update, float* score, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* The probe of calibrated adaptive caching: the change of block 0's modulated
+ * input between this call and the previous one.  Runs the step's timestep
+ * conditioning and input tokens (as dit_denoise_step), layer 0's modulation
+ * and its first adaLN, h = LN(x) (1 + scale1) + shift1 for every token
+ * (bf16 [batch, n_vis + n_txt, hidden]); then *score = relative L1 change of
+ * h against `saved` and saved <- h.  have_saved = 0 (no previous features)
+ * copies h into saved and writes *score = +inf, which forces a full step in
+ * any threshold controller.  Only layer 0's block and modulation weights are
+ * read.  Workspace as dit_denoise_step. */
+dit_status dit_cache_probe(const dit_model_desc* desc, const dit_model_weights* w,
+                           const float* latent, float sigma, uint16_t* saved,
+                           int32_t have_saved, float* score, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* One denoising step under step caching.  With v the guided velocity of the
+ * step (v_uncond + g (v_cond - v_uncond) with cfg, else the prediction):
+ *   DIT_STEP_FULL: run the denoiser exactly as dit_denoise_step; if have_prev,
+ *                  delta_v = v - prev_v and *score = relative L1 change of v
+ *                  against prev_v (else *score = +inf); prev_v = v;
+ *                  latent += (sigma_next - sigma) v
+ *   DIT_STEP_SKIP: no denoiser call; v = prev_v + delta_v; prev_v = v;
+ *                  latent += (sigma_next - sigma) v   (needs have_prev = 1:
+ *                  two completed full steps; *score untouched)
+ * prev_v, delta_v: fp32 [cfg ? 1 : batch, n_vis, latent_channels], 16-byte
+ * aligned, caller-owned state of one generation; score nullable. */
+typedef enum dit_step_action { DIT_STEP_FULL = 0, DIT_STEP_SKIP = 1 } dit_step_action;
+dit_status dit_denoise_step_cached(const dit_model_desc* desc, const dit_model_weights* w,
+                                   float* latent, float sigma, float sigma_next,
+                                   float guidance, int32_t action, int32_t have_prev,
+                                   float* prev_v, float* delta_v, float* score,
+                                   void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* The host controller (no device work, no allocation; the struct is caller
+ * state for one generation).  Steps are decided in order 0 .. n_steps-1.
+ * Step i is always computed when i < warmup, i >= n_steps - cooldown, or
+ * fewer than two full steps have completed.  Otherwise:
+ *   DIT_CACHE_OFF           never skips;
+ *   DIT_CACHE_CADENCE       skips unless (i - warmup) is a multiple of cadence;
+ *   DIT_CACHE_ONLINE_DELTA  skips when the last full step's output change
+ *                           (dit_cache_ctrl_observe) was below alpha times the
+ *                           first output change of the generation and the
+ *                           step before was not skipped;
+ *   DIT_CACHE_TEACACHE      adds poly(probe_score) (coefficients coef[0..n_coef),
+ *                           highest degree first) to an accumulator and skips
+ *                           while it stays below threshold; every full step
+ *                           resets it; a non-finite probe score computes.
+ * Arithmetic is double, without fused multiply-adds. */
+typedef enum dit_cache_mode {
+  DIT_CACHE_OFF = 0,
+  DIT_CACHE_CADENCE = 1,
+  DIT_CACHE_ONLINE_DELTA = 2,
+  DIT_CACHE_TEACACHE = 3
+} dit_cache_mode;
+#define DIT_CACHE_MAX_COEF 8
+typedef struct dit_cache_policy {
+  int32_t mode, n_steps, warmup, cooldown, cadence;
+  int32_t n_coef;
+  double alpha, threshold;
+  double coef[DIT_CACHE_MAX_COEF];
+} dit_cache_policy;
+typedef struct dit_cache_ctrl {
+  dit_cache_policy policy;
+  int32_t next_step, n_full, last_skipped, skip_next, have_first;
+  double first_change, acc;
+} dit_cache_ctrl;
+dit_status dit_cache_ctrl_init(dit_cache_ctrl* c, const dit_cache_policy* p);
+/* *action = DIT_STEP_FULL or DIT_STEP_SKIP for `step`; probe_score is read
+ * in DIT_CACHE_TEACACHE mode only (pass the probe's score of this step). */
+dit_status dit_cache_ctrl_decide(dit_cache_ctrl* c, int32_t step, float probe_score,
+                                 int32_t* action);
+/* After a full step: the output change it measured (online-delta only;
+ * non-finite values are ignored). */
+dit_status dit_cache_ctrl_observe(dit_cache_ctrl* c, float output_change);
+
 /* Debug: the integer (t, h, w) position of every token of one batch row,
  * int32 [n_vis + n_txt, 3] (device), from the same device code RoPE uses. */
 dit_status dit_debug_positions(const dit_block_desc* desc, int32_t* out,

@@ -172,3 +172,50 @@ def test_other_entry_points_argument_errors():
     _expect("DIT_EINVAL", D.dit_cast_f32_bf16, FAKE, 6, 4, 6, FAKE * 2, 8, stream=0)
     _expect("DIT_EINVAL", D.dit_qk_rmsnorm_rope, _block(), FAKE, 100, FAKE, FAKE, stream=0)
     assert D.lib().dit_last_error().decode() != ""
+
+
+def _fake_model(shape):
+    desc = D.model_desc(shape, [int(v) for v in (10, 3)][:shape.block.batch])
+    glue = {n: (1 << 24) * (i + 1) for i, n in enumerate(
+        ("t_w1", "t_b1", "t_w2", "t_b2", "in_w", "in_b", "fin_w", "fin_b", "out_w", "out_b", "text"))}
+    blk = {n: (1 << 32) + (1 << 24) * i for i, n in enumerate(
+        ("w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "w_up", "b_up", "w_dn", "b_dn"))}
+    w = D.model_weights(glue, [blk] * shape.depth, [1 << 34] * shape.depth, [1 << 35] * shape.depth)
+    return desc, w
+
+
+def test_step_cache_argument_errors():
+    f = D.dit_change_score
+    wsb = D.dit_change_score_workspace_bytes()
+    assert wsb >= 8
+    A, B, S_, W = 1 << 36, 1 << 37, 1 << 38, 1 << 39
+    _expect("DIT_EINVAL", f, A, B, 5, 16, 0, S_, W, wsb, stream=0)          # dtype
+    _expect("DIT_EINVAL", f, A, B, D.DTYPE_BF16, 0, 0, S_, W, wsb, stream=0)  # n < 1
+    _expect("DIT_EINVAL", f, A, B, D.DTYPE_BF16, 16, 2, S_, W, wsb, stream=0)
+    _expect("DIT_EINVAL", f, None, B, D.DTYPE_BF16, 16, 0, S_, W, wsb, stream=0)
+    _expect("DIT_EINVAL", f, A + 2, B, D.DTYPE_BF16, 16, 0, S_, W, wsb, stream=0)
+    _expect("DIT_EWORKSPACE", f, A, B, D.DTYPE_BF16, 16, 0, S_, W, wsb - 4, stream=0)
+    _expect("DIT_EINVAL", f, A, A + 16, D.DTYPE_F32, 16, 1, S_, W, wsb, stream=0)  # update overlap
+    _expect("DIT_EINVAL", f, A, B, D.DTYPE_F32, 16, 0, A + 32, W, wsb, stream=0)  # score in cur
+
+    from synthetic import configs as C_
+    desc, w = _fake_model(C_.TINY_LOOP)
+    wsb = D.dit_denoise_workspace_bytes(desc)
+    L, P, Dv, S_, W = 1 << 40, 1 << 41, 1 << 42, 1 << 43, 1 << 44
+    g = D.dit_denoise_step_cached
+    args = (1.0, 0.9, 5.0)
+    _expect("DIT_EINVAL", g, desc, w, L, *args, 2, 1, P, Dv, S_, W, wsb, stream=0)       # action
+    _expect("DIT_EINVAL", g, desc, w, L, *args, D.STEP_SKIP, 0, P, Dv, S_, W, wsb, stream=0)
+    _expect("DIT_EINVAL", g, desc, w, L, *args, D.STEP_FULL, 3, P, Dv, S_, W, wsb, stream=0)
+    _expect("DIT_EINVAL", g, desc, w, L, *args, D.STEP_FULL, 1, None, Dv, S_, W, wsb, stream=0)
+    _expect("DIT_EINVAL", g, desc, w, L, *args, D.STEP_FULL, 1, P, P + 64, S_, W, wsb, stream=0)
+    _expect("DIT_EINVAL", g, desc, w, L, *args, D.STEP_FULL, 1, P + 8, Dv, S_, W, wsb, stream=0)
+    _expect("DIT_EWORKSPACE", g, desc, w, L, *args, D.STEP_FULL, 1, P, Dv, S_, W, wsb - 256,
+            stream=0)
+    _expect("DIT_EINVAL", g, desc, w, L, 1.0, float("inf"), 5.0, D.STEP_FULL, 1, P, Dv, S_, W, wsb,
+            stream=0)
+    p = D.dit_cache_probe
+    _expect("DIT_EINVAL", p, desc, w, L, 0.5, P, 2, S_, W, wsb, stream=0)
+    _expect("DIT_EINVAL", p, desc, w, L, 0.5, None, 1, S_, W, wsb, stream=0)
+    _expect("DIT_EINVAL", p, desc, w, L, 0.5, P + 2, 1, S_, W, wsb, stream=0)
+    _expect("DIT_EINVAL", p, desc, w, L, 0.5, W + 256, 1, S_, W, wsb, stream=0)  # saved in workspace

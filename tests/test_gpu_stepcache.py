@@ -1,0 +1,337 @@
+"""GPU parity of step caching ("Difflet", section 5; "Difflet Engineering
+Report", DiT caching; "19. Diffusion, Image, Video, and World Models", Inside
+TeaCache's skip decision): the relative L1 change score kernel, the block-0
+probe, the cached denoising step (full and skip) and a whole cached loop
+driven by the library's host controller, against the oracle.
+
+* dit_change_score: the score equals the fp64 relative L1 change of the same
+  arrays to fp32-summation accuracy (rel 1e-5), for bf16 and fp32, ragged
+  sizes, with and without the fused update (prev == cur bitwise afterwards);
+  reruns are bitwise identical; the zero-reference cases are exact.
+* A 30-step cached loop of the tiny two-block CFG model per mode.  Every
+  step is checked teacher-forced on the GPU's own state: a full step's new
+  latent against the oracle's step from the same latent (composite bar) and
+  its guided velocity (the composite bar carried through the guidance
+  combination by the triangle inequality), the
+  change score against the fp64 change of the downloaded velocities, the
+  saved change and the latent update against their fp32 definitions; a skip
+  step's estimate and update exactly; the probe's features within one bf16
+  unit of the oracle's unrounded adaLN output and its score against the fp64
+  change of the downloaded features.  The controller's decisions equal the oracle
+  controller's on the same scores, and the final latent equals the oracle's
+  cached loop replaying the same decisions (to twice the oracle's own bf16
+  storage spread, which extrapolation through skipped steps magnifies; see
+  gpu_util.assert_composite_extrapolated)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import diffusion_transformer_denoising_dit_amd as D
+import oracle as O
+from oracle import stepcache as S
+from synthetic import configs as C
+from tests.gpu_util import (assert_bf16_ulp, assert_composite, assert_composite_extrapolated,
+                            assert_parity, bits_of, host)
+from tests.test_gpu_loop import Model, _latent
+
+pytestmark = pytest.mark.gpu
+
+WS = None
+
+
+def _ws():
+    global WS
+    if WS is None:
+        WS = torch.empty(D.dit_change_score_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    return WS
+
+
+def _score(cur, prev, dtype, update=False):
+    out = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+    ws = _ws()
+    D.dit_change_score(cur, prev, dtype, cur.numel(), update, out, ws, ws.numel())
+    torch.cuda.synchronize()
+    return float(out.item())
+
+
+@pytest.mark.parametrize("dtype", [D.DTYPE_BF16, D.DTYPE_F32])
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 1000, 12293, (1 << 20) + 3, 5_000_011])
+def test_change_score_matches_fp64(dtype, n):
+    g = torch.Generator("cuda").manual_seed(n)
+    tdt = torch.bfloat16 if dtype == D.DTYPE_BF16 else torch.float32
+    prev = torch.randn(n, generator=g, device="cuda").to(tdt)
+    cur = (prev.float() + 0.05 * torch.randn(n, generator=g, device="cuda")).to(tdt)
+    want = S.rel_l1(host(cur), host(prev))
+    got = _score(cur, prev, dtype)
+    again = _score(cur, prev, dtype)
+    print(f"[score] n={n} dtype={dtype}: gpu {got:.8f} fp64 {want:.8f}", flush=True)
+    assert got == again                                          # deterministic
+    assert abs(got - want) <= 1e-5 * want + 1e-7
+    got_u = _score(cur, prev, dtype, update=True)
+    assert got_u == got                                          # same sums with the update fused
+    if dtype == D.DTYPE_BF16:
+        np.testing.assert_array_equal(bits_of(prev), bits_of(cur))
+    else:
+        assert torch.equal(prev, cur)
+
+
+def test_change_score_special_cases():
+    z = torch.zeros(1001, dtype=torch.float32, device="cuda")
+    z2 = torch.zeros(1001, dtype=torch.float32, device="cuda")
+    assert _score(z, z2, D.DTYPE_F32) == 0.0
+    one = torch.ones(1001, dtype=torch.float32, device="cuda")
+    assert _score(one, z2, D.DTYPE_F32) == math.inf
+    x = torch.randn(4099, device="cuda").to(torch.bfloat16)
+    assert _score(x, x, D.DTYPE_BF16) == 0.0
+    # hand value: |[3,-1,0] - [2,1,-1]|_1 / |[2,1,-1]|_1 = 4 / 4
+    a = torch.tensor([3.0, -1.0, 0.0], device="cuda")
+    b = torch.tensor([2.0, 1.0, -1.0], device="cuda")
+    assert _score(a, b, D.DTYPE_F32) == 1.0
+
+
+@pytest.mark.slow
+def test_change_score_c3_feature_size():
+    """The probe's array at the c3 shape: 33272 tokens x 5120 bf16."""
+    n = 33272 * 5120
+    g = torch.Generator("cuda").manual_seed(33)
+    prev = torch.randn(n, generator=g, device="cuda").to(torch.bfloat16)
+    cur = (prev.float() * 0.97 + 0.02 * torch.randn(n, generator=g, device="cuda")).to(torch.bfloat16)
+    want = S.rel_l1(host(cur), host(prev))
+    got = _score(cur, prev, D.DTYPE_BF16)
+    print(f"[score] c3 features: gpu {got:.8f} fp64 {want:.8f}", flush=True)
+    assert abs(got - want) <= 1e-5 * want
+
+
+# ---------------------------------------------------------------------------
+# cached loop
+
+class GpuCache:
+    def __init__(self, m):
+        self.m = m
+        shp = m.shape
+        b = shp.block
+        Bl = 1 if shp.cfg else b.batch
+        self.vshape = (Bl, b.n_vis, shp.latent_channels)
+        self.prev = torch.zeros(self.vshape, dtype=torch.float32, device="cuda")
+        self.delta = torch.zeros(self.vshape, dtype=torch.float32, device="cuda")
+        self.score = torch.zeros(1, dtype=torch.float32, device="cuda")
+        self.saved = torch.zeros((b.batch, b.n_tok, b.hidden), dtype=torch.bfloat16, device="cuda")
+        self.pscore = torch.zeros(1, dtype=torch.float32, device="cuda")
+
+    def step(self, x, sig, nxt, action, have_prev):
+        m = self.m
+        D.dit_denoise_step_cached(m.desc, m.weights, x, sig, nxt, m.shape.guidance, action, have_prev,
+                                  self.prev, self.delta, self.score, m.ws, m.ws_bytes)
+
+    def probe(self, x, sig, have_saved):
+        m = self.m
+        D.dit_cache_probe(m.desc, m.weights, x, sig, self.saved, have_saved, self.pscore, m.ws,
+                          m.ws_bytes)
+
+
+def _guided(m, v):
+    return O.cfg_combine(v[0:1], v[1:2], m.shape.guidance) if m.shape.cfg else v
+
+
+def _assert_guided(m, got, v, v_exact, what):
+    """The guided velocity v_u + g (v_c - v_u) held as the cache state.  The
+    denoiser's per-branch output v meets the composite bar (max-abs <=
+    max(2e-2, bf16-storage spread), rel-L2 <= 5e-3); the combination scales
+    each branch's error by |g| and |1 - g|, so by the triangle inequality the
+    bar for the guided value is max-abs <= (|g| + |1 - g|) x the per-branch
+    bound and rel-L2 <= 5e-3 (|g| |v_c| + |1 - g| |v_u|) / |v_hat| (L2 norms
+    of the oracle's values)."""
+    g = m.shape.guidance
+    ref = _guided(m, v)
+    if not m.shape.cfg:
+        assert_composite(got, ref, _guided(m, v_exact), what)
+        return
+    spread = float(np.abs(np.asarray(v_exact) - np.asarray(v)).max())
+    amp = abs(g) + abs(1.0 - g)
+    nv_c, nv_u = np.linalg.norm(v[0]), np.linalg.norm(v[1])
+    rel = 5e-3 * (abs(g) * nv_c + abs(1.0 - g) * nv_u) / np.linalg.norm(ref)
+    assert_parity(got, ref, what + f" (guidance {g}: bounds x{amp:.0f}, rel-L2 {rel:.2e})",
+                  max_abs=amp * max(2e-2, spread), rel_l2=rel)
+
+
+def _run_cached_loop(m, lat0, policy, check=True):
+    """Drive the GPU loop with the library controller; teacher-forced checks
+    per step.  Returns (actions, probe scores, output changes, final latent)."""
+    shp = m.shape
+    sig = O.sigma_schedule(shp.steps)
+    ctl = D.CacheController(policy)
+    gc = GpuCache(m)
+    x = torch.from_numpy(lat0.astype(np.float32)).cuda()
+    acts, probes, changes = [], [], []
+    n_full = 0
+    for i in range(shp.steps):
+        s32, n32 = float(np.float32(sig[i])), float(np.float32(sig[i + 1]))
+        x_before = host(x)
+        p = math.inf
+        if policy.mode == D.CACHE_TEACACHE:
+            saved_before = host(gc.saved)
+            gc.probe(x, float(sig[i]), i > 0)
+            torch.cuda.synchronize()
+            p = float(gc.pscore.item())
+            if check:
+                h = host(gc.saved)
+                assert_bf16_ulp(h, _probe_unrounded(m, x_before, float(sig[i])),
+                                f"probe features step {i}")
+                if i == 0:
+                    assert p == math.inf
+                else:
+                    want = S.rel_l1(h, saved_before)
+                    assert abs(p - want) <= 1e-5 * want + 1e-7, (i, p, want)
+        probes.append(p)
+        a = ctl.decide(i, p)
+        acts.append(a)
+        prev_before, delta_before = host(gc.prev), host(gc.delta)
+        gc.step(x, float(sig[i]), float(sig[i + 1]), a, n_full >= 1)
+        torch.cuda.synchronize()
+        prev_after, x_after = host(gc.prev), host(x)
+        dt = np.float32(n32) - np.float32(s32)
+        if a == D.STEP_FULL:
+            sc = float(gc.score.item()) if n_full >= 1 else math.inf
+            changes.append(sc)
+            ctl.observe(sc)
+            if check:
+                if n_full >= 1:
+                    want = S.rel_l1(prev_after, prev_before)
+                    assert abs(sc - want) <= 1e-5 * want + 1e-7, (i, sc, want)
+                    np.testing.assert_array_equal(
+                        host(gc.delta), (prev_after.astype(np.float32) - prev_before.astype(np.float32)))
+                else:
+                    assert gc.score.item() == math.inf
+                ref_x, v = O.denoise_step(m, x_before, sig[i], sig[i + 1], shp.guidance)
+                ex_x, ve = O.denoise_step(m, x_before, sig[i], sig[i + 1], shp.guidance,
+                                          round_points=False)
+                assert_composite(x_after, ref_x, ex_x, f"latent after full step {i}")
+                _assert_guided(m, prev_after, v, ve, f"guided velocity step {i}")
+            n_full += 1
+        else:
+            changes.append(math.nan)
+            want_v = prev_before.astype(np.float32) + delta_before.astype(np.float32)
+            np.testing.assert_array_equal(prev_after, want_v)
+            np.testing.assert_array_equal(host(gc.delta), delta_before)
+        # latent update x + dt v in fp32 (the compiler may fuse it: one rounding apart)
+        want_x = x_before + np.float64(dt) * prev_after
+        np.testing.assert_allclose(x_after, want_x, rtol=2e-7, atol=2e-7 * np.abs(x_before).max())
+    return acts, probes, changes, x
+
+
+def _probe_unrounded(m, lat, sigma):
+    """The probe's adaLN output before its final bf16 store (every earlier
+    bf16 point rounded as on the GPU): the exact value a correctly rounded
+    kernel output lies within one bf16 unit of."""
+    b = m.shape.block
+    s, x = O.step_tokens(m, lat, sigma)
+    w = m.layer(0)
+    mod = O.round_bf16(O.linear(s, O.bf16_decode(w["mod_w"]), O.bf16_decode(w["mod_b"])))
+    mod = mod.reshape(6, b.hidden)
+    return O.adaln_modulate(x, mod[0], mod[1], b.ln_eps)
+
+
+def _oracle_replay(m, lat0, acts):
+    sig = O.sigma_schedule(m.shape.steps)
+    cache = S.OutputCache()
+    ref = lat0
+    exact_cache = S.OutputCache()
+    ex = lat0
+    for i, a in enumerate(acts):
+        ref, _ = S.cached_denoise_step(m, ref, sig[i], sig[i + 1], m.shape.guidance, a, cache)
+        ex, _ = S.cached_denoise_step(m, ex, sig[i], sig[i + 1], m.shape.guidance, a, exact_cache,
+                                      round_points=False)
+    return ref, ex
+
+
+def _output_changes(m, lat0):
+    """Output changes of an uncached GPU loop (every step full)."""
+    sig = O.sigma_schedule(m.shape.steps)
+    gc = GpuCache(m)
+    x = torch.from_numpy(lat0.astype(np.float32)).cuda()
+    out = []
+    for i in range(m.shape.steps):
+        gc.step(x, float(sig[i]), float(sig[i + 1]), D.STEP_FULL, i > 0)
+        torch.cuda.synchronize()
+        out.append(float(gc.score.item()) if i > 0 else math.inf)
+    return out
+
+
+def _probe_thresholds(m, lat0):
+    """Probe scores of an uncached GPU loop (to place a TeaCache threshold
+    where the tiny model actually skips)."""
+    sig = O.sigma_schedule(m.shape.steps)
+    gc = GpuCache(m)
+    x = torch.from_numpy(lat0.astype(np.float32)).cuda()
+    out = []
+    for i in range(m.shape.steps):
+        gc.probe(x, float(sig[i]), i > 0)
+        m.gpu_step(x, float(sig[i]), float(sig[i + 1]))
+        torch.cuda.synchronize()
+        out.append(float(gc.pscore.item()))
+    return out
+
+
+@pytest.mark.parametrize("mode", ["cadence", "online_delta", "teacache"])
+def test_cached_loop_tiny(mode):
+    shape = C.TINY_LOOP
+    m = Model(shape).upload()
+    lat0 = O.bf16_decode(_latent(shape, 75))
+    n = shape.steps
+    if mode == "cadence":
+        pol = D.cache_policy(D.CACHE_CADENCE, n, 3, 3, cadence=2)
+    elif mode == "online_delta":
+        # alpha placed just above the smallest change ratio an uncached run
+        # shows inside the window, so the case is certain to skip
+        ch = _output_changes(m, lat0)
+        ratios = [ch[i] / ch[1] for i in range(3, n - 4)]
+        alpha = 1.001 * min(ratios)
+        pol = D.cache_policy(D.CACHE_ONLINE_DELTA, n, 3, 3, alpha=alpha)
+    else:
+        ps = _probe_thresholds(m, lat0)
+        thr = 2.5 * float(np.median(ps[1:]))
+        pol = D.cache_policy(D.CACHE_TEACACHE, n, 3, 3, threshold=thr, coef=(1.0, 0.0))
+    acts, probes, changes, x = _run_cached_loop(m, lat0, pol)
+    print(f"[cache] {mode}: actions {''.join('F' if a == 0 else 's' for a in acts)}", flush=True)
+    # the oracle controller on the GPU's scores decides the same
+    oc = S.Controller({"cadence": S.CADENCE, "online_delta": S.ONLINE_DELTA,
+                       "teacache": S.TEACACHE}[mode], n, warmup=3, cooldown=3, cadence=2,
+                      alpha=pol.alpha, threshold=pol.threshold, coef=(1.0, 0.0))
+    oa = []
+    for i in range(n):
+        a = oc.decide(i, probes[i] if mode == "teacache" else None)
+        oa.append(a)
+        if a == S.FULL:
+            oc.observe(changes[i])
+    assert oa == acts
+    if mode == "cadence":
+        assert acts.count(D.STEP_SKIP) == 12
+    else:
+        assert acts.count(D.STEP_SKIP) >= 1, "no step was skipped: the case tests nothing"
+    ref, ex = _oracle_replay(m, lat0, acts)
+    assert_composite_extrapolated(host(x), ref, ex, f"cached loop ({mode}), final latent")
+
+
+def test_cached_full_steps_equal_plain_steps():
+    """With every step full, the cached step moves the latent as
+    dit_denoise_step does: the same velocity and update (one fp32 rounding
+    apart if the compiler fuses the update differently) after one step, and
+    within bf16 re-rounding of the latent after four."""
+    shape = C.TINY_LOOP
+    m = Model(shape).upload()
+    lat0 = O.bf16_decode(_latent(shape, 76))
+    sig = O.sigma_schedule(shape.steps)
+    gc = GpuCache(m)
+    x1 = torch.from_numpy(lat0.astype(np.float32)).cuda()
+    x2 = x1.clone()
+    for i in range(4):
+        gc.step(x1, float(sig[i]), float(sig[i + 1]), D.STEP_FULL, i > 0)
+        m.gpu_step(x2, float(sig[i]), float(sig[i + 1]))
+        torch.cuda.synchronize()
+        if i == 0:
+            np.testing.assert_allclose(host(x1), host(x2), rtol=2e-7, atol=1e-6)
+    a, b = host(x1), host(x2)
+    assert np.linalg.norm(a - b) <= 1e-4 * np.linalg.norm(b)
