@@ -10,8 +10,9 @@ synthetic tensors already resident in HBM.
 
 Prints ONE JSON line: ms/step (the value), the block alone, joint
 attention's TFLOP/s against the bf16 dense MFMA peak (the roofline object),
-split joint attention (a text partial plus 4 visual partials, merged), plus
-the CPU oracle timed on a bounded sample of the same step.
+split joint attention (a text partial plus 4 visual partials, merged), step
+caching (probe, skipped step, change-score kernel, a 30-step cadence-2 loop),
+plus the CPU oracle timed on a bounded sample of the same step.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -230,6 +231,58 @@ def main():
     ms_step = timed(step, args.steps, stream)
     assert torch.isfinite(lat).all(), "non-finite latent"
 
+    # step caching at the same shape: the block-0 probe, a cached (skipped)
+    # step, the change-score kernel alone on the probe's features, and a
+    # 30-step cadence-2 loop (5 initial and 5 final full steps) driven by the
+    # library's controller
+    Bl = 1 if shape.cfg else blk.batch
+    prev_v = torch.zeros((Bl, blk.n_vis, shape.latent_channels), dtype=torch.float32, device="cuda")
+    delta_v = torch.zeros_like(prev_v)
+    score = torch.zeros(1, dtype=torch.float32, device="cuda")
+    saved = torch.zeros((blk.batch, blk.n_tok, blk.hidden), dtype=torch.bfloat16, device="cuda")
+    pscore = torch.zeros(1, dtype=torch.float32, device="cuda")
+    lat_c = lat0.clone()
+
+    def cached(i, action, have_prev):
+        D.dit_denoise_step_cached(desc, weights, lat_c, sig[i], sig[i + 1], shape.guidance, action,
+                                  have_prev, prev_v, delta_v, score, ws, ws_bytes)
+
+    def probe():
+        D.dit_cache_probe(desc, weights, lat_c, sig[3], saved, 1, pscore, ws, ws_bytes)
+
+    cached(0, D.STEP_FULL, 0)
+    cached(1, D.STEP_FULL, 1)
+    probe()
+    ms_probe = timed(probe, max(5, args.steps), stream)
+    ms_skip = timed(lambda: cached(2, D.STEP_SKIP, 1), max(5, args.steps), stream)
+    feat_n = blk.batch * blk.n_tok * blk.hidden
+    cur_f = torch.randn(feat_n, generator=torch.Generator("cuda").manual_seed(6),
+                        device="cuda").to(torch.bfloat16)
+    sws = torch.empty(D.dit_change_score_workspace_bytes(), dtype=torch.uint8, device="cuda")
+
+    def change_score():
+        D.dit_change_score(cur_f, saved, D.DTYPE_BF16, feat_n, 1, pscore, sws, sws.numel())
+
+    change_score()
+    ms_score = timed(change_score, max(5, args.steps), stream)
+    score_bytes = 3 * feat_n * 2  # read current and saved, write saved
+
+    def cadence_loop():
+        ctl = D.CacheController(D.cache_policy(D.CACHE_CADENCE, shape.steps, 5, 5, cadence=2))
+        n_full = 0
+        for i in range(shape.steps):
+            a = ctl.decide(i)
+            cached(i, a, 1 if n_full else 0)
+            n_full += a == D.STEP_FULL
+        return n_full
+
+    lat_c.copy_(lat0)
+    n_full_loop = cadence_loop()
+    torch.cuda.synchronize()
+    lat_c.copy_(lat0)
+    ms_loop = timed(cadence_loop, 1, stream) / shape.steps
+    del cur_f, saved
+
     # the block alone (same weights, modulation from the step's own buffers)
     bdesc = D.block_desc(blk, inp.txt_valid, 0)
     bws_bytes = D.dit_block_workspace_bytes(bdesc)
@@ -334,6 +387,16 @@ def main():
             "merge_ms": round(ms_merge, 3),
             "tflops": round(a_flop / (ms_split * 1e-3) / 1e12, 1),
             "max_abs_vs_unsplit": round(split_err, 5),
+        },
+        "step_cache": {
+            "probe_ms": round(ms_probe, 3),
+            "skip_step_ms": round(ms_skip, 4),
+            "change_score_ms": round(ms_score, 4),
+            "change_score_gbps": round(score_bytes / (ms_score * 1e-3) / 1e9, 1),
+            "change_score_frac_hbm_peak": round(score_bytes / (ms_score * 1e-3) / 8e12, 4),
+            "cadence2_loop_ms_per_step": round(ms_loop, 3),
+            "cadence2_full_steps": int(n_full_loop),
+            "steps": shape.steps,
         },
         "roofline": {
             "bound": "mfma",
