@@ -184,3 +184,44 @@ class LoopInputs:
 
 def loop_inputs(shape: LoopShape) -> LoopInputs:
     return LoopInputs(shape)
+
+
+def double_block_inputs(shape: BlockShape) -> dict:
+    """Inputs of an MM-DiT double-stream block: the image stream x_img
+    [B, n_vis, D], the text stream x_txt [B, n_txt, D], one modulation set per
+    stream (mod_img, mod_txt [B, 6, D]), one weight set per stream (w_img,
+    w_txt; the DiT block's names and distributions) and txt_valid [B]."""
+    B, S, L, D, F = shape.batch, shape.n_vis, shape.n_txt, shape.hidden, shape.mlp
+    c = seed_sequence(shape.seed).spawn(6)
+    img_w = c[4].spawn(len(_BLOCK_ORDER))
+    txt_w = c[5].spawn(len(_BLOCK_ORDER))
+    mod_img, mod_txt = c[2].spawn(2)
+    return {
+        "x_img": _normal_bf16(c[0], (B, S, D)),
+        "x_txt": _normal_bf16(c[1], (B, L, D)),
+        "mod_img": _normal_bf16(mod_img, (B, 6, D)),
+        "mod_txt": _normal_bf16(mod_txt, (B, 6, D)),
+        "txt_valid": _valid_lengths(c[3], shape.txt_valid, B, L),
+        "w_img": block_weights(img_w, D, F),
+        "w_txt": block_weights(txt_w, D, F),
+    }
+
+
+def single_block_inputs(shape: BlockShape) -> dict:
+    """Inputs of an MM-DiT single-stream block: the joint stream x [B, N, D],
+    mod [B, 3, D] (shift, scale, gate), the fused linears w1 [3D + F, D], b1,
+    w2 [D, D + F], b2 (N(0, 0.02)), the Q/K RMSNorm gains g_q, g_k
+    (1 + N(0, 0.02)) and txt_valid [B]."""
+    B, N, D, F = shape.batch, shape.n_tok, shape.hidden, shape.mlp
+    c = seed_sequence(shape.seed).spawn(9)
+    return {
+        "x": _normal_bf16(c[0], (B, N, D)),
+        "mod": _normal_bf16(c[1], (B, 3, D)),
+        "w1": _normal_bf16(c[2], (3 * D + F, D), 0.02),
+        "b1": _normal_bf16(c[3], (3 * D + F,), 0.02),
+        "g_q": _normal_bf16(c[4], (D,), 0.02, 1.0),
+        "g_k": _normal_bf16(c[5], (D,), 0.02, 1.0),
+        "w2": _normal_bf16(c[6], (D, D + F), 0.02),
+        "b2": _normal_bf16(c[7], (D,), 0.02),
+        "txt_valid": _valid_lengths(c[8], shape.txt_valid, B, shape.n_txt),
+    }

@@ -108,3 +108,106 @@ def step(M, latent, sigma, sigma_next, guidance, t_scale=1000.0):
                   for c in range(len(v[0][i]))] for i in range(nv)]]
     return [[[latent[b][i][c] + dt * v[b][i][c] for c in range(len(v[b][i]))] for i in range(nv)]
             for b in range(B)]
+
+
+def _pos_fn(s):
+    T_, Hg, Wg = s.grid
+
+    def pos_of(i):
+        if i >= s.n_vis:
+            return (0, 0, 0)
+        return (i // (Hg * Wg), (i // Wg) % Hg, i % Wg)
+    return pos_of
+
+
+def _rms_rope(vec, g, p, s):
+    D, H, d = s.hidden, s.heads, s.head_dim
+    r = math.sqrt(sum(t * t for t in vec) / D + s.rms_eps)
+    v = [vec[c] / r * g[c] for c in range(D)]
+    out = list(v)
+    for h in range(H):
+        off = h * d
+        for a, da in enumerate(s.rope):
+            for j in range(da // 2):
+                ang = p[a] * s.rope_theta ** (-2.0 * j / da)
+                i0 = off + 2 * j
+                out[i0] = v[i0] * math.cos(ang) - v[i0 + 1] * math.sin(ang)
+                out[i0 + 1] = v[i0] * math.sin(ang) + v[i0 + 1] * math.cos(ang)
+            off += da
+    return out
+
+
+def _attend(q, ks, vs, nk, s):
+    D, H, d = s.hidden, s.heads, s.head_dim
+    o = [0.0] * D
+    for h in range(H):
+        sc = [sum(q[h * d + c] * ks[j][h * d + c] for c in range(d)) / math.sqrt(d) for j in range(nk)]
+        m = max(sc)
+        e = [math.exp(t - m) for t in sc]
+        z = sum(e)
+        for c in range(d):
+            o[h * d + c] = sum(e[j] / z * vs[j][h * d + c] for j in range(nk))
+    return o
+
+
+def _gelu(z):
+    return z * 0.5 * (1 + math.erf(z / math.sqrt(2)))
+
+
+def double_block(x_img, x_txt, mod_img, mod_txt, W_img, W_txt, s, valid):
+    """MM-DiT double-stream block, one token at a time: per-stream adaLN,
+    QKV, RMSNorm + RoPE, one attention over [image; valid text] keys, then
+    per-stream output projection, gated residual and gated GELU MLP."""
+    B, S, L, D = s.batch, s.n_vis, s.n_txt, s.hidden
+    pos_of = _pos_fn(s)
+    out_img, out_txt = [], []
+    for b in range(B):
+        toks = [(x_img[b][i], mod_img[b], W_img) for i in range(S)] + \
+               [(x_txt[b][i], mod_txt[b], W_txt) for i in range(L)]
+        qs, ks, vs = [], [], []
+        for i, (xr, mb, W) in enumerate(toks):
+            h = ln_mod(xr, mb[0], mb[1], s.ln_eps)
+            qkv = lin(h, W["w_qkv"], W["b_qkv"])
+            qs.append(_rms_rope(qkv[:D], W["g_q"], pos_of(i), s))
+            ks.append(_rms_rope(qkv[D:2 * D], W["g_k"], pos_of(i), s))
+            vs.append(qkv[2 * D:])
+        nk = S + int(valid[b])
+        rows = []
+        for i, (xr, mb, W) in enumerate(toks):
+            o = _attend(qs[i], ks, vs, nk, s)
+            y = lin(o, W["w_o"], W["b_o"])
+            x1 = [xr[c] + mb[2][c] * y[c] for c in range(D)]
+            h2 = ln_mod(x1, mb[3], mb[4], s.ln_eps)
+            u = [_gelu(z) for z in lin(h2, W["w_up"], W["b_up"])]
+            y2 = lin(u, W["w_dn"], W["b_dn"])
+            rows.append([x1[c] + mb[5][c] * y2[c] for c in range(D)])
+        out_img.append(rows[:S])
+        out_txt.append(rows[S:])
+    return out_img, out_txt
+
+
+def single_block(x, mod, W, s, valid):
+    """MM-DiT single-stream block, one token at a time: adaLN, linear1 split
+    into q | k | v | up, RMSNorm + RoPE, attention, GELU(up), linear2 on
+    [o | GELU(up)], gated residual."""
+    B, N, D = s.batch, s.n_tok, s.hidden
+    pos_of = _pos_fn(s)
+    res = []
+    for b in range(B):
+        mb = mod[b]
+        hs, qs, ks, vs, ups = [], [], [], [], []
+        for i in range(N):
+            h = ln_mod(x[b][i], mb[0], mb[1], s.ln_eps)
+            y1 = lin(h, W["w1"], W["b1"])
+            qs.append(_rms_rope(y1[:D], W["g_q"], pos_of(i), s))
+            ks.append(_rms_rope(y1[D:2 * D], W["g_k"], pos_of(i), s))
+            vs.append(y1[2 * D:3 * D])
+            ups.append(y1[3 * D:])
+        nk = s.n_vis + int(valid[b])
+        rows = []
+        for i in range(N):
+            o = _attend(qs[i], ks, vs, nk, s)
+            y2 = lin(o + [_gelu(z) for z in ups[i]], W["w2"], W["b2"])
+            rows.append([x[b][i][c] + mb[2][c] * y2[c] for c in range(D)])
+        res.append(rows)
+    return res
