@@ -12,6 +12,7 @@ Prints ONE JSON line: ms/step (the value), the block alone, joint
 attention's TFLOP/s against the bf16 dense MFMA peak (the roofline object),
 split joint attention (a text partial plus 4 visual partials, merged), step
 caching (probe, skipped step, change-score kernel, a 30-step cadence-2 loop),
+the MM-DiT double- and single-stream blocks at the FLUX-like image shape,
 plus the CPU oracle timed on a bounded sample of the same step.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -176,6 +177,77 @@ def traffic_probe(steps):
     torch.cuda.synchronize()
     print(f"[traffic-probe] {steps} attention launches + {steps} copies of 1 GiB done",
           file=sys.stderr, flush=True)
+
+
+def mmdit_blocks(reps, stream):
+    """MM-DiT double-stream and single-stream blocks at the FLUX-like image
+    shape (4096 image + 512 text tokens, hidden 3072, 24 heads x 128, MLP
+    12288, CFG batch 2 with valid text lengths 77 and 512): ms and TFLOP/s of
+    one block.  Seeded N(0,1) activations and modulation, N(0, 0.02) weights,
+    drawn on the device."""
+    import torch
+
+    import diffusion_transformer_denoising_dit_amd as D
+    from synthetic import configs as C
+    s = C.C2
+    B, S, L, Dh, F = s.batch, s.n_vis, s.n_txt, s.hidden, s.mlp
+    valid = [77, 512]
+    g = torch.Generator("cuda").manual_seed(11)
+
+    def rnd(*shape, std=1.0):
+        return (torch.randn(shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+
+    def block_w():
+        return {"w_qkv": rnd(3 * Dh, Dh, std=0.02), "b_qkv": rnd(3 * Dh, std=0.02),
+                "g_q": 1 + rnd(Dh, std=0.02), "g_k": 1 + rnd(Dh, std=0.02),
+                "w_o": rnd(Dh, Dh, std=0.02), "b_o": rnd(Dh, std=0.02),
+                "w_up": rnd(F, Dh, std=0.02), "b_up": rnd(F, std=0.02),
+                "w_dn": rnd(Dh, F, std=0.02), "b_dn": rnd(Dh, std=0.02)}
+
+    attn = sum(attention_flops(S + L, S + v, s.heads, s.head_dim) for v in valid)
+    out = {}
+    # double stream
+    desc = D.block_desc(s, valid, 6 * Dh)
+    wi, wt = block_w(), block_w()
+    mi, mt = rnd(B, 6, Dh), rnd(B, 6, Dh)
+    xi = torch.randn((B, S, Dh), generator=g, device="cuda")
+    xt = torch.randn((B, L, Dh), generator=g, device="cuda")
+    nb = D.dit_double_block_workspace_bytes(desc)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    bwi, bwt = D.block_weights(wi), D.block_weights(wt)
+
+    def dbl():
+        D.dit_double_block_forward(desc, bwi, bwt, mi, mt, xi, xt, ws, nb)
+
+    dbl()
+    ms = timed(dbl, reps, stream)
+    M = B * (S + L)
+    fl = 2.0 * M * Dh * 4 * Dh + 2.0 * M * Dh * F * 2 + attn
+    out["double_block"] = {"ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                           "algorithmic_tflop": round(fl / 1e12, 3)}
+    del wi, wt, bwi, bwt, xi, xt, ws
+    # single stream
+    desc = D.block_desc(s, valid, 3 * Dh)
+    w = {"w1": rnd(3 * Dh + F, Dh, std=0.02), "b1": rnd(3 * Dh + F, std=0.02),
+         "g_q": 1 + rnd(Dh, std=0.02), "g_k": 1 + rnd(Dh, std=0.02),
+         "w2": rnd(Dh, Dh + F, std=0.02), "b2": rnd(Dh, std=0.02)}
+    sw = D.single_block_weights(w)
+    mod = rnd(B, 3, Dh)
+    x = torch.randn((B, S + L, Dh), generator=g, device="cuda")
+    nb = D.dit_single_block_workspace_bytes(desc)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def sgl():
+        D.dit_single_block_forward(desc, sw, mod, x, ws, nb)
+
+    sgl()
+    ms = timed(sgl, reps, stream)
+    fl = 2.0 * M * Dh * (3 * Dh + F) + 2.0 * M * (Dh + F) * Dh + attn
+    out["single_block"] = {"ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                           "algorithmic_tflop": round(fl / 1e12, 3)}
+    out["shape"] = ("FLUX-like 1024x1024: 4096 image + 512 text tokens (valid 77, 512), hidden 3072, "
+                    "24x128, MLP 12288, batch 2")
+    return out
 
 
 def main():
@@ -351,6 +423,7 @@ def main():
     ms_merge = timed(split_merge, max(5, args.steps), stream)
     del p_out, p_lse, o_split
 
+    mm = mmdit_blocks(max(5, args.steps), stream)
     traffic = attn_traffic()
     result = {
         "metric": METRIC,
@@ -398,6 +471,7 @@ def main():
             "cadence2_full_steps": int(n_full_loop),
             "steps": shape.steps,
         },
+        "mmdit": mm,
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_kernel<128, false> (joint attention)",

@@ -27,6 +27,8 @@ EXPORTED = (
     "dit_change_score_workspace_bytes", "dit_change_score", "dit_cache_probe",
     "dit_denoise_step_cached", "dit_cache_ctrl_init", "dit_cache_ctrl_decide",
     "dit_cache_ctrl_observe",
+    "dit_double_block_workspace_bytes", "dit_double_block_forward",
+    "dit_single_block_workspace_bytes", "dit_single_block_forward",
     "dit_status_string", "dit_last_error", "dit_version",
 )
 DTYPE_BF16, DTYPE_F32 = 0, 1
@@ -99,6 +101,10 @@ class ModelWeights(ctypes.Structure):
         ("mod_b", ctypes.POINTER(ctypes.c_void_p))]
 
 
+class SingleBlockWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "b1", "g_q", "g_k", "w2", "b2")]
+
+
 class CachePolicy(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("n_steps", ctypes.c_int32), ("warmup", ctypes.c_int32),
                 ("cooldown", ctypes.c_int32), ("cadence", ctypes.c_int32), ("n_coef", ctypes.c_int32),
@@ -157,6 +163,14 @@ def lib() -> ctypes.CDLL:
             "dit_cache_ctrl_decide": (st, [ctypes.POINTER(CacheCtrl), i32, f32,
                                            ctypes.POINTER(ctypes.c_int32)]),
             "dit_cache_ctrl_observe": (st, [ctypes.POINTER(CacheCtrl), f32]),
+            "dit_double_block_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(BlockDesc)]),
+            "dit_double_block_forward": (st, [ctypes.POINTER(BlockDesc), ctypes.POINTER(BlockWeights),
+                                              ctypes.POINTER(BlockWeights), vp, vp, vp, vp, vp,
+                                              ctypes.c_size_t, vp]),
+            "dit_single_block_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(BlockDesc)]),
+            "dit_single_block_forward": (st, [ctypes.POINTER(BlockDesc),
+                                              ctypes.POINTER(SingleBlockWeights), vp, vp, vp,
+                                              ctypes.c_size_t, vp]),
             "dit_status_string": (ctypes.c_char_p, [st]),
             "dit_last_error": (ctypes.c_char_p, []),
             "dit_version": (ctypes.c_char_p, []),
@@ -397,3 +411,41 @@ class CacheController:
 
     def observe(self, output_change):
         _check(lib().dit_cache_ctrl_observe(ctypes.byref(self.state), output_change))
+
+
+# ---------------------------------------------------------------------------
+# MM-DiT blocks
+
+def _ws_bytes(fn, desc) -> int:
+    n = fn(ctypes.byref(desc))
+    if n == 0:
+        raise DitError(1, lib().dit_last_error().decode())
+    return n
+
+
+def dit_double_block_workspace_bytes(desc: BlockDesc) -> int:
+    return _ws_bytes(lib().dit_double_block_workspace_bytes, desc)
+
+
+def dit_double_block_forward(desc: BlockDesc, w_img, w_txt, mod_img, mod_txt, x_img, x_txt,
+                             workspace, workspace_bytes, stream=None):
+    wi = w_img if isinstance(w_img, BlockWeights) else block_weights(w_img)
+    wt = w_txt if isinstance(w_txt, BlockWeights) else block_weights(w_txt)
+    _check(lib().dit_double_block_forward(ctypes.byref(desc), ctypes.byref(wi), ctypes.byref(wt),
+                                          _ptr(mod_img), _ptr(mod_txt), _ptr(x_img), _ptr(x_txt),
+                                          _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def single_block_weights(tensors: dict) -> SingleBlockWeights:
+    return SingleBlockWeights(*[_ptr(tensors[n]) for n in ("w1", "b1", "g_q", "g_k", "w2", "b2")])
+
+
+def dit_single_block_workspace_bytes(desc: BlockDesc) -> int:
+    return _ws_bytes(lib().dit_single_block_workspace_bytes, desc)
+
+
+def dit_single_block_forward(desc: BlockDesc, weights, mod, x, workspace, workspace_bytes,
+                             stream=None):
+    w = weights if isinstance(weights, SingleBlockWeights) else single_block_weights(weights)
+    _check(lib().dit_single_block_forward(ctypes.byref(desc), ctypes.byref(w), _ptr(mod), _ptr(x),
+                                          _ptr(workspace), workspace_bytes, _stream(stream)))

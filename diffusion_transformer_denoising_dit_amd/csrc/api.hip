@@ -652,6 +652,206 @@ dit_status dit_cast_bf16_f32(const uint16_t* in, int64_t ld_in, int64_t rows, in
   return hip_status(dit::launch_cast_bf16_f32(in, ld_in, rows, cols, out, ld_out, stream), "cast launch");
 }
 
+// ---------------------------------------------------------------------------
+// MM-DiT blocks ("ChunkFlow", Appendix B: double-stream and single-stream
+// blocks).  Both are compositions of the DiT block's kernels; only the
+// operand routing differs.
+
+size_t dit_double_block_workspace_bytes(const dit_block_desc* desc) {
+  if (check_block_desc(desc) != DIT_OK) return 0;
+  ok();
+  return ws_layout(desc).total;
+}
+
+dit_status dit_double_block_forward(const dit_block_desc* desc, const dit_block_weights* w_img,
+                                    const dit_block_weights* w_txt, const uint16_t* mod_img,
+                                    const uint16_t* mod_txt, float* x_img, float* x_txt,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dit_status st = check_block_desc(desc);
+  if (st != DIT_OK) return st;
+  if ((st = check_block_weights(w_img)) != DIT_OK) return st;
+  if ((st = check_block_weights(w_txt)) != DIT_OK) return st;
+  const int B = desc->attn.batch, S = desc->attn.n_vis, L = desc->attn.n_txt;
+  const int D = desc->hidden, F = desc->mlp;
+  const int64_t N = static_cast<int64_t>(S) + L;
+  if (!mod_img || !aligned(mod_img, 16) || !mod_txt || !aligned(mod_txt, 16))
+    return fail(DIT_EINVAL, "mod_img and mod_txt must be non-NULL and 16-byte aligned");
+  if (!x_img || !aligned(x_img, 16) || (L > 0 && (!x_txt || !aligned(x_txt, 16))))
+    return fail(DIT_EINVAL, "x_img and x_txt must be non-NULL and 16-byte aligned");
+  if (!workspace || !aligned(workspace, 256)) return fail(DIT_EINVAL, "workspace is NULL or not 256-byte aligned");
+  const WsLayout WL = ws_layout(desc);
+  if (workspace_bytes < WL.total)
+    return fail(DIT_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, WL.total);
+  const size_t xi_bytes = static_cast<size_t>(B) * S * D * 4, xt_bytes = static_cast<size_t>(B) * L * D * 4;
+  if (overlap(x_img, xi_bytes, workspace, WL.total) ||
+      (L > 0 && (overlap(x_txt, xt_bytes, workspace, WL.total) || overlap(x_img, xi_bytes, x_txt, xt_bytes))))
+    return fail(DIT_EINVAL, "x_img, x_txt and the workspace must not overlap");
+  const int64_t ms = desc->mod_stride;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + WL.h_off);   // h per stream, o (joint), h2 per stream
+  uint16_t* big = reinterpret_cast<uint16_t*>(ws + WL.big_off);  // qkv (joint), MLP hidden per stream
+  uint16_t* h_txt = hbuf + static_cast<int64_t>(B) * S * D;
+  uint16_t* u_txt = big + static_cast<int64_t>(B) * S * F;
+  struct Stream {
+    const dit_block_weights* w;
+    const uint16_t* mod;
+    float* x;
+    int rows;            // tokens of this stream per batch row
+    int64_t first;       // its first token in the joint sequence
+    uint16_t* h;         // its adaLN outputs, contiguous [B * rows, D]
+    uint16_t* u;         // its MLP hidden, contiguous [B * rows, F]
+  } streams[2] = {{w_img, mod_img, x_img, S, 0, hbuf, big},
+                  {w_txt, mod_txt, x_txt, L, S, h_txt, u_txt}};
+#define DIT_TRY(expr, what)                            \
+  do {                                                 \
+    const hipError_t e_ = (expr);                      \
+    if (e_ != hipSuccess) return hip_status(e_, what); \
+  } while (0)
+  // per stream: h = adaLN(x; shift1, scale1); its q|k|v rows into the joint qkv buffer
+  for (const Stream& t : streams) {
+    if (t.rows == 0) continue;
+    const int64_t M = static_cast<int64_t>(B) * t.rows;
+    DIT_TRY(dit::launch_adaln(t.x, M, D, t.rows, t.mod, t.mod + D, ms, desc->ln_eps, t.h, stream),
+            "double block: adaln 1");
+    dit::GemmParams g = gemm(t.h, D, t.w->w_qkv, t.w->b_qkv, M, 3 * D, D, big + t.first * 3 * D, 3 * D);
+    g.group_rows = t.rows;
+    g.a_group_stride = static_cast<int64_t>(t.rows) * D;
+    g.c_group_stride = N * 3 * D;
+    DIT_TRY(dit::launch_gemm(g, DIT_EPI_BF16, stream), "double block: qkv gemm");
+  }
+  // Q/K RMSNorm with each stream's gains + RoPE (image rows at their grid
+  // position, text rows at 0), one launch per batch row and stream
+  for (int b = 0; b < B; ++b)
+    for (int si = 0; si < 2; ++si) {
+      const Stream& t = streams[si];
+      if (t.rows == 0) continue;
+      dit::RopeParams rp = rope_params(desc, big + (b * N + t.first) * 3 * D, 3 * D, t.w->g_q, t.w->g_k);
+      rp.rows = t.rows;
+      if (si == 1) {  // text rows: token index i < n_tok = L, none visual
+        rp.n_tok = L;
+        rp.n_vis = 0;
+      }
+      DIT_TRY(dit::launch_qk_rmsnorm_rope(rp, stream), "double block: rmsnorm/rope");
+    }
+  // one joint attention over [image; valid text], o in the joint layout
+  {
+    dit::AttnParams ap{};
+    ap.q = big; ap.k = big + D; ap.v = big + 2 * D;
+    ap.q_stride = ap.kv_stride = 3 * D;
+    ap.q_batch = ap.kv_batch = N * 3 * D;
+    ap.out = hbuf; ap.out_stride = D; ap.out_f32 = 0; ap.lse = nullptr;
+    ap.n_q = ap.n_k = static_cast<int>(N); ap.heads = desc->attn.heads; ap.head_dim = desc->attn.head_dim;
+    ap.batch = B;
+    for (int b = 0; b < DIT_MAX_BATCH; ++b) ap.n_valid[b] = b < B ? S + desc->attn.txt_valid[b] : 0;
+    ap.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(desc->attn.head_dim));
+    DIT_TRY(dit::launch_attention(ap, stream), "double block: attention");
+  }
+  // per stream: x += gate1 (o W_o^T + b_o)   (both read o before h2 reuses the buffer)
+  for (const Stream& t : streams) {
+    if (t.rows == 0) continue;
+    dit::GemmParams g = gemm(hbuf + t.first * D, D, t.w->w_o, t.w->b_o, static_cast<int64_t>(B) * t.rows,
+                             D, D, t.x, D);
+    g.group_rows = t.rows;
+    g.a_group_stride = N * D;
+    g.c_group_stride = static_cast<int64_t>(t.rows) * D;
+    g.gate = t.mod + 2 * D; g.gate_stride = ms; g.gate_rows = t.rows;
+    DIT_TRY(dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream), "double block: out-proj gemm");
+  }
+  // per stream: x += gate2 (GELU(adaLN(x; shift2, scale2) W_up^T + b_up) W_dn^T + b_dn)
+  for (const Stream& t : streams) {
+    if (t.rows == 0) continue;
+    const int64_t M = static_cast<int64_t>(B) * t.rows;
+    DIT_TRY(dit::launch_adaln(t.x, M, D, t.rows, t.mod + 3 * D, t.mod + 4 * D, ms, desc->ln_eps, t.h, stream),
+            "double block: adaln 2");
+    DIT_TRY(dit::launch_gemm(gemm(t.h, D, t.w->w_up, t.w->b_up, M, F, D, t.u, F), DIT_EPI_GELU_BF16, stream),
+            "double block: mlp-up gemm");
+    dit::GemmParams g = gemm(t.u, F, t.w->w_dn, t.w->b_dn, M, D, F, t.x, D);
+    g.gate = t.mod + 5 * D; g.gate_stride = ms; g.gate_rows = t.rows;
+    DIT_TRY(dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream), "double block: mlp-down gemm");
+  }
+  return ok();
+}
+
+namespace {
+struct SingleWs {
+  size_t h, qkv, cat, total;
+};
+SingleWs single_ws(const dit_block_desc* d) {
+  const size_t M = static_cast<size_t>(d->attn.batch) * (d->attn.n_vis + d->attn.n_txt);
+  const size_t D = d->hidden, F = d->mlp;
+  SingleWs w;
+  w.h = 0;
+  w.qkv = align256(M * D * 2);
+  w.cat = w.qkv + align256(M * 3 * D * 2);
+  w.total = w.cat + align256(M * (D + F) * 2);
+  return w;
+}
+}  // namespace
+
+size_t dit_single_block_workspace_bytes(const dit_block_desc* desc) {
+  if (check_block_desc(desc) != DIT_OK) return 0;
+  ok();
+  return single_ws(desc).total;
+}
+
+dit_status dit_single_block_forward(const dit_block_desc* desc, const dit_single_block_weights* w,
+                                    const uint16_t* mod, float* x, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  dit_status st = check_block_desc(desc);
+  if (st != DIT_OK) return st;
+  if (!w) return fail(DIT_EINVAL, "weights struct is NULL");
+  const uint16_t* ptrs[] = {w->w1, w->b1, w->g_q, w->g_k, w->w2, w->b2};
+  for (const uint16_t* p : ptrs)
+    if (!p || !aligned(p, 16)) return fail(DIT_EINVAL, "a weight pointer is NULL or not 16-byte aligned");
+  if (!mod || !aligned(mod, 16)) return fail(DIT_EINVAL, "mod is NULL or not 16-byte aligned");
+  if (!x || !aligned(x, 16)) return fail(DIT_EINVAL, "x is NULL or not 16-byte aligned");
+  if (!workspace || !aligned(workspace, 256)) return fail(DIT_EINVAL, "workspace is NULL or not 256-byte aligned");
+  const SingleWs WL = single_ws(desc);
+  if (workspace_bytes < WL.total)
+    return fail(DIT_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, WL.total);
+  const int B = desc->attn.batch, D = desc->hidden, F = desc->mlp;
+  const int64_t N = static_cast<int64_t>(desc->attn.n_vis) + desc->attn.n_txt;
+  const int64_t M = B * N;
+  if (overlap(x, static_cast<size_t>(M) * D * 4, workspace, WL.total))
+    return fail(DIT_EINVAL, "x overlaps the workspace");
+  const int64_t ms = desc->mod_stride;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + WL.h);
+  uint16_t* qkv = reinterpret_cast<uint16_t*>(ws + WL.qkv);
+  uint16_t* cat = reinterpret_cast<uint16_t*>(ws + WL.cat);  // [o | GELU(up)], row stride D + F
+  const int64_t ldcat = static_cast<int64_t>(D) + F;
+  // h = adaLN(x; shift, scale)
+  DIT_TRY(dit::launch_adaln(x, M, D, N, mod, mod + D, ms, desc->ln_eps, h, stream), "single block: adaln");
+  // linear1: rows [0, 3D) of w1 -> q|k|v, rows [3D, 3D + F) -> GELU(up) into the right of cat
+  DIT_TRY(dit::launch_gemm(gemm(h, D, w->w1, w->b1, M, 3 * D, D, qkv, 3 * D), DIT_EPI_BF16, stream),
+          "single block: linear1 qkv");
+  DIT_TRY(dit::launch_gemm(gemm(h, D, w->w1 + static_cast<int64_t>(3) * D * D, w->b1 + 3 * D, M, F, D,
+                                cat + D, ldcat),
+                           DIT_EPI_GELU_BF16, stream),
+          "single block: linear1 mlp");
+  DIT_TRY(dit::launch_qk_rmsnorm_rope(rope_params(desc, qkv, 3 * D, w->g_q, w->g_k), stream),
+          "single block: rmsnorm/rope");
+  {
+    dit::AttnParams ap{};
+    ap.q = qkv; ap.k = qkv + D; ap.v = qkv + 2 * D;
+    ap.q_stride = ap.kv_stride = 3 * D;
+    ap.q_batch = ap.kv_batch = N * 3 * D;
+    ap.out = cat; ap.out_stride = ldcat; ap.out_f32 = 0; ap.lse = nullptr;
+    ap.n_q = ap.n_k = static_cast<int>(N); ap.heads = desc->attn.heads; ap.head_dim = desc->attn.head_dim;
+    ap.batch = B;
+    for (int b = 0; b < DIT_MAX_BATCH; ++b)
+      ap.n_valid[b] = b < B ? desc->attn.n_vis + desc->attn.txt_valid[b] : 0;
+    ap.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(desc->attn.head_dim));
+    DIT_TRY(dit::launch_attention(ap, stream), "single block: attention");
+  }
+  // linear2 on [o | GELU(up)], gated residual
+  dit::GemmParams g = gemm(cat, ldcat, w->w2, w->b2, M, D, D + F, x, D);
+  g.gate = mod + 2 * D; g.gate_stride = ms; g.gate_rows = N;
+  DIT_TRY(dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream), "single block: linear2");
+#undef DIT_TRY
+  return ok();
+}
+
 size_t dit_denoise_workspace_bytes(const dit_model_desc* desc) {
   if (check_model_desc(desc) != DIT_OK) return 0;
   ok();

@@ -346,6 +346,50 @@ dit_status dit_denoise_step(const dit_model_desc* desc, const dit_model_weights*
                             size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * MM-DiT blocks ("ChunkFlow", Appendix B, Per-Block Compute Model: DiT and
+ * MM-DiT, equations (13)-(22)).  Same kernels as dit_block_forward, other
+ * operand routing.  Descriptor as dit_block_forward (attn.n_vis = S image
+ * tokens on the grid, attn.n_txt = L text slots with txt_valid[b] valid,
+ * mod_stride = elements between the batch rows of a modulation tensor, 0 to
+ * share one).  x streams fp32, updated in place; weights bf16 [out, in].
+ *
+ * Double-stream block: the image stream x_img [B, S, D] and the text stream
+ * x_txt [B, L, D] each have their own weights (w_img, w_txt: the DiT block's
+ * set) and modulation (mod_img, mod_txt: [B, 6, D], shift1, scale1, gate1,
+ * shift2, scale2, gate2).  Per stream: h = adaLN(x; shift1, scale1),
+ * q|k|v = h W_qkv^T + b_qkv, q^ = RoPE(RMSNorm_D(q) g_q), k^ likewise (the
+ * stream's own gains; image tokens at their grid position, text at 0).  One
+ * joint attention over [image; text] with keys [0, S + txt_valid[b]); then
+ * per stream x += gate1 (o W_o^T + b_o) and
+ * x += gate2 (GELU(adaLN(x; shift2, scale2) W_up^T + b_up) W_dn^T + b_dn).
+ * Workspace >= dit_double_block_workspace_bytes (= the DiT block's for the
+ * same descriptor), 256-byte aligned.  x_txt may be NULL when L == 0. */
+size_t dit_double_block_workspace_bytes(const dit_block_desc* desc);
+dit_status dit_double_block_forward(const dit_block_desc* desc,
+                                    const dit_block_weights* w_img,
+                                    const dit_block_weights* w_txt,
+                                    const uint16_t* mod_img, const uint16_t* mod_txt,
+                                    float* x_img, float* x_txt, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/* Single-stream block on the joint stream x [B, S + L, D] (image tokens
+ * first): mod [B, 3, D] = (shift, scale, gate);
+ *   h = adaLN(x; shift, scale)
+ *   [q | k | v | up] = h w1^T + b1            w1 [3D + F, D], b1 [3D + F]
+ *   q^, k^ = RoPE(RMSNorm_D(q) g_q), RoPE(RMSNorm_D(k) g_k)
+ *   o = joint attention, keys [0, S + txt_valid[b])
+ *   x += gate ([o | GELU(up)] w2^T + b2)      w2 [D, D + F], b2 [D]
+ * Workspace >= dit_single_block_workspace_bytes, 256-byte aligned. */
+typedef struct dit_single_block_weights {
+  const uint16_t *w1, *b1, *g_q, *g_k, *w2, *b2;
+} dit_single_block_weights;
+size_t dit_single_block_workspace_bytes(const dit_block_desc* desc);
+dit_status dit_single_block_forward(const dit_block_desc* desc,
+                                    const dit_single_block_weights* w,
+                                    const uint16_t* mod, float* x, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Step caching ("Difflet", section 5 Adaptive Step Caching on Trainium;
  * "Difflet Engineering Report", DiT caching: adaptive TeaCache, online delta,
  * and fixed cadence; "19. Diffusion, Image, Video, and World Models", Inside

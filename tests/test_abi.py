@@ -219,3 +219,29 @@ def test_step_cache_argument_errors():
     _expect("DIT_EINVAL", p, desc, w, L, 0.5, None, 1, S_, W, wsb, stream=0)
     _expect("DIT_EINVAL", p, desc, w, L, 0.5, P + 2, 1, S_, W, wsb, stream=0)
     _expect("DIT_EINVAL", p, desc, w, L, 0.5, W + 256, 1, S_, W, wsb, stream=0)  # saved in workspace
+
+
+def test_mmdit_block_argument_errors():
+    desc = _block()
+    nb = D.dit_double_block_workspace_bytes(desc)
+    assert nb == D.dit_block_workspace_bytes(desc)
+    wi = {n: (1 << 32) + (1 << 24) * i for i, n in enumerate(
+        ("w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "w_up", "b_up", "w_dn", "b_dn"))}
+    wt = {n: v + (1 << 31) for n, v in wi.items()}
+    MI, MT, XI, XT, W = 1 << 36, 1 << 37, 1 << 38, 1 << 39, 1 << 40
+    f = D.dit_double_block_forward
+    f_ok = (desc, wi, wt, MI, MT, XI, XT, W, nb)
+    bad_w = dict(wt, w_o=None)
+    _expect("DIT_EINVAL", f, desc, wi, bad_w, MI, MT, XI, XT, W, nb, stream=0)
+    _expect("DIT_EINVAL", f, desc, wi, wt, None, MT, XI, XT, W, nb, stream=0)
+    _expect("DIT_EINVAL", f, desc, wi, wt, MI, MT, XI, None, W, nb, stream=0)
+    _expect("DIT_EINVAL", f, desc, wi, wt, MI, MT, XI, XI + 64, W, nb, stream=0)  # streams overlap
+    _expect("DIT_EWORKSPACE", f, desc, wi, wt, MI, MT, XI, XT, W, nb - 256, stream=0)
+    assert len(f_ok) == 9
+    g = D.dit_single_block_forward
+    sn = D.dit_single_block_workspace_bytes(desc)
+    sw = {n: (1 << 32) + (1 << 24) * i for i, n in enumerate(("w1", "b1", "g_q", "g_k", "w2", "b2"))}
+    _expect("DIT_EINVAL", g, desc, dict(sw, w2=None), MI, XI, W, sn, stream=0)
+    _expect("DIT_EINVAL", g, desc, dict(sw, b1=(1 << 32) + 2), MI, XI, W, sn, stream=0)
+    _expect("DIT_EINVAL", g, desc, sw, MI, W + 256, W, sn, stream=0)  # x inside the workspace
+    _expect("DIT_EWORKSPACE", g, desc, sw, MI, XI, W, sn - 256, stream=0)
