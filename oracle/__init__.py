@@ -8,7 +8,7 @@ residual, classifier-free guidance and the flow-matching Euler update; split
 attention with a statistic merge; and step caching (``stepcache``: the skip
 controller, the relative L1 change score, the output estimator and the
 block-0 probe); and the MM-DiT double-stream and single-stream blocks
-(``mmdit``).
+(``mmdit``); a Wan-style block with text cross-attention (``wan``).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
 leg may import this package.  It shares no code with the HIP path and never
@@ -42,7 +42,7 @@ from .dit import (
     denoise_step,
     step_tokens,
 )
-from . import mmdit, stepcache
+from . import mmdit, stepcache, wan
 
 __all__ = [
     "bf16_decode", "round_bf16", "adaln_modulate", "linear", "rms_norm_full",

@@ -225,3 +225,34 @@ def single_block_inputs(shape: BlockShape) -> dict:
         "b2": _normal_bf16(c[7], (D,), 0.02),
         "txt_valid": _valid_lengths(c[8], shape.txt_valid, B, shape.n_txt),
     }
+
+
+_WAN_ORDER = ("x", "ctx", "mod", "txt_valid", "w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o",
+              "w_cq", "b_cq", "w_ckv", "b_ckv", "g_cq", "g_ck", "w_co", "b_co",
+              "w_up", "b_up", "w_dn", "b_dn")
+
+
+def wan_block_inputs(shape: BlockShape) -> dict:
+    """Inputs of a Wan-style block: video tokens x [B, n_vis, D], text context
+    ctx [B, n_txt, D] (N(0, 1)), mod [B, 6, D], txt_valid [B] and the weights
+    of its self-attention (w_qkv, b_qkv, g_q, g_k, w_o, b_o), cross-attention
+    (w_cq [D, D], b_cq, w_ckv [2D, D], b_ckv, g_cq, g_ck, w_co [D, D], b_co)
+    and MLP (w_up, b_up, w_dn, b_dn); weights and biases N(0, 0.02), gains
+    1 + N(0, 0.02)."""
+    B, S, L, D, F = shape.batch, shape.n_vis, shape.n_txt, shape.hidden, shape.mlp
+    c = dict(zip(_WAN_ORDER, seed_sequence(shape.seed).spawn(len(_WAN_ORDER))))
+    shapes = {"w_qkv": (3 * D, D), "b_qkv": (3 * D,), "w_o": (D, D), "b_o": (D,),
+              "w_cq": (D, D), "b_cq": (D,), "w_ckv": (2 * D, D), "b_ckv": (2 * D,),
+              "w_co": (D, D), "b_co": (D,), "w_up": (F, D), "b_up": (F,), "w_dn": (D, F),
+              "b_dn": (D,)}
+    out = {
+        "x": _normal_bf16(c["x"], (B, S, D)),
+        "ctx": _normal_bf16(c["ctx"], (B, L, D)),
+        "mod": _normal_bf16(c["mod"], (B, 6, D)),
+        "txt_valid": _valid_lengths(c["txt_valid"], shape.txt_valid, B, L),
+    }
+    for k, shp in shapes.items():
+        out[k] = _normal_bf16(c[k], shp, 0.02)
+    for k in ("g_q", "g_k", "g_cq", "g_ck"):
+        out[k] = _normal_bf16(c[k], (D,), 0.02, 1.0)
+    return out

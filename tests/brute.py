@@ -211,3 +211,44 @@ def single_block(x, mod, W, s, valid):
             rows.append([x[b][i][c] + mb[2][c] * y2[c] for c in range(D)])
         res.append(rows)
     return res
+
+
+def wan_block(x, ctx, mod, W, s, valid):
+    """Wan-style block, one token at a time: adaLN + self-attention over the
+    video tokens (RMSNorm + RoPE), gated residual; plain LayerNorm +
+    cross-attention to the valid context tokens (RMSNorm, no RoPE), residual;
+    adaLN + GELU MLP, gated residual."""
+    B, S, L, D = s.batch, s.n_vis, s.n_txt, s.hidden
+    pos_of = _pos_fn(s)
+    zeros = [0.0] * D
+    res = []
+    for b in range(B):
+        mb = mod[b]
+        qs, ks, vs = [], [], []
+        for i in range(S):
+            h = ln_mod(x[b][i], mb[0], mb[1], s.ln_eps)
+            qkv = lin(h, W["w_qkv"], W["b_qkv"])
+            qs.append(_rms_rope(qkv[:D], W["g_q"], pos_of(i), s))
+            ks.append(_rms_rope(qkv[D:2 * D], W["g_k"], pos_of(i), s))
+            vs.append(qkv[2 * D:])
+        kc, vc = [], []
+        for j in range(L):
+            kv = lin(ctx[b][j], W["w_ckv"], W["b_ckv"])
+            kc.append(_rms_rope(kv[:D], W["g_ck"], (0, 0, 0), s))
+            vc.append(kv[D:])
+        rows = []
+        for i in range(S):
+            o = _attend(qs[i], ks, vs, S, s)
+            y = lin(o, W["w_o"], W["b_o"])
+            x1 = [x[b][i][c] + mb[2][c] * y[c] for c in range(D)]
+            hc = ln_mod(x1, zeros, zeros, s.ln_eps)
+            qc = _rms_rope(lin(hc, W["w_cq"], W["b_cq"]), W["g_cq"], (0, 0, 0), s)
+            oc = _attend(qc, kc, vc, int(valid[b]), s) if int(valid[b]) > 0 else [0.0] * D
+            yc = lin(oc, W["w_co"], W["b_co"])
+            x2 = [x1[c] + yc[c] for c in range(D)]
+            h2 = ln_mod(x2, mb[3], mb[4], s.ln_eps)
+            u = [_gelu(z) for z in lin(h2, W["w_up"], W["b_up"])]
+            y2 = lin(u, W["w_dn"], W["b_dn"])
+            rows.append([x2[c] + mb[5][c] * y2[c] for c in range(D)])
+        res.append(rows)
+    return res
