@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libdit.so")
 
 DIT_MAX_BATCH = 8
 STATUS = {0: "DIT_OK", 1: "DIT_EINVAL", 2: "DIT_EUNSUPPORTED", 3: "DIT_EWORKSPACE", 4: "DIT_EHIP"}
-EPI_BF16, EPI_GELU_BF16, EPI_SILU_BF16, EPI_F32, EPI_GATED_RES_F32 = range(5)
+EPI_BF16, EPI_GELU_BF16, EPI_SILU_BF16, EPI_F32, EPI_GATED_RES_F32, EPI_RES_F32 = range(6)
 
 EXPORTED = (
     "dit_joint_attention", "dit_attention_partial", "dit_attention_merge", "dit_linear", "dit_adaln_modulate", "dit_qk_rmsnorm_rope",
@@ -29,6 +29,7 @@ EXPORTED = (
     "dit_cache_ctrl_observe",
     "dit_double_block_workspace_bytes", "dit_double_block_forward",
     "dit_single_block_workspace_bytes", "dit_single_block_forward",
+    "dit_wan_block_workspace_bytes", "dit_wan_block_forward",
     "dit_status_string", "dit_last_error", "dit_version",
 )
 DTYPE_BF16, DTYPE_F32 = 0, 1
@@ -105,6 +106,14 @@ class SingleBlockWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "b1", "g_q", "g_k", "w2", "b2")]
 
 
+WAN_WEIGHT_NAMES = ("w_qkv", "b_qkv", "g_q", "g_k", "w_o", "b_o", "w_cq", "b_cq", "w_ckv", "b_ckv",
+                    "g_cq", "g_ck", "w_co", "b_co", "w_up", "b_up", "w_dn", "b_dn")
+
+
+class WanBlockWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WAN_WEIGHT_NAMES]
+
+
 class CachePolicy(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("n_steps", ctypes.c_int32), ("warmup", ctypes.c_int32),
                 ("cooldown", ctypes.c_int32), ("cadence", ctypes.c_int32), ("n_coef", ctypes.c_int32),
@@ -171,6 +180,9 @@ def lib() -> ctypes.CDLL:
             "dit_single_block_forward": (st, [ctypes.POINTER(BlockDesc),
                                               ctypes.POINTER(SingleBlockWeights), vp, vp, vp,
                                               ctypes.c_size_t, vp]),
+            "dit_wan_block_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(BlockDesc)]),
+            "dit_wan_block_forward": (st, [ctypes.POINTER(BlockDesc), ctypes.POINTER(WanBlockWeights),
+                                           vp, vp, vp, vp, ctypes.c_size_t, vp]),
             "dit_status_string": (ctypes.c_char_p, [st]),
             "dit_last_error": (ctypes.c_char_p, []),
             "dit_version": (ctypes.c_char_p, []),
@@ -449,3 +461,21 @@ def dit_single_block_forward(desc: BlockDesc, weights, mod, x, workspace, worksp
     w = weights if isinstance(weights, SingleBlockWeights) else single_block_weights(weights)
     _check(lib().dit_single_block_forward(ctypes.byref(desc), ctypes.byref(w), _ptr(mod), _ptr(x),
                                           _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Wan-style block
+
+def wan_block_weights(tensors: dict) -> WanBlockWeights:
+    return WanBlockWeights(*[_ptr(tensors[n]) for n in WAN_WEIGHT_NAMES])
+
+
+def dit_wan_block_workspace_bytes(desc: BlockDesc) -> int:
+    return _ws_bytes(lib().dit_wan_block_workspace_bytes, desc)
+
+
+def dit_wan_block_forward(desc: BlockDesc, weights, mod, x, ctx, workspace, workspace_bytes,
+                          stream=None):
+    w = weights if isinstance(weights, WanBlockWeights) else wan_block_weights(weights)
+    _check(lib().dit_wan_block_forward(ctypes.byref(desc), ctypes.byref(w), _ptr(mod), _ptr(x),
+                                       _ptr(ctx), _ptr(workspace), workspace_bytes, _stream(stream)))

@@ -156,7 +156,7 @@ dit_status check_linear(const dit_linear_args* a) {
   if (!a->a || !a->w || !a->out) return fail(DIT_EINVAL, "NULL a, w or out");
   if (a->k % 64 != 0) return fail(DIT_EUNSUPPORTED, "k %d must be a multiple of 64", a->k);
   if (a->n % 8 != 0) return fail(DIT_EUNSUPPORTED, "n %d must be a multiple of 8", a->n);
-  if (a->epilogue < DIT_EPI_BF16 || a->epilogue > DIT_EPI_GATED_RES_F32)
+  if (a->epilogue < DIT_EPI_BF16 || a->epilogue > DIT_EPI_RES_F32)
     return fail(DIT_EINVAL, "unknown epilogue %d", a->epilogue);
   if (a->lda < a->k || a->lda % 8 != 0)
     return fail(DIT_EINVAL, "lda %lld must be >= k and a multiple of 8", static_cast<long long>(a->lda));
@@ -179,7 +179,7 @@ dit_status check_linear(const dit_linear_args* a) {
     const int64_t groups = a->group_rows > 0 ? (a->m + a->group_rows - 1) / a->group_rows : 1;
     const size_t a_bytes = static_cast<size_t>(((groups - 1) * (a->group_rows > 0 ? a->a_group_stride : 0)) +
                                                (span_rows - 1) * a->lda + a->k) * 2;
-    const size_t esz = a->epilogue == DIT_EPI_F32 ? 4 : 2;
+    const size_t esz = a->epilogue == DIT_EPI_F32 || a->epilogue == DIT_EPI_RES_F32 ? 4 : 2;
     const size_t c_bytes = static_cast<size_t>(((groups - 1) * (a->group_rows > 0 ? a->c_group_stride : 0)) +
                                                (span_rows - 1) * a->ldc + a->n) * esz;
     if (overlap(a->a, a_bytes, a->out, c_bytes))
@@ -534,14 +534,16 @@ dit_status dit_adaln_modulate(const float* x, int64_t rows, int32_t hidden, int6
                               float eps, uint16_t* out, hipStream_t stream) {
   if (rows < 0) return fail(DIT_EINVAL, "rows %lld < 0", static_cast<long long>(rows));
   if (rows == 0) return ok();
-  if (!x || !shift || !scale || !out) return fail(DIT_EINVAL, "NULL x, shift, scale or out");
+  if (!x || !out) return fail(DIT_EINVAL, "NULL x or out");
+  if ((shift == nullptr) != (scale == nullptr))
+    return fail(DIT_EINVAL, "shift and scale must both be given or both be NULL");
   if (hidden < 8 || hidden % 8 != 0 || hidden > 16384)
     return fail(DIT_EUNSUPPORTED, "hidden %d must be a multiple of 8 in [8, 16384]", hidden);
   if (rows_per_batch < 1) return fail(DIT_EINVAL, "rows_per_batch must be >= 1");
   if (mod_stride < 0 || mod_stride % 4 != 0)
     return fail(DIT_EINVAL, "mod_stride must be >= 0 and a multiple of 4");
   if (!(eps >= 0.f)) return fail(DIT_EINVAL, "eps must be >= 0");
-  if (!aligned(x, 16) || !aligned(out, 8) || !aligned(shift, 8) || !aligned(scale, 8))
+  if (!aligned(x, 16) || !aligned(out, 8) || (shift && (!aligned(shift, 8) || !aligned(scale, 8))))
     return fail(DIT_EINVAL, "x must be 16-byte aligned; out, shift, scale 8-byte aligned");
   if (overlap(x, static_cast<size_t>(rows) * hidden * 4, out, static_cast<size_t>(rows) * hidden * 2))
     return fail(DIT_EINVAL, "out overlaps x");
@@ -848,6 +850,146 @@ dit_status dit_single_block_forward(const dit_block_desc* desc, const dit_single
   dit::GemmParams g = gemm(cat, ldcat, w->w2, w->b2, M, D, D + F, x, D);
   g.gate = mod + 2 * D; g.gate_stride = ms; g.gate_rows = N;
   DIT_TRY(dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream), "single block: linear2");
+#undef DIT_TRY
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Wan-style block ("ChunkFlow", Appendix B, equations (7)-(12)): self-
+// attention over the video tokens, cross-attention to the text context, MLP.
+
+namespace {
+struct WanWs {
+  size_t h, big, ckv, total;
+};
+WanWs wan_ws(const dit_block_desc* d) {
+  const size_t B = d->attn.batch, S = d->attn.n_vis, L = d->attn.n_txt;
+  const size_t D = d->hidden, F = d->mlp;
+  WanWs w;
+  w.h = 0;
+  w.big = align256(B * S * D * 2);
+  w.ckv = w.big + align256(B * S * (3 * D > F ? 3 * D : F) * 2);
+  w.total = w.ckv + align256(B * L * 2 * D * 2);
+  return w;
+}
+
+dit::AttnParams attn_params(const uint16_t* q, int64_t q_stride, int64_t q_batch, const uint16_t* k,
+                            const uint16_t* v, int64_t kv_stride, int64_t kv_batch, uint16_t* out,
+                            int64_t out_stride, int n_q, int n_k, const dit_attn_desc& a,
+                            const int* n_valid) {
+  dit::AttnParams ap{};
+  ap.q = q; ap.k = k; ap.v = v;
+  ap.q_stride = q_stride; ap.kv_stride = kv_stride;
+  ap.q_batch = q_batch; ap.kv_batch = kv_batch;
+  ap.out = out; ap.out_stride = out_stride; ap.out_f32 = 0; ap.lse = nullptr;
+  ap.n_q = n_q; ap.n_k = n_k; ap.heads = a.heads; ap.head_dim = a.head_dim; ap.batch = a.batch;
+  for (int b = 0; b < DIT_MAX_BATCH; ++b) ap.n_valid[b] = b < a.batch ? n_valid[b] : 0;
+  ap.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(a.head_dim));
+  return ap;
+}
+}  // namespace
+
+size_t dit_wan_block_workspace_bytes(const dit_block_desc* desc) {
+  if (check_block_desc(desc) != DIT_OK) return 0;
+  ok();
+  return wan_ws(desc).total;
+}
+
+dit_status dit_wan_block_forward(const dit_block_desc* desc, const dit_wan_block_weights* w,
+                                 const uint16_t* mod, float* x, const uint16_t* ctx,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dit_status st = check_block_desc(desc);
+  if (st != DIT_OK) return st;
+  if (!w) return fail(DIT_EINVAL, "weights struct is NULL");
+  const uint16_t* ptrs[] = {w->w_qkv, w->b_qkv, w->g_q,  w->g_k,  w->w_o,  w->b_o,
+                            w->w_cq,  w->b_cq,  w->w_ckv, w->b_ckv, w->g_cq, w->g_ck,
+                            w->w_co,  w->b_co,  w->w_up, w->b_up, w->w_dn, w->b_dn};
+  for (const uint16_t* p : ptrs)
+    if (!p || !aligned(p, 16)) return fail(DIT_EINVAL, "a weight pointer is NULL or not 16-byte aligned");
+  const int B = desc->attn.batch, S = desc->attn.n_vis, L = desc->attn.n_txt;
+  const int D = desc->hidden, F = desc->mlp;
+  if (!mod || !aligned(mod, 16)) return fail(DIT_EINVAL, "mod is NULL or not 16-byte aligned");
+  if (!x || !aligned(x, 16)) return fail(DIT_EINVAL, "x is NULL or not 16-byte aligned");
+  if (L > 0 && (!ctx || !aligned(ctx, 16))) return fail(DIT_EINVAL, "ctx is NULL or not 16-byte aligned");
+  if (!workspace || !aligned(workspace, 256)) return fail(DIT_EINVAL, "workspace is NULL or not 256-byte aligned");
+  const WanWs WL = wan_ws(desc);
+  if (workspace_bytes < WL.total)
+    return fail(DIT_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, WL.total);
+  const int64_t M = static_cast<int64_t>(B) * S;
+  const size_t x_bytes = static_cast<size_t>(M) * D * 4;
+  if (overlap(x, x_bytes, workspace, WL.total) ||
+      (L > 0 && overlap(x, x_bytes, ctx, static_cast<size_t>(B) * L * D * 2)))
+    return fail(DIT_EINVAL, "x overlaps the workspace or ctx");
+  const int64_t ms = desc->mod_stride;
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + WL.h);  // h, o, LN(x1), cross o, h2
+  uint16_t* big = reinterpret_cast<uint16_t*>(ws + WL.big);  // self q|k|v, cross q, MLP hidden
+  uint16_t* ckv = reinterpret_cast<uint16_t*>(ws + WL.ckv);  // context k|v [B*L, 2D]
+#define DIT_TRY(expr, what)                            \
+  do {                                                 \
+    const hipError_t e_ = (expr);                      \
+    if (e_ != hipSuccess) return hip_status(e_, what); \
+  } while (0)
+  // self-attention over the video tokens
+  DIT_TRY(dit::launch_adaln(x, M, D, S, mod, mod + D, ms, desc->ln_eps, hbuf, stream), "wan block: adaln 1");
+  DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_qkv, w->b_qkv, M, 3 * D, D, big, 3 * D), DIT_EPI_BF16, stream),
+          "wan block: qkv gemm");
+  {
+    dit::RopeParams rp = rope_params(desc, big, 3 * D, w->g_q, w->g_k);
+    rp.n_tok = S;  // the sequence is the video tokens alone
+    rp.rows = M;
+    DIT_TRY(dit::launch_qk_rmsnorm_rope(rp, stream), "wan block: rmsnorm/rope");
+  }
+  {
+    int nv[DIT_MAX_BATCH];
+    for (int b = 0; b < DIT_MAX_BATCH; ++b) nv[b] = S;
+    DIT_TRY(dit::launch_attention(attn_params(big, 3 * D, static_cast<int64_t>(S) * 3 * D, big + D, big + 2 * D,
+                                              3 * D, static_cast<int64_t>(S) * 3 * D, hbuf, D, S, S,
+                                              desc->attn, nv),
+                                  stream),
+            "wan block: self-attention");
+  }
+  {
+    dit::GemmParams g = gemm(hbuf, D, w->w_o, w->b_o, M, D, D, x, D);
+    g.gate = mod + 2 * D; g.gate_stride = ms; g.gate_rows = S;
+    DIT_TRY(dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream), "wan block: out-proj gemm");
+  }
+  // cross-attention: q from LN(x), k|v from the context, keys [0, txt_valid[b])
+  DIT_TRY(dit::launch_adaln(x, M, D, S, nullptr, nullptr, 0, desc->ln_eps, hbuf, stream), "wan block: layernorm");
+  DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_cq, w->b_cq, M, D, D, big, D), DIT_EPI_BF16, stream),
+          "wan block: cross q gemm");
+  {
+    // RMSNorm over D with the cross gains; position 0 for every row makes the
+    // rotation the identity
+    dit::RopeParams rp = rope_params(desc, big, D, w->g_cq, w->g_cq);
+    rp.q_only = 1; rp.n_tok = 1; rp.n_vis = 0; rp.rows = M;
+    DIT_TRY(dit::launch_qk_rmsnorm_rope(rp, stream), "wan block: cross q rmsnorm");
+  }
+  if (L > 0) {
+    DIT_TRY(dit::launch_gemm(gemm(ctx, D, w->w_ckv, w->b_ckv, static_cast<int64_t>(B) * L, 2 * D, D, ckv, 2 * D),
+                             DIT_EPI_BF16, stream),
+            "wan block: cross kv gemm");
+    dit::RopeParams rp = rope_params(desc, ckv, 2 * D, w->g_ck, w->g_ck);
+    rp.q_only = 1; rp.n_tok = 1; rp.n_vis = 0; rp.rows = static_cast<int64_t>(B) * L;
+    DIT_TRY(dit::launch_qk_rmsnorm_rope(rp, stream), "wan block: cross k rmsnorm");
+  }
+  DIT_TRY(dit::launch_attention(attn_params(big, D, static_cast<int64_t>(S) * D, ckv, ckv + D, 2 * D,
+                                            static_cast<int64_t>(L) * 2 * D, hbuf, D, S, L > 0 ? L : 1,
+                                            desc->attn, desc->attn.txt_valid),
+                                stream),
+          "wan block: cross-attention");
+  DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_co, w->b_co, M, D, D, x, D), DIT_EPI_RES_F32, stream),
+          "wan block: cross out-proj gemm");
+  // MLP
+  DIT_TRY(dit::launch_adaln(x, M, D, S, mod + 3 * D, mod + 4 * D, ms, desc->ln_eps, hbuf, stream),
+          "wan block: adaln 2");
+  DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_up, w->b_up, M, F, D, big, F), DIT_EPI_GELU_BF16, stream),
+          "wan block: mlp-up gemm");
+  {
+    dit::GemmParams g = gemm(big, F, w->w_dn, w->b_dn, M, D, F, x, D);
+    g.gate = mod + 5 * D; g.gate_stride = ms; g.gate_rows = S;
+    DIT_TRY(dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream), "wan block: mlp-down gemm");
+  }
 #undef DIT_TRY
   return ok();
 }

@@ -40,7 +40,7 @@ constexpr int kThreads = 256;
 constexpr int kAChunks = kTM * kBK / 8 / kThreads;  // 16-byte chunks per thread: 8
 constexpr int kWChunks = kTN * kBK / 8 / kThreads;  // 4
 
-enum { EPI_BF16 = 0, EPI_GELU = 1, EPI_SILU = 2, EPI_F32 = 3, EPI_GATED = 4 };
+enum { EPI_BF16 = 0, EPI_GELU = 1, EPI_SILU = 2, EPI_F32 = 3, EPI_GATED = 4, EPI_RES = 5 };
 
 __device__ __forceinline__ int64_t a_row_offset(const GemmParams& p, int64_t r) {
   return p.group_rows > 0 ? (r / p.group_rows) * p.a_group_stride + (r % p.group_rows) * p.lda
@@ -70,10 +70,13 @@ __device__ __forceinline__ void store_epilogue(const GemmParams& p, int64_t m, i
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = y[e] / (1.f + expf(-y[e]));
   }
-  if (EPI == EPI_F32 || EPI == EPI_GATED) {
+  if (EPI == EPI_F32 || EPI == EPI_GATED || EPI == EPI_RES) {
     float* dst = static_cast<float*>(p.out) + crow + n;
     f32x4 o;
-    if (EPI == EPI_GATED) {
+    if (EPI == EPI_RES) {
+      o = *reinterpret_cast<const f32x4*>(dst);
+      o[0] += y[0]; o[1] += y[1]; o[2] += y[2]; o[3] += y[3];
+    } else if (EPI == EPI_GATED) {
       const uint16_t* grow = p.gate + (m / p.gate_rows) * p.gate_stride;
       o = *reinterpret_cast<const f32x4*>(dst);
       const u32x2 gg = *reinterpret_cast<const u32x2*>(grow + n);
@@ -422,6 +425,7 @@ hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s) {
       case EPI_SILU: hipLaunchKernelGGL(big::gemm_kernel<EPI_SILU>, grid, block, 0, s, p, tiles_m, tiles_n); break;
       case EPI_F32: hipLaunchKernelGGL(big::gemm_kernel<EPI_F32>, grid, block, 0, s, p, tiles_m, tiles_n); break;
       case EPI_GATED: hipLaunchKernelGGL(big::gemm_kernel<EPI_GATED>, grid, block, 0, s, p, tiles_m, tiles_n); break;
+      case EPI_RES: hipLaunchKernelGGL(big::gemm_kernel<EPI_RES>, grid, block, 0, s, p, tiles_m, tiles_n); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -434,6 +438,7 @@ hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s) {
     case EPI_SILU: hipLaunchKernelGGL(gemm_kernel<EPI_SILU>, grid, block, 0, s, p); break;
     case EPI_F32: hipLaunchKernelGGL(gemm_kernel<EPI_F32>, grid, block, 0, s, p); break;
     case EPI_GATED: hipLaunchKernelGGL(gemm_kernel<EPI_GATED>, grid, block, 0, s, p); break;
+    case EPI_RES: hipLaunchKernelGGL(gemm_kernel<EPI_RES>, grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -66,6 +66,7 @@ struct RopeParams {
   int grid_h, grid_w;
   int rope_t, rope_h, rope_w;
   float theta, eps;
+  int q_only;  // normalise only the q half (columns [0, hidden)) of each row
 };
 hipError_t launch_qk_rmsnorm_rope(const RopeParams& p, hipStream_t s);
 hipError_t launch_positions(const RopeParams& p, int32_t* out, hipStream_t s);

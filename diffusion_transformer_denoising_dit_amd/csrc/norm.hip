@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kThreads) void adaln_kernel(const float* __restrict
   const float var = block_sum<kThreads>(q, red) / hidden;
   const float rstd = 1.f / sqrtf(var + eps);
   const int64_t b = r / rows_per_batch;
+  const bool modulated = shift != nullptr;  // else a plain LayerNorm (shift = scale = 0)
   const uint16_t* sh = shift + b * mod_stride;
   const uint16_t* sc = scale + b * mod_stride;
   uint16_t* orow = out + r * hidden;
@@ -61,8 +62,11 @@ __global__ __launch_bounds__(kThreads) void adaln_kernel(const float* __restrict
   for (int i = 0; i < NV; ++i) {
     const int c = tid + i * kThreads;
     if (c < nvec) {
-      const u32x2 s2 = *reinterpret_cast<const u32x2*>(sh + 4 * c);
-      const u32x2 c2 = *reinterpret_cast<const u32x2*>(sc + 4 * c);
+      u32x2 s2 = {0u, 0u}, c2 = {0u, 0u};
+      if (modulated) {
+        s2 = *reinterpret_cast<const u32x2*>(sh + 4 * c);
+        c2 = *reinterpret_cast<const u32x2*>(sc + 4 * c);
+      }
       const float shf[4] = {__uint_as_float(s2[0] << 16), __uint_as_float(s2[0] & 0xffff0000u),
                             __uint_as_float(s2[1] << 16), __uint_as_float(s2[1] & 0xffff0000u)};
       const float scf[4] = {__uint_as_float(c2[0] << 16), __uint_as_float(c2[0] & 0xffff0000u),
@@ -119,13 +123,14 @@ __global__ __launch_bounds__(kThreads) void qk_rmsnorm_rope_kernel(RopeParams p)
   }
 
   const int nq = p.hidden / 8;  // chunks in the q half; the k half follows
+  const int nc = p.q_only ? nq : 2 * nq;
   uint16_t* row = p.qkv + r * p.row_stride;
   u32x4 v[NV];
   float sq = 0.f, sk = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = tid + i * kThreads;
-    if (c < 2 * nq) {
+    if (c < nc) {
       const int col = c < nq ? 8 * c : p.hidden + 8 * (c - nq);
       v[i] = *reinterpret_cast<const u32x4*>(row + col);
       float f[8];
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void qk_rmsnorm_rope_kernel(RopeParams p)
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = tid + i * kThreads;
-    if (c < 2 * nq) {
+    if (c < nc) {
       const bool isq = c < nq;
       const int cin = isq ? 8 * c : 8 * (c - nq);  // column within the q or k half
       const uint16_t* g = (isq ? p.g_q : p.g_k) + cin;

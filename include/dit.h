@@ -165,7 +165,8 @@ typedef enum dit_epilogue {
   DIT_EPI_GELU_BF16 = 1,   /* out(bf16) = GELU_erf(acc + bias)               */
   DIT_EPI_SILU_BF16 = 2,   /* out(bf16) = SiLU(acc + bias)                   */
   DIT_EPI_F32 = 3,         /* out(fp32) = acc + bias                         */
-  DIT_EPI_GATED_RES_F32 = 4 /* out(fp32) += gate[g,:] * (acc + bias)         */
+  DIT_EPI_GATED_RES_F32 = 4, /* out(fp32) += gate[g,:] * (acc + bias)        */
+  DIT_EPI_RES_F32 = 5        /* out(fp32) += acc + bias                        */
 } dit_epilogue;
 
 /* y = A W^T + bias with an epilogue.
@@ -174,8 +175,9 @@ typedef enum dit_epilogue {
  *   w     bf16 [n, k], contiguous (k contiguous): PyTorch Linear layout.
  *   bias  bf16 [n] or NULL.
  *   out   row r at out + (r / group_rows)*c_group_stride + (r % group_rows)*ldc;
- *         bf16 or fp32 by epilogue.  With DIT_EPI_GATED_RES_F32 `out` is read
- *         and written (the residual stream); otherwise it must not overlap a.
+ *         bf16 or fp32 by epilogue.  With DIT_EPI_GATED_RES_F32 and
+ *         DIT_EPI_RES_F32 `out` is read and written (the residual stream); it
+ *         must not overlap a (checked for every epilogue but the gated one).
  *   gate  bf16, DIT_EPI_GATED_RES_F32 only: row r uses gate + (r / gate_rows)
  *         * gate_stride (gate_rows >= 1).
  * Requires k % 64 == 0 (DIT_EUNSUPPORTED otherwise), lda/ldc/strides multiples
@@ -202,7 +204,8 @@ dit_status dit_linear(const dit_linear_args* args, hipStream_t stream);
  *   out[r,:] = (x - mean) / sqrt(var + eps) * (1 + scale[b,:]) + shift[b,:]
  * with biased variance, no learned affine, b = r / rows_per_batch, and
  * shift/scale bf16 rows at shift + b*mod_stride, scale + b*mod_stride
- * (mod_stride may be 0 to share one vector).  out is bf16 [rows, hidden].
+ * (mod_stride may be 0 to share one vector); shift = scale = NULL is a plain
+ * LayerNorm without affine.  out is bf16 [rows, hidden].
  * hidden % 8 == 0 and hidden <= 16384. */
 dit_status dit_adaln_modulate(const float* x, int64_t rows, int32_t hidden,
                               int64_t rows_per_batch, const uint16_t* shift,
@@ -388,6 +391,35 @@ dit_status dit_single_block_forward(const dit_block_desc* desc,
                                     const dit_single_block_weights* w,
                                     const uint16_t* mod, float* x, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Wan-style block ("ChunkFlow", Appendix B, equations (7)-(12)): self-
+ * attention over the video tokens, cross-attention to the text context, MLP.
+ * Descriptor as dit_block_forward, read as: attn.n_vis = S video tokens on
+ * the grid (the self-attention sequence), attn.n_txt = L context slots of
+ * which txt_valid[b] are valid (the cross-attention keys [0, txt_valid[b])).
+ *   x    fp32 [B, S, D], in place;  ctx bf16 [B, L, D] (may be NULL if L == 0)
+ *   mod  bf16 [B, 6, D] (shift1, scale1, gate1, shift2, scale2, gate2), batch
+ *        rows mod_stride apart (0 = shared)
+ *   h  = adaLN(x; shift1, scale1);  q|k|v = h W_qkv^T + b_qkv;
+ *   q^, k^ = RoPE(RMSNorm_D(.) g_q / g_k) at the grid positions;
+ *   x += gate1 (SelfAttn(q^, k^, v) W_o^T + b_o)
+ *   c  = LN(x) (no affine);  qc = RMSNorm_D(c W_cq^T + b_cq) g_cq;
+ *   kc|vc = ctx W_ckv^T + b_ckv (w_ckv [2D, D]: key rows, then value rows);
+ *   kc = RMSNorm_D(kc) g_ck;  x += CrossAttn(qc, kc, vc) W_co^T + b_co
+ *        (no RoPE; a row with no valid context token attends to nothing: 0)
+ *   x += gate2 (GELU(adaLN(x; shift2, scale2) W_up^T + b_up) W_dn^T + b_dn)
+ * Workspace >= dit_wan_block_workspace_bytes, 256-byte aligned. */
+typedef struct dit_wan_block_weights {
+  const uint16_t *w_qkv, *b_qkv, *g_q, *g_k, *w_o, *b_o;
+  const uint16_t *w_cq, *b_cq, *w_ckv, *b_ckv, *g_cq, *g_ck, *w_co, *b_co;
+  const uint16_t *w_up, *b_up, *w_dn, *b_dn;
+} dit_wan_block_weights;
+size_t dit_wan_block_workspace_bytes(const dit_block_desc* desc);
+dit_status dit_wan_block_forward(const dit_block_desc* desc, const dit_wan_block_weights* w,
+                                 const uint16_t* mod, float* x, const uint16_t* ctx,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Step caching ("Difflet", section 5 Adaptive Step Caching on Trainium;

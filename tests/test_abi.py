@@ -245,3 +245,17 @@ def test_mmdit_block_argument_errors():
     _expect("DIT_EINVAL", g, desc, dict(sw, b1=(1 << 32) + 2), MI, XI, W, sn, stream=0)
     _expect("DIT_EINVAL", g, desc, sw, MI, W + 256, W, sn, stream=0)  # x inside the workspace
     _expect("DIT_EWORKSPACE", g, desc, sw, MI, XI, W, sn - 256, stream=0)
+
+
+def test_wan_block_argument_errors():
+    desc = _block()
+    nb = D.dit_wan_block_workspace_bytes(desc)
+    w = {n: (1 << 32) + (1 << 24) * i for i, n in enumerate(D.WAN_WEIGHT_NAMES)}
+    MOD, X, CTX, W = 1 << 36, 1 << 37, 1 << 38, 1 << 40
+    f = D.dit_wan_block_forward
+    _expect("DIT_EINVAL", f, desc, dict(w, w_ckv=None), MOD, X, CTX, W, nb, stream=0)
+    _expect("DIT_EINVAL", f, desc, dict(w, g_cq=(1 << 32) + 8), MOD, X, CTX, W, nb, stream=0)
+    _expect("DIT_EINVAL", f, desc, w, MOD, X, None, W, nb, stream=0)         # context needed
+    _expect("DIT_EINVAL", f, desc, w, MOD, X, X + 64, W, nb, stream=0)      # ctx inside x
+    _expect("DIT_EINVAL", f, desc, w, MOD, W + 512, CTX, W, nb, stream=0)   # x inside workspace
+    _expect("DIT_EWORKSPACE", f, desc, w, MOD, X, CTX, W, nb - 256, stream=0)

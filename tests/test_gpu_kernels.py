@@ -56,12 +56,23 @@ def test_linear_epilogues(M, N, K, epi):
 # workgroup tiles, K slices streamed into an LDS ring): ragged M and N, one
 # and several K slices, every epilogue, bitwise-equal reruns.
 @pytest.mark.parametrize("M,N,K", [(1100, 520, 128), (1031, 264, 64), (2304, 512, 320)])
-@pytest.mark.parametrize("epi", ["bf16", "gelu", "f32", "gated"])
+@pytest.mark.parametrize("epi", ["bf16", "gelu", "f32", "gated", "res"])
 def test_linear_large_tiles(M, N, K, epi):
     a, w, b = _gemm_case(200 + M + K, M, N, K)
     y = O.linear(_dec(a), _dec(w), _dec(b))
     da, dw, db = dev_bf16(a), dev_bf16(w), dev_bf16(b)
-    if epi == "gated":
+    if epi == "res":
+        x0 = G.normal_bf16(13, (M, N))
+        want = _dec(x0) + y
+        outs = []
+        for _ in range(2):
+            x = dev_f32_from_bf16(x0)
+            D.dit_linear(da, K, dw, db, M, N, K, D.EPI_RES_F32, x, N)
+            outs.append(x)
+        torch.cuda.synchronize()
+        assert_parity(host(outs[0]), want, f"large residual {M}x{N}x{K}",
+                      max_abs=1e-4 * np.abs(want).max(), rel_l2=1e-5)
+    elif epi == "gated":
         rows_g = M // 2 + 1
         gate = G.normal_bf16(11, (2, N))
         x0 = G.normal_bf16(12, (M, N))
@@ -364,3 +375,25 @@ def test_casts_roundtrip():
     np.testing.assert_array_equal(host(f)[:, :40], _dec(a))
     assert np.isnan(host(f)[:, 40:]).all()
     np.testing.assert_array_equal(bits_of(b)[:, :40], a)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 200, 192), (33, 64, 64)])
+def test_linear_residual_small_tiles(M, N, K):
+    a, w, b = _gemm_case(300 + M, M, N, K)
+    x0 = G.normal_bf16(14, (M, N))
+    want = _dec(x0) + O.linear(_dec(a), _dec(w), _dec(b))
+    x = dev_f32_from_bf16(x0)
+    D.dit_linear(dev_bf16(a), K, dev_bf16(w), dev_bf16(b), M, N, K, D.EPI_RES_F32, x, N)
+    torch.cuda.synchronize()
+    assert_parity(host(x), want, f"residual {M}x{N}x{K}", max_abs=1e-4 * np.abs(want).max(),
+                  rel_l2=1e-5)
+
+
+@pytest.mark.parametrize("rows,hidden", [(300, 256), (7, 5120)])
+def test_layernorm_without_modulation(rows, hidden):
+    x = G.normal_bf16(22, (rows, hidden), 2.0, 0.3)
+    want = O.adaln_modulate(_dec(x), np.zeros(hidden), np.zeros(hidden), 1e-6)
+    out = torch.empty((rows, hidden), dtype=torch.bfloat16, device="cuda")
+    D.dit_adaln_modulate(dev_f32_from_bf16(x), rows, hidden, rows, None, None, 0, 1e-6, out)
+    torch.cuda.synchronize()
+    assert_bf16_ulp(host(out), want, f"layernorm {rows}x{hidden}")
