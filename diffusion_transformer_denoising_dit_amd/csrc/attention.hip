@@ -153,6 +153,7 @@ struct WaveState {
   float m_run;        // running max of the scaled scores (log2 domain)
   float alpha;        // rescale of O still owed for the last raise of m_run
   float l_run;        // this lane's partial sum of p
+  bool rescale;       // wave-uniform: the last softmax phase raised m_run (O owes alpha)
   int k_off[kKS];     // K fragment byte offsets within a stage (row lane%32)
   int v_off[2][kDB];  // V^T transposing-read byte offsets (rows 8g + 4*hi + s16/4)
 };
@@ -198,21 +199,19 @@ __device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, con
 #pragma unroll
     for (int i = 0; i < kQK; ++i) {
       if (i + kAhead < kQK) kf[i + kAhead] = kread(i + kAhead);
-      // the O rescale owed by the last softmax phase rides along (VALU)
-      if constexpr (kPVPart) {
-        if (i < W::kDB * 4) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) st.o[i / 4][4 * (i % 4) + e] *= st.alpha;
-        }
-      }
       __builtin_amdgcn_sched_barrier(0);
       st.s[i % 2] = mfma32x32x16(kf[i], st.qf[i / 2], st.s[i % 2]);
     }
-  } else if constexpr (kPVPart) {
+  }
+  if constexpr (kPVPart) {
+    // the O rescale owed by the last softmax phase, skipped (wave-uniform
+    // branch) when no running max of the wave moved
+    if (st.rescale) {
 #pragma unroll
-    for (int i = 0; i < W::kDB; ++i)
+      for (int i = 0; i < W::kDB; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) st.o[i][e] *= st.alpha;
+        for (int e = 0; e < 16; ++e) st.o[i][e] *= st.alpha;
+    }
   }
   if constexpr (kPVPart) {
     auto vread = [&](int i) {
@@ -235,9 +234,9 @@ __device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, con
 }
 
 // Softmax phase for key tile j (keys j0 .. j0+63): mask past the bound (only
-// the tile that holds it), tile max, online update of the running max with
-// the rescale of O and l, p = exp2(s*c - m) into the running sum and, rounded
-// to bf16, into pf.  VALU only.
+// the tile that holds it), tile max, update of the running max with the
+// rescale of l (O's is owed to the next MFMA phase), p = exp2(s*c - m) into
+// the running sum and, rounded to bf16, into pf.  VALU only.
 template <int D>
 __device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_valid, int hi, float c) {
   using W = WaveState<D>;
@@ -259,11 +258,18 @@ __device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_va
     m[c4] = fmaxf(x, st.s[t][r0 + 7]);
   }
   const float m0 = fmaxf(m[0], m[1]), m1 = fmaxf(m[2], m[3]);
-  // running max; l is rescaled here, O in the next MFMA phase (alpha)
-  const float m_new = fmaxf(st.m_run, max_halves(fmaxf(m0, m1)) * c);  // c > 0 keeps the order
-  st.alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
-  st.m_run = m_new;
-  st.l_run *= st.alpha;
+  // Running max.  When no query of the wave sees a score above its running
+  // max, alpha would be exactly 1: the rescale of l here and of O in the next
+  // MFMA phase are skipped, wave-uniformly (after the first tiles most tiles
+  // raise no max), and the result is bitwise the same as rescaling by 1.
+  const float m_tile = max_halves(fmaxf(m0, m1)) * c;  // c > 0 keeps the order
+  st.rescale = __builtin_amdgcn_ballot_w64(m_tile > st.m_run) != 0;
+  if (st.rescale) {
+    const float m_new = fmaxf(st.m_run, m_tile);
+    st.alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+    st.m_run = m_new;
+    st.l_run *= st.alpha;
+  }
   const float nm = -st.m_run;
   float l0 = 0.f, l1 = 0.f;
 #pragma unroll
@@ -416,6 +422,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   st.m_run = -INFINITY;
   st.l_run = 0.f;
   st.alpha = 1.f;
+  st.rescale = false;
   // LDS read offsets.  A K fragment row is lane%32 (+32t) and a V^T read row
   // is 16u + 8g + 4*hi + s16/4; the swizzle depends only on row % 16, so t
   // and u only add immediate row offsets.
