@@ -13,7 +13,8 @@ attention's TFLOP/s against the bf16 dense MFMA peak (the roofline object),
 split joint attention (a text partial plus 4 visual partials, merged), step
 caching (probe, skipped step, change-score kernel, a 30-step cadence-2 loop),
 the MM-DiT double- and single-stream blocks at the FLUX-like image shape,
-plus the CPU oracle timed on a bounded sample of the same step.
+the Wan-style block (self- plus cross-attention) at the c3 video shape, plus
+the CPU oracle timed on a bounded sample of the same step.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -39,9 +40,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
 # WRITE x1.0); summary and commands in profiles/attn_c3_hbm_traffic.md.  Valid
 # only for the kernel source they were taken on.
 ATTN_TRAFFIC = {
-    "source_sha256": "5829bfd7cd02ceadc24e0f0d2f0a45b332671cd728d375c1492812143896b0ba",
-    "fetch_bytes": 3.7187e9,
-    "write_bytes": 0.3434e9,
+    "source_sha256": "ded7d05554ae6e5b04f14aea4dc713991dbd007a422dd1b99552277dc27c6677",
+    "fetch_bytes": 3.7193e9,
+    "write_bytes": 0.3408e9,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     "profile": "profiles/attn_c3_hbm_traffic.md",
@@ -250,6 +251,53 @@ def mmdit_blocks(reps, stream):
     return out
 
 
+def wan_block(reps, stream):
+    """The Wan-style block (self-attention over the video tokens, text
+    cross-attention, MLP) at the c3 video shape: 32760 video tokens, 512
+    context slots of which 226 valid, hidden 5120, 40 heads x 128, MLP 13824,
+    batch 1.  Seeded device draws (activations N(0,1), weights N(0, 0.02))."""
+    import torch
+
+    import diffusion_transformer_denoising_dit_amd as D
+    from synthetic import configs as C
+    s = C.C3
+    B, S, L, Dh, F = s.batch, s.n_vis, s.n_txt, s.hidden, s.mlp
+    valid = [226]
+    g = torch.Generator("cuda").manual_seed(12)
+
+    def rnd(*shape, std=1.0, mean=0.0):
+        return (torch.randn(shape, generator=g, device="cuda") * std + mean).to(torch.bfloat16)
+
+    shapes = {"w_qkv": (3 * Dh, Dh), "b_qkv": (3 * Dh,), "w_o": (Dh, Dh), "b_o": (Dh,),
+              "w_cq": (Dh, Dh), "b_cq": (Dh,), "w_ckv": (2 * Dh, Dh), "b_ckv": (2 * Dh,),
+              "w_co": (Dh, Dh), "b_co": (Dh,), "w_up": (F, Dh), "b_up": (F,), "w_dn": (Dh, F),
+              "b_dn": (Dh,)}
+    w = {k: rnd(*v, std=0.02) for k, v in shapes.items()}
+    for k in ("g_q", "g_k", "g_cq", "g_ck"):
+        w[k] = rnd(Dh, std=0.02, mean=1.0)
+    ww = D.wan_block_weights(w)
+    desc = D.block_desc(s, valid, 6 * Dh)
+    mod = rnd(B, 6, Dh)
+    x = torch.randn((B, S, Dh), generator=g, device="cuda")
+    ctx = rnd(B, L, Dh)
+    nb = D.dit_wan_block_workspace_bytes(desc)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def run():
+        D.dit_wan_block_forward(desc, ww, mod, x, ctx, ws, nb)
+
+    run()
+    ms = timed(run, reps, stream)
+    M = B * S
+    fl = (2.0 * M * Dh * 4 * Dh + attention_flops(S, S, s.heads, s.head_dim, B)
+          + 2.0 * M * Dh * 2 * Dh + 2.0 * B * L * Dh * 2 * Dh
+          + sum(attention_flops(S, v, s.heads, s.head_dim) for v in valid) + 2.0 * M * Dh * F * 2)
+    return {"ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+            "algorithmic_tflop": round(fl / 1e12, 3),
+            "shape": "Wan 480p: 32760 video tokens, 512 context slots (226 valid), hidden 5120, "
+                     "40x128, MLP 13824, batch 1"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -424,6 +472,7 @@ def main():
     del p_out, p_lse, o_split
 
     mm = mmdit_blocks(max(5, args.steps), stream)
+    wan = wan_block(max(3, args.steps // 2), stream)
     traffic = attn_traffic()
     result = {
         "metric": METRIC,
@@ -472,6 +521,7 @@ def main():
             "steps": shape.steps,
         },
         "mmdit": mm,
+        "wan_block": wan,
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_kernel<128, false> (joint attention)",
