@@ -13,11 +13,12 @@
 // = 4 x 2 MFMA 32x32 tiles with the accumulators in AGPRs.  A 256 x 256 tile
 // moves 64 bytes of operands from L2 per 2 x 256 x 256 flops, half of what a
 // 128 x 256 tile needs, which keeps L2 below its bandwidth at full MFMA
-// rate.  K slices of 32 stream from HBM/L2 straight into LDS with
-// global_load_lds_dwordx4 through a 4-stage ring (three slices ahead, one
-// barrier per slice); rows are stored unpadded with their 16-byte chunks
-// XOR-swizzled by row so the operand reads of a wave hit distinct bank
-// groups.  Workgroups are ordered XCD by XCD (the dispatcher deals workgroup
+// rate.  K slices of 64 stream from HBM/L2 straight into LDS with
+// global_load_lds_dwordx4 into two 64 KB stages (one slice ahead, one barrier
+// per slice); each operand row of a slice is one full 128-byte line, stored
+// unpadded with its 16-byte chunks XOR-swizzled by row so the operand reads
+// of a wave hit distinct bank groups.  (Slices of 32 through a 4-stage ring
+// measured 5% slower: twice the barriers and half-line requests.)  Workgroups are ordered XCD by XCD (the dispatcher deals workgroup
 // ids round-robin over the 8 XCDs, each with its own L2) and, inside an XCD,
 // in groups of 8 token tiles that sweep all feature tiles, so the
 // workgroups running together on one XCD share operand slices in its L2.
@@ -207,30 +208,27 @@ namespace big {
 
 constexpr int kTM = 256;                          // token rows per workgroup
 constexpr int kTN = 256;                          // output features per workgroup
-constexpr int kBK = 32;                           // k per ring stage
-constexpr int kStages = 4;
+constexpr int kBK = 64;                           // k per stage
+constexpr int kStages = 2;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowBytes = 2 * kBK;                // 64
-constexpr int kChunks = kRowBytes / 16;           // 4 chunks of 16 bytes per row
-constexpr int kRowsPerLoad = 1024 / kRowBytes;    // rows per wave-wide 16 B/lane load
-constexpr int kLoadsA = kTM / kRowsPerLoad / kWaves;
-constexpr int kLoadsW = kTN / kRowsPerLoad / kWaves;
+constexpr int kRowBytes = 2 * kBK;                // 128
+constexpr int kChunks = kRowBytes / 16;           // 8 chunks of 16 bytes per row
+constexpr int kRowsPerLoad = 1024 / kRowBytes;    // 8 rows per wave-wide 16 B/lane load
+constexpr int kLoadsA = kTM / kRowsPerLoad / kWaves;  // 4
+constexpr int kLoadsW = kTN / kRowsPerLoad / kWaves;  // 4
 constexpr int kTileA = kTM * kRowBytes;
 constexpr int kTileW = kTN * kRowBytes;
-constexpr int kStageBytes = kTileA + kTileW;
+constexpr int kStageBytes = kTileA + kTileW;      // 64 KB
 constexpr int kGroupM = 8;
 
-// 16-byte chunk c of a 64-byte row r sits at chunk position c ^ swz(r).  LDS
-// serves 16 bank groups of 16 bytes per clock and a 16-byte operand read
-// serves 16 lanes (16 consecutive rows, one chunk) per clock; rows r, r+4,
-// r+8, r+12 start in the same bank group, and swz separates them.
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// 16-byte chunk c of a 128-byte row r sits at chunk position c ^ swz(r).  LDS
+// serves 16 bank groups of 16 bytes per clock; rows r and r+2 start in the
+// same bank group, and swz separates the 16 rows one operand read touches.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
+// Waits until every global load and LDS access of this wave has completed.
+__device__ __forceinline__ void wait_vm_lgkm0() { __builtin_amdgcn_s_waitcnt(7 << 4); }
 
 // Wave-wide 16-byte-per-lane load into LDS: lane i's 16 bytes at src land at
 // LDS byte lds_addr + 16*i (lds_addr wave-uniform).  Issued from inline
@@ -309,23 +307,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
 #pragma unroll
     for (int n = 0; n < kLoadsW; ++n) lds_dma16(w_src[n] + ko, st + kTileA + (wave * kLoadsW + n) * 1024);
   };
-  constexpr int L = kLoadsA + kLoadsW;  // loads per wave per k slice
 
   const int k_tiles = p.k / kBK;
-#pragma unroll
-  for (int kt = 0; kt < kStages - 1; ++kt)
-    if (kt < k_tiles) issue(kt);
+  issue(0);
 
   // wave tile: 128 token rows (wm) x 64 features (wn)
   const int wm = wave / 4, wn = wave % 4;
+  constexpr int kSteps = kBK / 16;
   // operand read offsets within a stage: row = base row + lane%32 (+32 per
-  // MFMA tile, an immediate); the swizzle depends on the row's bits 2..3,
+  // MFMA tile, an immediate); the swizzle depends on the row's bits 1..3,
   // which the tile offsets do not change
-  int a_off[kBK / 16], w_off[kBK / 16];
+  int a_off[kSteps], w_off[kSteps];
   {
     const int r = lane % 32;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
+    for (int ks = 0; ks < kSteps; ++ks) {
       a_off[ks] = (wm * 128 + r) * kRowBytes + (((2 * ks + hi) ^ swz(r)) * 16);
       w_off[ks] = kTileA + (wn * 64 + r) * kRowBytes + (((2 * ks + hi) ^ swz(r)) * 16);
     }
@@ -339,13 +335,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // Software pipeline over k steps of 16: the fragments of the next step are
-  // read from LDS while the MFMAs of the current one run.  The barrier that
-  // publishes slice kt+1 sits in the middle of slice kt (after its first k
-  // step), so the first reads of slice kt+1 overlap the last MFMAs of slice
-  // kt; at that barrier every wave is also done with slice kt-1, whose ring
-  // slot then receives slice kt+3.
-  constexpr int kSteps = kBK / 16;
   auto read_frags = [&](int kt, int ks, bf16x8 (&wf)[2], bf16x8 (&af)[4]) {
     const char* st = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
@@ -359,30 +348,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(wf[i], af[j], acc[i][j]);
   };
-  // Slice `need` has landed once at most the loads of the slices issued after
-  // it are in flight; `issued` is the last slice issued so far.
-  auto wait_slice = [&](int need, int issued) {
-    const int later = min(issued, k_tiles - 1) - need;
-    if (later >= 2)
-      wait_vmcnt<2 * L>();
-    else if (later == 1)
-      wait_vmcnt<L>();
-    else
-      wait_vmcnt<0>();
-  };
 
-  static_assert(kSteps == 2, "the pipeline below is written for two k steps per slice");
+  // Software pipeline over the four k steps of 16 in a slice: the fragments
+  // of the next step are read from LDS while the MFMAs of the current one
+  // run.  The barrier before the last step publishes slice kt+1 (landed, as
+  // the wait before it checks for this wave) and retires slice kt (this
+  // wave's reads of it have completed), whose stage then receives slice kt+2.
+  static_assert(kSteps == 4, "the pipeline below is written for four k steps per slice");
   bf16x8 wf0[2], af0[4], wf1[2], af1[4];
-  wait_slice(0, kStages - 2);  // slices 0 .. kStages-2 were issued above
+  wait_vm_lgkm0();
   __builtin_amdgcn_s_barrier();
+  if (1 < k_tiles) issue(1);
   read_frags(0, 0, wf0, af0);
   for (int kt = 0; kt < k_tiles; ++kt) {
     read_frags(kt, 1, wf1, af1);
     mfmas(wf0, af0);
+    read_frags(kt, 2, wf0, af0);
+    mfmas(wf1, af1);
+    read_frags(kt, 3, wf1, af1);
+    mfmas(wf0, af0);
     if (kt + 1 < k_tiles) {
-      wait_slice(kt + 1, kt + kStages - 2);  // slice kt+3 is issued only after this barrier
+      // slice kt+1 has landed and this wave's reads of slice kt are done;
+      // after the barrier slice kt's stage receives slice kt+2
+      wait_vm_lgkm0();
       __builtin_amdgcn_s_barrier();
-      if (kt + kStages - 1 < k_tiles) issue(kt + kStages - 1);
+      if (kt + 2 < k_tiles) issue(kt + 2);
       read_frags(kt + 1, 0, wf0, af0);
     }
     mfmas(wf1, af1);
@@ -414,6 +404,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
 
 hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s) {
   if (p.m == 0) return hipSuccess;
+  if (p.k <= 0 || p.k % 64 != 0) return hipErrorInvalidValue;  // both kernels step K by 64
   if (p.m >= 4 * big::kTM && p.n >= big::kTN) {
     const int tiles_m = static_cast<int>((p.m + big::kTM - 1) / big::kTM);
     const int tiles_n = (p.n + big::kTN - 1) / big::kTN;
