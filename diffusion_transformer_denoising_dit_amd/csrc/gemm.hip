@@ -10,15 +10,16 @@
 //
 // Large GEMMs (the block's projections and MLP): a workgroup of 8 waves (two
 // per SIMD) computes a 256 (tokens) x 256 (features) tile, each wave 128 x 64
-// = 4 x 2 MFMA 32x32 tiles with the accumulators in AGPRs.  A 256 x 256 tile
+// = 4 x 2 MFMA 32x32 tiles with the accumulators in registers.  A 256 x 256 tile
 // moves 64 bytes of operands from L2 per 2 x 256 x 256 flops, half of what a
 // 128 x 256 tile needs, which keeps L2 below its bandwidth at full MFMA
 // rate.  K slices of 64 stream from HBM/L2 straight into LDS with
-// global_load_lds_dwordx4 into two 64 KB stages (one slice ahead, one barrier
-// per slice); each operand row of a slice is one full 128-byte line, stored
-// unpadded with its 16-byte chunks XOR-swizzled by row so the operand reads
-// of a wave hit distinct bank groups.  (Slices of 32 through a 4-stage ring
-// measured 5% slower: twice the barriers and half-line requests.)  Workgroups are ordered XCD by XCD (the dispatcher deals workgroup
+// global_load_lds_dwordx4 into two 64 KB stages; each operand row of a slice
+// is one full 128-byte line, stored unpadded with its 16-byte chunks
+// XOR-swizzled by row so the operand reads of a wave hit distinct bank
+// groups.  The two waves of a SIMD take turns: one multiplies a whole slice
+// from registers while the other reads its next fragments from LDS (see the
+// kernel).  Workgroups are ordered XCD by XCD (the dispatcher deals workgroup
 // ids round-robin over the 8 XCDs, each with its own L2) and, inside an XCD,
 // in groups of 8 token tiles that sweep all feature tiles, so the
 // workgroups running together on one XCD share operand slices in its L2.
@@ -215,8 +216,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowBytes = 2 * kBK;                // 128
 constexpr int kChunks = kRowBytes / 16;           // 8 chunks of 16 bytes per row
 constexpr int kRowsPerLoad = 1024 / kRowBytes;    // 8 rows per wave-wide 16 B/lane load
-constexpr int kLoadsA = kTM / kRowsPerLoad / kWaves;  // 4
-constexpr int kLoadsW = kTN / kRowsPerLoad / kWaves;  // 4
+constexpr int kLoaders = 4;                       // waves 0-3 issue every load
+constexpr int kLoadsA = kTM / kRowsPerLoad / kLoaders;  // 8
+constexpr int kLoadsW = kTN / kRowsPerLoad / kLoaders;  // 8
+constexpr int kLoads = kLoadsA + kLoadsW;         // loads per loader wave per slice
 constexpr int kTileA = kTM * kRowBytes;
 constexpr int kTileW = kTN * kRowBytes;
 constexpr int kStageBytes = kTileA + kTileW;      // 64 KB
@@ -227,28 +230,54 @@ constexpr int kGroupM = 8;
 // same bank group, and swz separates the 16 rows one operand read touches.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-// Waits until every global load and LDS access of this wave has completed.
-__device__ __forceinline__ void wait_vm_lgkm0() { __builtin_amdgcn_s_waitcnt(7 << 4); }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Waits until every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
 
-// Wave-wide 16-byte-per-lane load into LDS: lane i's 16 bytes at src land at
-// LDS byte lds_addr + 16*i (lds_addr wave-uniform).  Issued from inline
-// assembly so the compiler does not guard LDS reads with waits on it; M0 is
-// saved and restored.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
+// Workgroup barrier that the compiler may not move memory operations or any
+// other instruction across (the phases below depend on that placement).
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// Wave-wide 16-byte-per-lane load into LDS: lane i's 16 bytes at base + voff
+// (voff a 32-bit per-lane byte offset, base wave-uniform) land at LDS byte
+// lds_addr + 16*i (lds_addr wave-uniform).  Issued from inline assembly so
+// the compiler does not guard LDS reads with waits on it; M0 is saved and
+// restored.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(lds_addr)
+      : "v"(voff), "s"(base), "s"(lds_addr)
       : "memory");
 }
 
 typedef __attribute__((address_space(3))) char* lds_char_ptr;
 
+// The 8 waves form two groups, one wave of each per SIMD: the loaders (waves
+// 0-3, token rows 0-127 of the tile) and the others (token rows 128-255), each
+// wave 128 tokens x 64 features.  A wave alternates a memory phase (read the
+// 16 A and 8 W operand fragments of one 64-k slice from LDS into registers;
+// loaders also issue the loads of the next slice) and an MFMA phase (the 32
+// MFMAs of that slice), the second group one phase behind the first, with a
+// workgroup barrier at every phase boundary.  On each SIMD one wave then
+// multiplies while the other moves data: a phase's 32 MFMAs issue back to
+// back from registers.  Slice s is read by the loaders in phase 2s and by the
+// others in phase 2s+1; its stage receives slice s+2 when the loaders start
+// phase 2s+2.
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
@@ -257,6 +286,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int hi = lane / 32;
+  const int grp = wave / 4, wq = wave % 4;
+  const bool loader = grp == 0;
 
   // tile of this workgroup: XCD-contiguous ids, then groups of kGroupM token tiles
   int tm, tn;
@@ -277,51 +308,54 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
   const int64_t m0 = static_cast<int64_t>(tm) * kTM;
   const int n0 = tn * kTN;
 
-  // Loads: wave w fills rows [(w*kLoads + n) * kRowsPerLoad, +kRowsPerLoad) of
-  // the A and W tiles; lane i lands at row i / kChunks, chunk position
-  // i % kChunks and fetches the chunk that swizzles there.  Rows past m or n
-  // are clamped (computed, never stored).
-  const char* a_src[kLoadsA];
-  const char* w_src[kLoadsW];
+  // Loads (loader waves): wave w fills rows [(w*kLoads + n) * kRowsPerLoad,
+  // +kRowsPerLoad) of the A and W tiles; lane i lands at row i / kChunks,
+  // chunk position i % kChunks and fetches the chunk that swizzles there.
+  // Rows past m or n are clamped (computed, never stored).  Byte offsets from
+  // p.a and p.w fit 32 bits (checked by the launcher).
+  uint32_t a_vo[kLoadsA], w_vo[kLoadsW];
 #pragma unroll
   for (int n = 0; n < kLoadsA; ++n) {
-    const int rr = (wave * kLoadsA + n) * kRowsPerLoad + lane / kChunks;
+    const int rr = (wq * kLoadsA + n) * kRowsPerLoad + lane / kChunks;
     const int c = (lane % kChunks) ^ swz(rr);
     int64_t m = m0 + rr;
     if (m > p.m - 1) m = p.m - 1;
-    a_src[n] = reinterpret_cast<const char*>(p.a + a_row_offset(p, m)) + c * 16;
+    a_vo[n] = static_cast<uint32_t>(a_row_offset(p, m) * 2 + c * 16);
   }
 #pragma unroll
   for (int n = 0; n < kLoadsW; ++n) {
-    const int rr = (wave * kLoadsW + n) * kRowsPerLoad + lane / kChunks;
+    const int rr = (wq * kLoadsW + n) * kRowsPerLoad + lane / kChunks;
     const int c = (lane % kChunks) ^ swz(rr);
     const int nr = min(n0 + rr, p.n - 1);
-    w_src[n] = reinterpret_cast<const char*>(p.w + static_cast<int64_t>(nr) * p.k) + c * 16;
+    w_vo[n] = static_cast<uint32_t>(static_cast<int64_t>(nr) * p.k * 2 + c * 16);
   }
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_ptr)smem));
   auto issue = [&](int kt) {
     const uint32_t st = lds_base + (kt % kStages) * kStageBytes;
-    const int64_t ko = static_cast<int64_t>(kt) * kRowBytes;
+    const char* ba = reinterpret_cast<const char*>(p.a) + static_cast<int64_t>(kt) * kRowBytes;
+    const char* bw = reinterpret_cast<const char*>(p.w) + static_cast<int64_t>(kt) * kRowBytes;
 #pragma unroll
-    for (int n = 0; n < kLoadsA; ++n) lds_dma16(a_src[n] + ko, st + (wave * kLoadsA + n) * 1024);
+    for (int n = 0; n < kLoadsA; ++n) lds_dma16(ba, a_vo[n], st + (wq * kLoadsA + n) * 1024);
 #pragma unroll
-    for (int n = 0; n < kLoadsW; ++n) lds_dma16(w_src[n] + ko, st + kTileA + (wave * kLoadsW + n) * 1024);
+    for (int n = 0; n < kLoadsW; ++n) lds_dma16(bw, w_vo[n], st + kTileA + (wq * kLoadsW + n) * 1024);
   };
 
   const int k_tiles = p.k / kBK;
-  issue(0);
+  if (loader) {
+    issue(0);
+    if (k_tiles > 1) issue(1);
+  }
 
-  // wave tile: 128 token rows (wm) x 64 features (wn)
-  const int wm = wave / 4, wn = wave % 4;
-  constexpr int kSteps = kBK / 16;
-  // operand read offsets within a stage: row = base row + lane%32 (+32 per
-  // MFMA tile, an immediate); the swizzle depends on the row's bits 1..3,
-  // which the tile offsets do not change
-  int a_off[kSteps], w_off[kSteps];
+  // wave tile: 128 token rows (grp) x 64 features (wq).  Operand read offsets
+  // within a stage: row = base row + lane%32 (+32 per MFMA tile, an
+  // immediate); the swizzle depends on the row's bits 1..3, which the tile
+  // offsets do not change.
+  const int wm = grp, wn = wq;
+  int a_off[4], w_off[4];
   {
     const int r = lane % 32;
 #pragma unroll
-    for (int ks = 0; ks < kSteps; ++ks) {
+    for (int ks = 0; ks < 4; ++ks) {
       a_off[ks] = (wm * 128 + r) * kRowBytes + (((2 * ks + hi) ^ swz(r)) * 16);
       w_off[ks] = kTileA + (wn * 64 + r) * kRowBytes + (((2 * ks + hi) ^ swz(r)) * 16);
     }
@@ -335,48 +369,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  auto read_frags = [&](int kt, int ks, bf16x8 (&wf)[2], bf16x8 (&af)[4]) {
-    const char* st = smem + (kt % kStages) * kStageBytes;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) wf[i] = *reinterpret_cast<const bf16x8*>(st + w_off[ks] + i * 32 * kRowBytes);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) af[j] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + j * 32 * kRowBytes);
-  };
-  auto mfmas = [&](const bf16x8 (&wf)[2], const bf16x8 (&af)[4]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(wf[i], af[j], acc[i][j]);
-  };
-
-  // Software pipeline over the four k steps of 16 in a slice: the fragments
-  // of the next step are read from LDS while the MFMAs of the current one
-  // run.  The barrier before the last step publishes slice kt+1 (landed, as
-  // the wait before it checks for this wave) and retires slice kt (this
-  // wave's reads of it have completed), whose stage then receives slice kt+2.
-  static_assert(kSteps == 4, "the pipeline below is written for four k steps per slice");
-  bf16x8 wf0[2], af0[4], wf1[2], af1[4];
-  wait_vm_lgkm0();
-  __builtin_amdgcn_s_barrier();
-  if (1 < k_tiles) issue(1);
-  read_frags(0, 0, wf0, af0);
-  for (int kt = 0; kt < k_tiles; ++kt) {
-    read_frags(kt, 1, wf1, af1);
-    mfmas(wf0, af0);
-    read_frags(kt, 2, wf0, af0);
-    mfmas(wf1, af1);
-    read_frags(kt, 3, wf1, af1);
-    mfmas(wf0, af0);
-    if (kt + 1 < k_tiles) {
-      // slice kt+1 has landed and this wave's reads of slice kt are done;
-      // after the barrier slice kt's stage receives slice kt+2
-      wait_vm_lgkm0();
-      __builtin_amdgcn_s_barrier();
-      if (kt + 2 < k_tiles) issue(kt + 2);
-      read_frags(kt + 1, 0, wf0, af0);
+  // The second group takes one extra barrier first (and the loaders one at
+  // the end), which puts it exactly one phase behind.  Before the barrier
+  // that opens phase 2s, each loader waits for its own loads of slice s
+  // (slices up to s are in flight then, up to s+1 at s = 0).
+  if (!loader) phase_barrier();
+  for (int s = 0; s < k_tiles; ++s) {
+    if (loader) {
+      if (s == 0 && k_tiles > 1)
+        wait_vmcnt<kLoads>();
+      else
+        wait_vmcnt<0>();
     }
-    mfmas(wf1, af1);
+    phase_barrier();
+    if (loader && s >= 1 && s + 1 < k_tiles) issue(s + 1);
+    bf16x8 wf[4][2], af[4][4];
+    {
+      const char* st = smem + (s % kStages) * kStageBytes;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          wf[ks][i] = *reinterpret_cast<const bf16x8*>(st + w_off[ks] + i * 32 * kRowBytes);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          af[ks][j] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + j * 32 * kRowBytes);
+      }
+    }
+    wait_lgkm0();  // this wave's reads of slice s are done before its stage is reused
+    phase_barrier();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(wf[ks][i], af[ks][j], acc[i][j]);
   }
+  if (loader) phase_barrier();
 
   // acc[i][j][4*g + e] is C[m, n] with
   //   m = m0 + wm*128 + j*32 + lane%32,  n = n0 + wn*64 + i*32 + 8*g + 4*(lane/32) + e.
@@ -405,7 +434,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
 hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s) {
   if (p.m == 0) return hipSuccess;
   if (p.k <= 0 || p.k % 64 != 0) return hipErrorInvalidValue;  // both kernels step K by 64
-  if (p.m >= 4 * big::kTM && p.n >= big::kTN) {
+  // The large kernel addresses operand bytes by 32-bit offsets from p.a and p.w.
+  const int64_t a_extent = 2 * (p.group_rows > 0 ? ((p.m - 1) / p.group_rows) * p.a_group_stride +
+                                                        ((p.m - 1) % p.group_rows) * p.lda
+                                                  : (p.m - 1) * p.lda) + 2 * static_cast<int64_t>(p.k);
+  const int64_t w_extent = 2 * static_cast<int64_t>(p.n) * p.k;
+  const bool offsets_fit = a_extent <= (int64_t{1} << 32) && w_extent <= (int64_t{1} << 32);
+  if (p.m >= 4 * big::kTM && p.n >= big::kTN && offsets_fit) {
     const int tiles_m = static_cast<int>((p.m + big::kTM - 1) / big::kTM);
     const int tiles_n = (p.n + big::kTN - 1) / big::kTN;
     dim3 grid(tiles_m * tiles_n);
