@@ -13,10 +13,11 @@ attention's TFLOP/s against the bf16 dense MFMA peak (the roofline object),
 split joint attention (a text partial plus 4 visual partials, merged), step
 caching (probe, skipped step, change-score kernel, a 30-step cadence-2 loop),
 the MM-DiT double- and single-stream blocks at the FLUX-like image shape,
-the Wan-style block (self- plus cross-attention) at the c3 video shape, plus
-the CPU oracle timed on a bounded sample of the same step.
+the Wan-style block (self- plus cross-attention) at the c3 video shape, the
+block's four GEMMs alone (beside torch's hipBLASLt matmul of the same shapes,
+for reference), plus the CPU oracle timed on a bounded sample of the same step.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--gemm-only]
 """
 
 from __future__ import annotations
@@ -74,6 +75,8 @@ def parse():
     p.add_argument("--traffic-probe", action="store_true",
                    help="only launch c3 joint attention --steps times and a plain 1 GiB copy "
                         "--steps times (for hardware-counter runs), print nothing else")
+    p.add_argument("--gemm-only", action="store_true",
+                   help="time only the block's GEMMs (ours and hipBLASLt) and print them")
     p.add_argument("--cpu-rows", type=int, default=64,
                    help="query rows in the CPU oracle's bounded sample")
     return p.parse_args()
@@ -178,6 +181,50 @@ def traffic_probe(steps):
     torch.cuda.synchronize()
     print(f"[traffic-probe] {steps} attention launches + {steps} copies of 1 GiB done",
           file=sys.stderr, flush=True)
+
+
+def block_gemms(reps, stream):
+    """The DiT block's four large GEMMs at the c3 shape (33,272 tokens, hidden
+    5120, MLP 13824), each through dit_linear with the epilogue the block uses,
+    and beside each the same product as a plain torch matmul (hipBLASLt, no
+    epilogue) for reference.  Seeded N(0,1) activations, N(0, 0.02) weights."""
+    import torch
+
+    import diffusion_transformer_denoising_dit_amd as D
+    from synthetic import configs as C
+    blk = C.C3_STEP.block
+    M, Dh, F = blk.batch * blk.n_tok, blk.hidden, blk.mlp
+    g = torch.Generator("cuda").manual_seed(13)
+    out = {}
+    for name, n, k, epi in (("qkv", 3 * Dh, Dh, D.EPI_BF16), ("out_proj", Dh, Dh, D.EPI_GATED_RES_F32),
+                            ("mlp_up", F, Dh, D.EPI_GELU_BF16), ("mlp_down", Dh, F, D.EPI_GATED_RES_F32)):
+        a = torch.randn((M, k), generator=g, device="cuda").to(torch.bfloat16)
+        w = (torch.randn((n, k), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        bias = (torch.randn((n,), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        gated = epi == D.EPI_GATED_RES_F32
+        y = torch.zeros((M, n), dtype=torch.float32 if gated else torch.bfloat16, device="cuda")
+        gate = torch.randn((1, n), generator=g, device="cuda").to(torch.bfloat16) if gated else None
+
+        def ours():
+            D.dit_linear(a, k, w, bias, M, n, k, epi, y, n, gate=gate, gate_stride=n, gate_rows=M)
+
+        wt = w.t()
+
+        def ref():
+            torch.matmul(a, wt)
+
+        ours()
+        ref()
+        flop = 2.0 * M * n * k
+        ms_o = timed(ours, reps, stream)
+        ms_r = timed(ref, reps, stream)
+        out[name] = {"m": M, "n": n, "k": k, "ms": round(ms_o, 3),
+                     "tflops": round(flop / (ms_o * 1e-3) / 1e12, 1),
+                     "hipblaslt_ms": round(ms_r, 3),
+                     "hipblaslt_tflops": round(flop / (ms_r * 1e-3) / 1e12, 1)}
+        del a, w, bias, y, gate, wt
+    torch.cuda.empty_cache()
+    return out
 
 
 def mmdit_blocks(reps, stream):
@@ -315,6 +362,10 @@ def main():
     torch.cuda.set_device(0)
     if args.traffic_probe:
         traffic_probe(args.steps)
+        return
+    if args.gemm_only:
+        print(json.dumps({"block_gemms": block_gemms(max(3, args.steps), torch.cuda.current_stream())}),
+              flush=True)
         return
     shape = C.C3_STEP
     blk = shape.block
@@ -471,6 +522,7 @@ def main():
     ms_merge = timed(split_merge, max(5, args.steps), stream)
     del p_out, p_lse, o_split
 
+    gemms = block_gemms(max(3, args.steps // 2), stream)
     mm = mmdit_blocks(max(5, args.steps), stream)
     wan = wan_block(max(3, args.steps // 2), stream)
     traffic = attn_traffic()
@@ -520,6 +572,7 @@ def main():
             "cadence2_full_steps": int(n_full_loop),
             "steps": shape.steps,
         },
+        "block_gemms": gemms,
         "mmdit": mm,
         "wan_block": wan,
         "roofline": {

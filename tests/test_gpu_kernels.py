@@ -229,6 +229,10 @@ ATTN_SHAPES = [
                 txt_valid=("fixed", (0, 13)), seed=42),
     C.AttnShape("attn_tiny", batch=1, n_vis=5, n_txt=3, heads=1, head_dim=128,
                 txt_valid=("fixed", (2,)), seed=43),
+    # eight batch rows, each with its own valid text length (none, all, and between):
+    # exercises the workgroup -> (batch row, head, query tile) decode past batch 2
+    C.AttnShape("attn_b8", batch=8, n_vis=300, n_txt=20, heads=3, head_dim=64,
+                txt_valid=("fixed", (0, 1, 5, 19, 20, 7, 13, 2)), seed=44),
 ]
 
 
