@@ -147,6 +147,27 @@ def test_linear_gated_residual_and_row_groups():
                   max_abs=1e-4 * np.abs(y2).max(), rel_l2=1e-5)
 
 
+def test_linear_operand_past_4gib():
+    """An A operand whose rows span more than 4 GiB (two row groups 4 GiB + 128 bytes apart):
+    the large-tile kernel addresses operands by 32-bit byte offsets, so the launcher must hand
+    this shape (M >= 1024, N >= 256) to the kernel with 64-bit addressing; the result must
+    still match the oracle."""
+    M, N, K, G_rows = 1200, 256, 128, 600
+    stride = (1 << 31) + 64                       # elements between the two groups' first rows
+    a, w, b = _gemm_case(23, M, N, K)
+    y = O.linear(_dec(a), _dec(w), _dec(b))
+    big = torch.empty(stride + G_rows * K, dtype=torch.bfloat16, device="cuda")
+    big[:G_rows * K].copy_(dev_bf16(a[:G_rows]).reshape(-1))
+    big[stride:].copy_(dev_bf16(a[G_rows:]).reshape(-1))
+    out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    D.dit_linear(big, K, dev_bf16(w), dev_bf16(b), M, N, K, D.EPI_F32, out, N,
+                 group_rows=G_rows, a_group_stride=stride, c_group_stride=G_rows * N)
+    torch.cuda.synchronize()
+    del big
+    torch.cuda.empty_cache()
+    assert_parity(host(out), y, "A operand past 4 GiB", max_abs=1e-4 * np.abs(y).max(), rel_l2=1e-5)
+
+
 def test_linear_rejects_bad_k_without_launch():
     a = torch.zeros((4, 96), dtype=torch.bfloat16, device="cuda")
     w = torch.zeros((8, 96), dtype=torch.bfloat16, device="cuda")
