@@ -41,8 +41,8 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
 # WRITE x1.0); summary and commands in profiles/attn_c3_hbm_traffic.md.  Valid
 # only for the kernel source they were taken on.
 ATTN_TRAFFIC = {
-    "source_sha256": "ded7d05554ae6e5b04f14aea4dc713991dbd007a422dd1b99552277dc27c6677",
-    "fetch_bytes": 3.7193e9,
+    "source_sha256": "1efde9864a20691d6003f0268eb1c6b750e6bb7d2bcb88c88da420efccff6407",
+    "fetch_bytes": 3.7194e9,
     "write_bytes": 0.3408e9,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
