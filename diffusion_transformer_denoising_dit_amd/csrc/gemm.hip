@@ -24,10 +24,12 @@
 // in groups of 8 token tiles that sweep all feature tiles, so the
 // workgroups running together on one XCD share operand slices in its L2.
 //
-// Small GEMMs (loop glue: timestep MLP, modulation, input/output projection):
-// a workgroup of 4 waves computes a 128 (features) x 256 (tokens) tile, each
-// wave 64 x 128; K is staged through padded LDS 64 at a time, the next slice
-// fetched into registers while the current one is multiplied.
+// Small GEMMs (input/output projection, the MM-DiT text stream, anything below
+// the large kernel's shape): a workgroup of 4 waves computes a 128 (features)
+// x 256 (tokens) tile, each wave 64 x 128; K is staged through padded LDS 64
+// at a time, the next slice fetched into registers while the current one is
+// multiplied.  Matrix-vector products (at most 8 token rows: the timestep MLP
+// and the modulation projections) stream W once without tiles.
 #include "common.h"
 #include "kernels.h"
 
@@ -429,11 +431,106 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
 
 }  // namespace big
 
+// ---------------------------------------------------------------------------
+// Matrix-vector products (M <= 8 token rows: the conditioning MLP and the
+// modulation projections of the loop glue).  They read W once and little
+// else, so they are HBM-bound: each wave owns 4 output features (one
+// epilogue group), its lanes stream 16-byte chunks of those 4 W rows along K
+// (a wave-wide step covers 512 k, coalesced), multiply them with the same
+// chunks of the M A rows (L2-resident) into fp32 sums, and reduce the sums
+// across the wave at the end (fixed order: deterministic).
+namespace gemv {
+
+constexpr int kRows = 4;           // output features per wave
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxM = 8;
+constexpr int kStep = 64 * 8;      // k per wave-wide step (8 bf16 per lane)
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+template <int EPI, int M>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemmParams p) {
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int n0 = (blockIdx.x * kWaves + wave) * kRows;
+  if (n0 >= p.n) return;  // n is a multiple of 8, so a wave's 4 rows are all valid or all not
+  const uint16_t* wrow[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) wrow[r] = p.w + static_cast<int64_t>(n0 + r) * p.k;
+  const uint16_t* arow[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) arow[m] = p.a + a_row_offset(p, m);
+  float acc[M][kRows];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) acc[m][r] = 0.f;
+#pragma unroll 2
+  for (int k = lane * 8; k < p.k; k += kStep) {  // k is a multiple of 8: chunks are whole
+    u32x4 wv[kRows], av[M];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) wv[r] = *reinterpret_cast<const u32x4*>(wrow[r] + k);
+#pragma unroll
+    for (int m = 0; m < M; ++m) av[m] = *reinterpret_cast<const u32x4*>(arow[m] + k);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float a0 = bf_lo(av[m][j]), a1 = bf_hi(av[m][j]);
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+          acc[m][r] = fmaf(a0, bf_lo(wv[r][j]), acc[m][r]);
+          acc[m][r] = fmaf(a1, bf_hi(wv[r][j]), acc[m][r]);
+        }
+      }
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) acc[m][r] = wave_sum(acc[m][r]);
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    if (lane == m) store_epilogue<EPI>(p, m, n0, acc[m]);
+}
+
+template <int EPI>
+hipError_t launch(const GemmParams& p, hipStream_t s) {
+  const dim3 grid((p.n / kRows + kWaves - 1) / kWaves), block(kThreads);
+  switch (p.m) {
+    case 1: hipLaunchKernelGGL((gemv_kernel<EPI, 1>), grid, block, 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gemv_kernel<EPI, 2>), grid, block, 0, s, p); break;
+    case 3: hipLaunchKernelGGL((gemv_kernel<EPI, 3>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((gemv_kernel<EPI, 4>), grid, block, 0, s, p); break;
+    case 5: hipLaunchKernelGGL((gemv_kernel<EPI, 5>), grid, block, 0, s, p); break;
+    case 6: hipLaunchKernelGGL((gemv_kernel<EPI, 6>), grid, block, 0, s, p); break;
+    case 7: hipLaunchKernelGGL((gemv_kernel<EPI, 7>), grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((gemv_kernel<EPI, 8>), grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gemv
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s) {
   if (p.m == 0) return hipSuccess;
-  if (p.k <= 0 || p.k % 64 != 0) return hipErrorInvalidValue;  // both kernels step K by 64
+  if (p.k <= 0 || p.k % 64 != 0) return hipErrorInvalidValue;  // the tiled kernels step K by 64
+  if (p.m <= gemv::kMaxM) {
+    if (p.n % 8 != 0) return hipErrorInvalidValue;
+    switch (epilogue) {
+      case EPI_BF16: return gemv::launch<EPI_BF16>(p, s);
+      case EPI_GELU: return gemv::launch<EPI_GELU>(p, s);
+      case EPI_SILU: return gemv::launch<EPI_SILU>(p, s);
+      case EPI_F32: return gemv::launch<EPI_F32>(p, s);
+      case EPI_GATED: return gemv::launch<EPI_GATED>(p, s);
+      case EPI_RES: return gemv::launch<EPI_RES>(p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   // The large kernel addresses operand bytes by 32-bit offsets from p.a and p.w.
   const int64_t a_extent = 2 * (p.group_rows > 0 ? ((p.m - 1) / p.group_rows) * p.a_group_stride +
                                                         ((p.m - 1) % p.group_rows) * p.lda

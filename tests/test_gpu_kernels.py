@@ -105,6 +105,68 @@ def test_linear_large_tiles(M, N, K, epi):
     assert torch.equal(outs[0], outs[1]), "large-tile GEMM rerun differs"
 
 
+# M <= 8 token rows (the conditioning MLP and modulation projections) run the
+# matrix-vector kernel: every epilogue, row counts 1..8, K below and above one
+# 512-wide wave step, grouped rows, bitwise-equal reruns.
+@pytest.mark.parametrize("M,N,K", [(1, 8, 64), (2, 264, 320), (3, 96, 1088), (8, 520, 5120),
+                                   (1, 5120, 5120)])
+@pytest.mark.parametrize("epi", ["bf16", "gelu", "silu", "f32", "gated", "res"])
+def test_linear_matrix_vector(M, N, K, epi):
+    a, w, b = _gemm_case(300 + M + K, M, N, K)
+    y = O.linear(_dec(a), _dec(w), _dec(b))
+    da, dw, db = dev_bf16(a), dev_bf16(w), dev_bf16(b)
+    outs = []
+    if epi in ("gated", "res"):
+        x0 = G.normal_bf16(31, (M, N))
+        gate = G.normal_bf16(32, (1, N))
+        want = _dec(x0) + (_dec(gate) * y if epi == "gated" else y)
+        for _ in range(2):
+            x = dev_f32_from_bf16(x0)
+            if epi == "gated":
+                D.dit_linear(da, K, dw, db, M, N, K, D.EPI_GATED_RES_F32, x, N, gate=dev_bf16(gate),
+                             gate_stride=N, gate_rows=M)
+            else:
+                D.dit_linear(da, K, dw, db, M, N, K, D.EPI_RES_F32, x, N)
+            outs.append(x)
+        torch.cuda.synchronize()
+        assert_parity(host(outs[0]), want, f"gemv {epi} {M}x{N}x{K}",
+                      max_abs=1e-4 * np.abs(want).max(), rel_l2=1e-5)
+    else:
+        code = {"bf16": D.EPI_BF16, "gelu": D.EPI_GELU_BF16, "silu": D.EPI_SILU_BF16,
+                "f32": D.EPI_F32}[epi]
+        for _ in range(2):
+            out = torch.empty((M, N), dtype=torch.float32 if epi == "f32" else torch.bfloat16,
+                              device="cuda")
+            D.dit_linear(da, K, dw, db, M, N, K, code, out, N)
+            outs.append(out)
+        torch.cuda.synchronize()
+        got = host(outs[0])
+        if epi == "f32":
+            assert_parity(got, y, f"gemv f32 {M}x{N}x{K}", max_abs=1e-4 * np.abs(y).max(),
+                          rel_l2=1e-5)
+        else:
+            ref = {"bf16": y, "gelu": O.gelu_erf(y), "silu": O.silu(y)}[epi]
+            assert_bf16_ulp(got, ref, f"gemv {epi} {M}x{N}x{K}")
+    assert torch.equal(outs[0], outs[1]), "matrix-vector rerun differs"
+
+
+def test_linear_matrix_vector_row_groups():
+    """Two token rows in two row groups of a larger buffer (one row each, with gaps)."""
+    M, N, K = 2, 264, 320
+    a, w, b = _gemm_case(41, M, N, K)
+    y = O.linear(_dec(a), _dec(w), _dec(b))
+    a_pad = np.zeros((2, 3, K), np.uint16)
+    a_pad[:, 1] = a
+    out = torch.full((2, 2, N), float("nan"), dtype=torch.float32, device="cuda")
+    da_pad = dev_bf16(a_pad)
+    D.dit_linear(da_pad[:, 1], K, dev_bf16(w), dev_bf16(b), M, N, K, D.EPI_F32, out, N,
+                 group_rows=1, a_group_stride=3 * K, c_group_stride=2 * N)
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.isnan(got[:, 1]).all(), "rows outside the groups were written"
+    assert_parity(got[:, 0], y, "gemv grouped rows", max_abs=1e-4 * np.abs(y).max(), rel_l2=1e-5)
+
+
 def test_linear_gated_residual_and_row_groups():
     M, N, K, rows_g = 300, 128, 128, 150
     a, w, b = _gemm_case(7, M, N, K)
