@@ -537,7 +537,11 @@ hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s) {
                                                   : (p.m - 1) * p.lda) + 2 * static_cast<int64_t>(p.k);
   const int64_t w_extent = 2 * static_cast<int64_t>(p.n) * p.k;
   const bool offsets_fit = a_extent <= (int64_t{1} << 32) && w_extent <= (int64_t{1} << 32);
-  if (p.m >= 4 * big::kTM && p.n >= big::kTN && offsets_fit) {
+  // Below K = 256 (four slices) the large kernel's one 128 KB-LDS workgroup per
+  // CU cannot overlap a tile's load latency and store with other work; the
+  // small kernel (two workgroups per CU) is faster there (input projection
+  // 32760 x 5120 x 64: 0.178 vs 0.207 ms).
+  if (p.m >= 4 * big::kTM && p.n >= big::kTN && p.k >= 256 && offsets_fit) {
     const int tiles_m = static_cast<int>((p.m + big::kTM - 1) / big::kTM);
     const int tiles_n = (p.n + big::kTN - 1) / big::kTN;
     dim3 grid(tiles_m * tiles_n);

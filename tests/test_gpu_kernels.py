@@ -52,10 +52,13 @@ def test_linear_epilogues(M, N, K, epi):
         assert_bf16_ulp(got, ref, f"linear {epi} {M}x{N}x{K}")
 
 
-# Shapes with M >= 1024 and N >= 256 run the large-tile kernel (256 x 256
-# workgroup tiles, K slices streamed into an LDS ring): ragged M and N, one
-# and several K slices, every epilogue, bitwise-equal reruns.
-@pytest.mark.parametrize("M,N,K", [(1100, 520, 128), (1031, 264, 64), (2304, 512, 320)])
+# Shapes with M >= 1024, N >= 256 and K >= 256 run the large-tile kernel
+# (256 x 256 workgroup tiles, 64-wide K slices streamed into two LDS stages):
+# ragged M and N, an even and an odd number of K slices, every epilogue,
+# bitwise-equal reruns.  (Smaller K falls to the small-tile kernel: the
+# (1031, 264, 64) shape checks that routing.)
+@pytest.mark.parametrize("M,N,K", [(1100, 520, 256), (1031, 264, 384), (2304, 512, 320),
+                                   (1031, 264, 64)])
 @pytest.mark.parametrize("epi", ["bf16", "gelu", "f32", "gated", "res"])
 def test_linear_large_tiles(M, N, K, epi):
     a, w, b = _gemm_case(200 + M + K, M, N, K)
@@ -193,15 +196,15 @@ def test_linear_gated_residual_and_row_groups():
     assert_parity(got[:, :G_rows].reshape(2 * G_rows, N), y[:2 * G_rows], "grouped rows",
                   max_abs=1e-4 * np.abs(y).max(), rel_l2=1e-5)
 
-    # the same grouped addressing through the large-tile kernel (M >= 1024, N >= 256)
-    M2, N2, G2 = 1200, 256, 600
-    a2, w2, b2 = _gemm_case(17, M2, N2, K)
+    # the same grouped addressing through the large-tile kernel (M >= 1024, N >= 256, K >= 256)
+    M2, N2, G2, K2 = 1200, 256, 600, 256
+    a2, w2, b2 = _gemm_case(17, M2, N2, K2)
     y2 = O.linear(_dec(a2), _dec(w2), _dec(b2))
-    a2_pad = np.zeros((2, G2 + 3, K), np.uint16)
-    a2_pad[:, :G2] = a2.reshape(2, G2, K)
+    a2_pad = np.zeros((2, G2 + 3, K2), np.uint16)
+    a2_pad[:, :G2] = a2.reshape(2, G2, K2)
     out2 = torch.full((2, G2 + 5, N2), float("nan"), dtype=torch.float32, device="cuda")
-    D.dit_linear(dev_bf16(a2_pad), K, dev_bf16(w2), dev_bf16(b2), M2, N2, K, D.EPI_F32, out2, N2,
-                 group_rows=G2, a_group_stride=(G2 + 3) * K, c_group_stride=(G2 + 5) * N2)
+    D.dit_linear(dev_bf16(a2_pad), K2, dev_bf16(w2), dev_bf16(b2), M2, N2, K2, D.EPI_F32, out2, N2,
+                 group_rows=G2, a_group_stride=(G2 + 3) * K2, c_group_stride=(G2 + 5) * N2)
     torch.cuda.synchronize()
     got2 = host(out2)
     assert np.isnan(got2[:, G2:]).all(), "rows outside the groups were written (large tiles)"
@@ -214,7 +217,7 @@ def test_linear_operand_past_4gib():
     the large-tile kernel addresses operands by 32-bit byte offsets, so the launcher must hand
     this shape (M >= 1024, N >= 256) to the kernel with 64-bit addressing; the result must
     still match the oracle."""
-    M, N, K, G_rows = 1200, 256, 128, 600
+    M, N, K, G_rows = 1200, 256, 256, 600       # a large-tile shape but for the 4 GiB span
     stride = (1 << 31) + 64                       # elements between the two groups' first rows
     a, w, b = _gemm_case(23, M, N, K)
     y = O.linear(_dec(a), _dec(w), _dec(b))
