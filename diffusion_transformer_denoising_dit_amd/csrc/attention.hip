@@ -20,7 +20,8 @@
 //    mostly does not.)
 //  * K and V tiles (64 keys) stream from HBM/L2 straight into LDS with
 //    global_load_lds_dwordx4 (no VGPR staging) through a 4-stage ring, two
-//    tiles ahead of the math.  Rows are stored unpadded with their 16-byte
+//    tiles ahead of the math, issued by the group entering its softmax
+//    phase (whose VALU-bound stream has issue slots to spare).  Rows are stored unpadded with their 16-byte
 //    chunks XOR-swizzled by row so the K fragment reads and the transposing V
 //    reads hit distinct bank groups.  The loads are issued from inline
 //    assembly so the compiler does not guard each LDS read with a wait for
@@ -42,6 +43,8 @@
 //    and O is divided by the sum once at the end.  The MFMA accumulators are
 //    VGPRs (the file is built with the VGPR form of MFMA) so the softmax
 //    phase reads the scores without AGPR copies.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -60,7 +63,8 @@ struct Tile {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kBytes = kBN * kRowBytes;         // one K or V tile
   static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows per wave-wide 16 B/lane load
-  static constexpr int kLoads = kBN / kRowsPerLoad / kWaves;  // loads per tensor per wave per tile
+  static constexpr int kLoads = kBN / kRowsPerLoad / kWaves;  // prologue: all 8 waves load
+  static constexpr int kLoads4 = kBN / kRowsPerLoad / 4;      // later tiles: the 4 waves of group 1
   static constexpr int kStageBytes = 2 * kBytes;         // K tile then V tile
 };
 
@@ -117,26 +121,25 @@ __device__ __forceinline__ void lds_dma16(const char* gbase, uint32_t voff, uint
 // lane i of a load lands at row i / kChunks, chunk position i % kChunks, so it
 // fetches the chunk that swizzles there.  Rows past `last_row` (the last
 // valid key, relative to the tile) are clamped to it.
-template <int D>
-__device__ __forceinline__ void dma_offsets(uint32_t (&voff)[Tile<D>::kLoads], int wave, int lane,
+template <int D, int NL>
+__device__ __forceinline__ void dma_offsets(uint32_t (&voff)[NL], int wave, int lane,
                                             int64_t stride_bytes, int last_row) {
   using T = Tile<D>;
 #pragma unroll
-  for (int n = 0; n < T::kLoads; ++n) {
-    const int r = (wave * T::kLoads + n) * T::kRowsPerLoad + lane / T::kChunks;
+  for (int n = 0; n < NL; ++n) {
+    const int r = (wave * NL + n) * T::kRowsPerLoad + lane / T::kChunks;
     const int c = (lane % T::kChunks) ^ swz<D>(r);
     voff[n] = static_cast<uint32_t>(min(r, last_row) * stride_bytes + c * 16);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void dma_tile(const char* kg, const char* vg,
-                                         const uint32_t (&voff)[Tile<D>::kLoads],
+template <int D, int NL>
+__device__ __forceinline__ void dma_tile(const char* kg, const char* vg, const uint32_t (&voff)[NL],
                                          uint32_t lds_stage, int wave) {
   using T = Tile<D>;
 #pragma unroll
-  for (int n = 0; n < T::kLoads; ++n) {
-    const uint32_t dst = lds_stage + (wave * T::kLoads + n) * 1024;
+  for (int n = 0; n < NL; ++n) {
+    const uint32_t dst = lds_stage + (wave * NL + n) * 1024;
     lds_dma16(kg, voff[n], dst);
     lds_dma16(vg, voff[n], dst + T::kBytes);
   }
@@ -163,7 +166,7 @@ struct WaveState {
 // (x[l], x[l+32]) in lanes l < 32 and (x[l-32], x[l]) in lanes l >= 32.
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -173,8 +176,9 @@ __device__ __forceinline__ float sum_halves(float x) {
 // MFMA phase: S^T of key tile j+1 (sK = its K stage; absent after the last
 // tile), then O^T = alpha O^T + V^T P^T for tile j (sV = its V stage; absent
 // before the first tile).  LDS reads and MFMAs, plus the O rescale owed by
-// the softmax phase, woven into the score MFMAs (this wave's VALU is idle
-// here while the other wave of the SIMD runs its softmax).  Fragment reads run a fixed number of
+// the softmax phase, a few independent multiplies after each score MFMA so
+// the matrix pipe keeps its queue (as one block before the value MFMAs it
+// idled the pipe for the whole block).  Fragment reads run a fixed number of
 // steps ahead of their MFMA (scheduling fences keep the compiler from hoisting
 // all 32 of them, which would cost 128 VGPRs).
 template <int D, bool kPVPart, bool kQKPart>
@@ -184,33 +188,43 @@ __device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, con
   constexpr int kPV = 4 * W::kDB;  // value steps: (u, db)
   constexpr int kQK = 2 * W::kKS;  // score steps: (ks, t), t fastest: two accumulator chains
   constexpr int kAhead = 2;  // fragment reads in flight ahead of their MFMA
+  // The O rescale owed by the last softmax phase (skipped, wave-uniformly,
+  // when no running max of the wave moved) is spread over the score MFMAs,
+  // kDB*16/kQK multiplies after each, so the matrix pipe never waits for it.
+  constexpr int kMulsPerStep = W::kDB * 16 / kQK;
+  auto rescale_part = [&](int i) {
+#pragma unroll
+    for (int n = 0; n < kMulsPerStep; ++n) {
+      const int idx = i * kMulsPerStep + n;
+      st.o[idx / 16][idx % 16] *= st.alpha;
+    }
+  };
   if constexpr (kQKPart) {
     auto kread = [&](int i) {
       const int t = i % 2, ks = i / 2;
       return *reinterpret_cast<const bf16x8*>(sK + 32 * t * T::kRowBytes + st.k_off[ks]);
     };
-    bf16x8 kf[kQK];
+    auto qk_loop = [&](auto with_rescale) {
+      bf16x8 kf[kQK];
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) kf[i] = kread(i);
+      for (int i = 0; i < kAhead; ++i) kf[i] = kread(i);
+      const f32x16 zero = {};  // first step of each chain: an inline-constant 0 accumulator
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) st.s[t][e] = 0.f;
-#pragma unroll
-    for (int i = 0; i < kQK; ++i) {
-      if (i + kAhead < kQK) kf[i + kAhead] = kread(i + kAhead);
-      __builtin_amdgcn_sched_barrier(0);
-      st.s[i % 2] = mfma32x32x16(kf[i], st.qf[i / 2], st.s[i % 2]);
-    }
-  }
-  if constexpr (kPVPart) {
-    // the O rescale owed by the last softmax phase, skipped (wave-uniform
-    // branch) when no running max of the wave moved
+      for (int i = 0; i < kQK; ++i) {
+        if (i + kAhead < kQK) kf[i + kAhead] = kread(i + kAhead);
+        __builtin_amdgcn_sched_barrier(0);
+        st.s[i % 2] = mfma32x32x16(kf[i], st.qf[i / 2], i < 2 ? zero : st.s[i % 2]);
+        if constexpr (decltype(with_rescale)::value) rescale_part(i);
+      }
+    };
+    if (kPVPart && st.rescale)
+      qk_loop(std::true_type{});
+    else
+      qk_loop(std::false_type{});
+  } else if constexpr (kPVPart) {
     if (st.rescale) {
 #pragma unroll
-      for (int i = 0; i < W::kDB; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st.o[i][e] *= st.alpha;
+      for (int i = 0; i < kQK; ++i) rescale_part(i);
     }
   }
   if constexpr (kPVPart) {
@@ -255,23 +269,22 @@ __device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_va
     float x = max3f(st.s[t][r0], st.s[t][r0 + 1], st.s[t][r0 + 2]);
     x = max3f(x, st.s[t][r0 + 3], st.s[t][r0 + 4]);
     x = max3f(x, st.s[t][r0 + 5], st.s[t][r0 + 6]);
-    m[c4] = fmaxf(x, st.s[t][r0 + 7]);
+    m[c4] = max3f(x, st.s[t][r0 + 7], st.s[t][r0 + 7]);
   }
-  const float m0 = fmaxf(m[0], m[1]), m1 = fmaxf(m[2], m[3]);
   // Running max.  When no query of the wave sees a score above its running
   // max, alpha would be exactly 1: the rescale of l here and of O in the next
   // MFMA phase are skipped, wave-uniformly (after the first tiles most tiles
   // raise no max), and the result is bitwise the same as rescaling by 1.
-  const float m_tile = max_halves(fmaxf(m0, m1)) * c;  // c > 0 keeps the order
+  const float m_tile = max_halves(max3f(m[0], m[1], max3f(m[2], m[3], m[3]))) * c;  // c > 0 keeps the order
   st.rescale = __builtin_amdgcn_ballot_w64(m_tile > st.m_run) != 0;
   if (st.rescale) {
-    const float m_new = fmaxf(st.m_run, m_tile);
+    const float m_new = max3f(st.m_run, m_tile, m_tile);
     st.alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
     st.m_run = m_new;
     st.l_run *= st.alpha;
   }
   const float nm = -st.m_run;
-  float l0 = 0.f, l1 = 0.f;
+  float l0, l1;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     u32x4 w;
@@ -279,8 +292,8 @@ __device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_va
     for (int i = 0; i < 8; i += 2) {
       const float e0 = __builtin_amdgcn_exp2f(fmaf(st.s[u / 2][8 * (u % 2) + i], c, nm));
       const float e1 = __builtin_amdgcn_exp2f(fmaf(st.s[u / 2][8 * (u % 2) + i + 1], c, nm));
-      l0 += e0;
-      l1 += e1;
+      l0 = (u == 0 && i == 0) ? e0 : l0 + e0;
+      l1 = (u == 0 && i == 0) ? e1 : l1 + e1;
       w[i / 2] = pack_bf16x2(e0, e1);
     }
     st.pf[u] = __builtin_bit_cast(bf16x8, w);
@@ -288,33 +301,21 @@ __device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_va
   st.l_run += l0 + l1;
 }
 
-// Wait (each wave for its own loads) until tile `need` has landed, knowing
-// how many tiles were issued after it.
-template <int L>
-__device__ __forceinline__ void wait_tile(int later_tiles) {
-  if (later_tiles >= 2)
-    wait_vmcnt<2 * L>();
-  else if (later_tiles == 1)
-    wait_vmcnt<L>();
-  else
-    wait_vmcnt<0>();
-}
-
 // Issue the loads of tile j into its ring slot (clamping rows past the last
 // valid key in the tile that holds the bound).
-template <int D>
+template <int D, int NL>
 __device__ __forceinline__ void issue_tile(const char* kg0, const char* vg0, int64_t stride_bytes,
                                            int j, int n_valid, uint32_t lds_base, int wave,
-                                           int lane, const uint32_t (&voff)[Tile<D>::kLoads]) {
+                                           int lane, const uint32_t (&voff)[NL]) {
   using T = Tile<D>;
   const int64_t adv = static_cast<int64_t>(j) * kBN * stride_bytes;
   const uint32_t stage = lds_base + (j % kStages) * T::kStageBytes;
   if ((j + 1) * kBN <= n_valid) {
-    dma_tile<D>(kg0 + adv, vg0 + adv, voff, stage, wave);
+    dma_tile<D, NL>(kg0 + adv, vg0 + adv, voff, stage, wave);
   } else {
-    uint32_t vc[T::kLoads];
-    dma_offsets<D>(vc, wave, lane, stride_bytes, n_valid - 1 - j * kBN);
-    dma_tile<D>(kg0 + adv, vg0 + adv, vc, stage, wave);
+    uint32_t vc[NL];
+    dma_offsets<D, NL>(vc, wave, lane, stride_bytes, n_valid - 1 - j * kBN);
+    dma_tile<D, NL>(kg0 + adv, vg0 + adv, vc, stage, wave);
   }
 }
 
@@ -335,7 +336,6 @@ template <int D, bool kOutF32>
 __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   using T = Tile<D>;
   using W = WaveState<D>;
-  constexpr int L = 2 * T::kLoads;  // loads per wave per tile
   __shared__ __attribute__((aligned(1024))) char smem[kStages * T::kStageBytes];
 
   const int tid = threadIdx.x;
@@ -399,10 +399,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   const float c = p.scale_log2;
 
   uint32_t voff[T::kLoads];
-  dma_offsets<D>(voff, wave, lane, stride_bytes, kBN - 1);
+  dma_offsets<D, T::kLoads>(voff, wave, lane, stride_bytes, kBN - 1);
 #pragma unroll
   for (int j = 0; j < kStages - 1; ++j)
-    if (j < n_tiles) issue_tile<D>(kg0, vg0, stride_bytes, j, n_valid, lds_base, wave, lane, voff);
+    if (j < n_tiles) issue_tile<D, T::kLoads>(kg0, vg0, stride_bytes, j, n_valid, lds_base, wave, lane, voff);
+  uint32_t voff4[T::kLoads4];
+  dma_offsets<D, T::kLoads4>(voff4, wave % 4, lane, stride_bytes, kBN - 1);
 
   W st;
   // Q fragments.  The wait for them also covers the first tiles' loads;
@@ -442,16 +444,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     }
   }
 
+  const bool a_grp_c = grp == 0;
   // Global phase 2m opens with "tile m has landed, ring slot of tile m-2 is
-  // free": every wave waits for its own loads of tile m, then after the
-  // barrier issues its share of tile m+2 (tiles 0..2 were issued above).  The
-  // first group meets phase 2m before the MFMA phase of tile m-1, the second
-  // (one phase behind) before the softmax phase of tile m-1.
+  // free" (the value reads of tile m-2 ended with phase 2m-1).  The first
+  // group meets phase 2m before the MFMA phase that starts on tile m, the
+  // second (one phase behind) before the softmax phase of tile m-1.  Tiles
+  // 0..2 come from the prologue (every wave, waited for with the Q loads);
+  // tile m+2 (m >= 1) is issued right after barrier 2m by the 4 waves of the
+  // second group alone -- they are entering a softmax phase, whose in-order
+  // stream has issue slots to spare between VALU instructions, while the
+  // MFMA group's stream has none -- and those waves wait for their loads of
+  // tile m (issued at phase 2m-4; only tile m+1's are newer) before barrier
+  // 2m.
+  constexpr int L4 = 2 * T::kLoads4;  // loads per loading wave per tile
   auto phase_barrier = [&](bool duty, int m) {
-    if (duty && m < n_tiles) wait_tile<L>(min(m == 0 ? 2 : m + 1, n_tiles - 1) - m);
+    duty = duty && !a_grp_c;
+    if (duty && m >= 3 && m < n_tiles) {
+      if (m + 1 < n_tiles) wait_vmcnt<L4>(); else wait_vmcnt<0>();
+    }
     __builtin_amdgcn_s_barrier();
     if (duty && m >= 1 && m + 2 < n_tiles)
-      issue_tile<D>(kg0, vg0, stride_bytes, m + 2, n_valid, lds_base, wave, lane, voff);
+      issue_tile<D, T::kLoads4>(kg0, vg0, stride_bytes, m + 2, n_valid, lds_base, wave % 4, lane, voff4);
   };
   auto stage = [&](int j) { return smem + (j % kStages) * T::kStageBytes; };
   // A wave in its MFMA phase runs at raised issue priority: when both waves
