@@ -298,6 +298,110 @@ def mmdit_blocks(reps, stream):
     return out
 
 
+def other_configs(reps, stream):
+    """ms and TFLOP/s of the other workloads, each through the same entry
+    points: the DiT block at the tiny shape (256 + 32 tokens, hidden 256) and
+    at the FLUX-like image shape (CFG batch 2, 4096 + 512 tokens, hidden 3072),
+    joint attention alone at the Wan-like 720p shape (75600 + 512 tokens, 300
+    valid, 40 heads x 128), and the full denoising loop (24-block image DiT,
+    CFG batch 2, guidance 5, 30 Euler steps from sigma 1 to 0) as end-to-end
+    ms per step.  Valid text lengths are the seeded draws of the parity
+    inputs; activations N(0,1) and weights N(0, 0.02) are drawn on the device
+    (timing does not depend on the values)."""
+    import torch
+
+    import diffusion_transformer_denoising_dit_amd as D
+    from synthetic import configs as C
+    from synthetic import gen as G
+    g = torch.Generator("cuda").manual_seed(12)
+
+    def rnd(*shape, std=1.0, mean=0.0):
+        return (torch.randn(shape, generator=g, device="cuda") * std + mean).to(torch.bfloat16)
+
+    def block_w(Dh, F):
+        return {"w_qkv": rnd(3 * Dh, Dh, std=0.02), "b_qkv": rnd(3 * Dh, std=0.02),
+                "g_q": rnd(Dh, std=0.02, mean=1.0), "g_k": rnd(Dh, std=0.02, mean=1.0),
+                "w_o": rnd(Dh, Dh, std=0.02), "b_o": rnd(Dh, std=0.02),
+                "w_up": rnd(F, Dh, std=0.02), "b_up": rnd(F, std=0.02),
+                "w_dn": rnd(Dh, F, std=0.02), "b_dn": rnd(Dh, std=0.02)}
+
+    out = {}
+    for key, s, valid in (("c1_block", C.C1, [20]),
+                          ("c2_block", C.C2, [int(v) for v in G.block_inputs(C.C2, weights=False)["txt_valid"]])):
+        desc = D.block_desc(s, valid)
+        w = block_w(s.hidden, s.mlp)
+        mod = rnd(s.batch, 6, s.hidden)
+        x = torch.randn((s.batch, s.n_tok, s.hidden), generator=g, device="cuda")
+        nb = D.dit_block_workspace_bytes(desc)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+        def blk(desc=desc, w=w, mod=mod, x=x, ws=ws, nb=nb):
+            D.dit_block_forward(desc, w, mod, x, ws, nb)
+
+        blk()
+        ms = timed(blk, max(10, reps), stream)
+        fl = block_flops(s, valid)
+        out[key] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                    "algorithmic_tflop": round(fl / 1e12, 4), "txt_valid": valid}
+        del w, mod, x, ws
+
+    s = C.C4
+    HD = s.heads * s.head_dim
+    q, k, v = (rnd(s.batch, s.n_tok, HD) for _ in range(3))
+    o = torch.empty_like(q)
+    adesc = D.attn_desc(s.batch, s.n_vis, s.n_txt, s.heads, s.head_dim, [300])
+
+    def attn():
+        D.dit_joint_attention(adesc, q, k, v, HD, o, HD)
+
+    attn()
+    ms = timed(attn, max(3, reps // 2), stream)
+    fl = attention_flops(s.n_tok, s.n_vis + 300, s.heads, s.head_dim, s.batch)
+    out["c4_attention"] = {"ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                           "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "algorithmic_tflop": round(fl / 1e12, 3), "txt_valid": [300]}
+    del q, k, v, o
+
+    shape = C.C5
+    b = shape.block
+    Dh, F, Cl = b.hidden, b.mlp, shape.latent_channels
+    valid = [int(v) for v in G.loop_inputs(shape).txt_valid]
+    glue = {"t_w1": rnd(Dh, shape.freq_dim, std=0.02), "t_b1": rnd(Dh, std=0.02),
+            "t_w2": rnd(Dh, Dh, std=0.02), "t_b2": rnd(Dh, std=0.02),
+            "in_w": rnd(Dh, Cl, std=0.02), "in_b": rnd(Dh, std=0.02),
+            "fin_w": rnd(2 * Dh, Dh, std=0.02), "fin_b": rnd(2 * Dh, std=0.02),
+            "out_w": rnd(Cl, Dh, std=0.02), "out_b": rnd(Cl, std=0.02),
+            "text": rnd(b.batch, b.n_txt, Dh)}
+    layers = [block_w(Dh, F) for _ in range(shape.depth)]
+    mod_w = [rnd(6 * Dh, Dh, std=0.02) for _ in range(shape.depth)]
+    mod_b = [rnd(6 * Dh, std=0.02) for _ in range(shape.depth)]
+    weights = D.model_weights(glue, layers, mod_w, mod_b)
+    desc = D.model_desc(shape, valid)
+    nb = D.dit_denoise_workspace_bytes(desc)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    lat = rnd(1, b.n_vis, Cl).float()
+    sig = [1.0 - i / shape.steps for i in range(shape.steps + 1)]
+
+    def loop(n):
+        for i in range(n):
+            D.dit_denoise_step(desc, weights, lat, sig[i], sig[i + 1], shape.guidance, ws, nb)
+
+    loop(2)
+    ms = timed(lambda: loop(shape.steps), 1, stream) / shape.steps
+    assert torch.isfinite(lat).all(), "non-finite latent in the denoising loop"
+    fl = shape.depth * block_flops(b, valid)
+    out["c5_loop"] = {"ms_per_step": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                      "algorithmic_tflop_per_step": round(fl / 1e12, 3),
+                      "steps": shape.steps, "depth": shape.depth, "guidance": shape.guidance,
+                      "txt_valid": valid,
+                      "note": "end-to-end denoiser step (timestep MLP, modulation, input projection, "
+                              "24 blocks, final projection, guided Euler update); TFLOP/s counts the "
+                              "blocks' algorithmic work only"}
+    del layers, mod_w, mod_b, weights, ws, lat, glue
+    torch.cuda.empty_cache()
+    return out
+
+
 def wan_block(reps, stream):
     """The Wan-style block (self-attention over the video tokens, text
     cross-attention, MLP) at the c3 video shape: 32760 video tokens, 512
@@ -525,6 +629,7 @@ def main():
     gemms = block_gemms(max(3, args.steps // 2), stream)
     mm = mmdit_blocks(max(5, args.steps), stream)
     wan = wan_block(max(3, args.steps // 2), stream)
+    others = other_configs(args.steps, stream)
     traffic = attn_traffic()
     result = {
         "metric": METRIC,
@@ -575,6 +680,7 @@ def main():
         "block_gemms": gemms,
         "mmdit": mm,
         "wan_block": wan,
+        "other_configs": others,
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_kernel<128, false> (joint attention)",
