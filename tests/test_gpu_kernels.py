@@ -319,6 +319,15 @@ ATTN_SHAPES = [
     # exercises the workgroup -> (batch row, head, query tile) decode past batch 2
     C.AttnShape("attn_b8", batch=8, n_vis=300, n_txt=20, heads=3, head_dim=64,
                 txt_valid=("fixed", (0, 1, 5, 19, 20, 7, 13, 2)), seed=44),
+    # one launch whose batch rows hold 120, 128, 129, 192, 193, 256, 257 and
+    # 320 valid keys: 2 to 5 key tiles of 64, the last one full or ragged --
+    # every path of the K/V ring (tiles from the prologue only, the first
+    # tile issued inside the loop, the last tile with and without a newer
+    # load in flight)
+    C.AttnShape("attn_tiles_d128", batch=8, n_vis=120, n_txt=200, heads=2, head_dim=128,
+                txt_valid=("fixed", (0, 8, 9, 72, 73, 136, 137, 200)), seed=45),
+    C.AttnShape("attn_tiles_d64", batch=8, n_vis=120, n_txt=200, heads=2, head_dim=64,
+                txt_valid=("fixed", (0, 8, 9, 72, 73, 136, 137, 200)), seed=46),
 ]
 
 
