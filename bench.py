@@ -41,9 +41,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
 # WRITE x1.0); summary and commands in profiles/attn_c3_hbm_traffic.md.  Valid
 # only for the kernel source they were taken on.
 ATTN_TRAFFIC = {
-    "source_sha256": "5da62184316822ef72d88abd24a609926f1462080e97f1409d261cef447483c9",
-    "fetch_bytes": 3.7189e9,
-    "write_bytes": 0.3413e9,
+    "source_sha256": "1dc6aefa54e4bfe882583ca71cc59d26a49c8b24d2beb43dcae33cff422f271f",
+    "fetch_bytes": 3.7190e9,
+    "write_bytes": 0.3410e9,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     "profile": "profiles/attn_c3_hbm_traffic.md",

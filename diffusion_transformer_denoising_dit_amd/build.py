@@ -34,11 +34,13 @@ COMMON_FLAGS = [
 ]
 
 
-# Per-file device flags.  attention.hip keeps its MFMA accumulators in VGPRs:
-# its softmax phase reads the scores with VALU instructions, and the AGPR form
-# would copy every accumulator register across the register files each tile.
+# Per-file device flags.  attention.hip keeps its MFMA accumulators in VGPRs
+# (its softmax phase reads the scores with VALU instructions, and the AGPR form
+# would copy every accumulator register across the register files each tile)
+# and is built without NaN semantics (its scores are never NaN), which lets
+# the compiler fuse its maxima into v_max3_f32 without quieting operations.
 FILE_FLAGS = {
-    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
 }
 
 

@@ -161,12 +161,19 @@ struct WaveState {
   int v_off[2][kDB];  // V^T transposing-read byte offsets (rows 8g + 4*hi + s16/4)
 };
 
+// max of three floats.  This file is compiled with -fno-honor-nans (its
+// scores and running maxima are never NaN: masked keys are -inf and padded
+// key rows are never loaded), so the compiler fuses the two fmaxf into one
+// v_max3_f32 without quieting ops and schedules it freely (an inline-asm
+// v_max3 costs hazard no-ops between dependent maxima).
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
 // max / sum of a value with the one in the other half of the wave (lane^32),
 // without an LDS round trip: v_permlane32_swap of (x, x) leaves
 // (x[l], x[l+32]) in lanes l < 32 and (x[l-32], x[l]) in lanes l >= 32.
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max3f(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+  return vmax3(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -266,19 +273,19 @@ __device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_va
 #pragma unroll
   for (int c4 = 0; c4 < 4; ++c4) {
     const int t = c4 / 2, r0 = 8 * (c4 % 2);
-    float x = max3f(st.s[t][r0], st.s[t][r0 + 1], st.s[t][r0 + 2]);
-    x = max3f(x, st.s[t][r0 + 3], st.s[t][r0 + 4]);
-    x = max3f(x, st.s[t][r0 + 5], st.s[t][r0 + 6]);
-    m[c4] = max3f(x, st.s[t][r0 + 7], st.s[t][r0 + 7]);
+    float x = vmax3(st.s[t][r0], st.s[t][r0 + 1], st.s[t][r0 + 2]);
+    x = vmax3(x, st.s[t][r0 + 3], st.s[t][r0 + 4]);
+    x = vmax3(x, st.s[t][r0 + 5], st.s[t][r0 + 6]);
+    m[c4] = vmax3(x, st.s[t][r0 + 7], st.s[t][r0 + 7]);
   }
   // Running max.  When no query of the wave sees a score above its running
   // max, alpha would be exactly 1: the rescale of l here and of O in the next
   // MFMA phase are skipped, wave-uniformly (after the first tiles most tiles
   // raise no max), and the result is bitwise the same as rescaling by 1.
-  const float m_tile = max_halves(max3f(m[0], m[1], max3f(m[2], m[3], m[3]))) * c;  // c > 0 keeps the order
+  const float m_tile = max_halves(vmax3(m[0], m[1], vmax3(m[2], m[3], m[3]))) * c;  // c > 0 keeps the order
   st.rescale = __builtin_amdgcn_ballot_w64(m_tile > st.m_run) != 0;
   if (st.rescale) {
-    const float m_new = max3f(st.m_run, m_tile, m_tile);
+    const float m_new = vmax3(st.m_run, m_tile, m_tile);
     st.alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
     st.m_run = m_new;
     st.l_run *= st.alpha;
