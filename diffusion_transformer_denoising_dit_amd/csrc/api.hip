@@ -173,17 +173,27 @@ dit_status check_linear(const dit_linear_args* a) {
         !aligned(a->gate, 8))
       return fail(DIT_EINVAL, "gated epilogue needs gate (8-byte aligned), gate_rows >= 1 and a "
                               "gate_stride that is a multiple of 4");
-  } else {
-    // the output must not overlap the A operand's rows (bytes spanned by A)
-    const int64_t span_rows = a->group_rows > 0 ? a->group_rows : a->m;
-    const int64_t groups = a->group_rows > 0 ? (a->m + a->group_rows - 1) / a->group_rows : 1;
-    const size_t a_bytes = static_cast<size_t>(((groups - 1) * (a->group_rows > 0 ? a->a_group_stride : 0)) +
-                                               (span_rows - 1) * a->lda + a->k) * 2;
-    const size_t esz = a->epilogue == DIT_EPI_F32 || a->epilogue == DIT_EPI_RES_F32 ? 4 : 2;
-    const size_t c_bytes = static_cast<size_t>(((groups - 1) * (a->group_rows > 0 ? a->c_group_stride : 0)) +
-                                               (span_rows - 1) * a->ldc + a->n) * esz;
-    if (overlap(a->a, a_bytes, a->out, c_bytes))
-      return fail(DIT_EINVAL, "out overlaps the A operand");
+  }
+  // The output is written while other workgroups still read A, the bias and
+  // the gate: it must not overlap any of them (bytes spanned, row grouping
+  // and strides included).
+  const int64_t span_rows = a->group_rows > 0 ? a->group_rows : a->m;
+  const int64_t groups = a->group_rows > 0 ? (a->m + a->group_rows - 1) / a->group_rows : 1;
+  const size_t a_bytes = static_cast<size_t>(((groups - 1) * (a->group_rows > 0 ? a->a_group_stride : 0)) +
+                                             (span_rows - 1) * a->lda + a->k) * 2;
+  const size_t esz = a->epilogue == DIT_EPI_F32 || a->epilogue == DIT_EPI_RES_F32 ||
+                             a->epilogue == DIT_EPI_GATED_RES_F32 ? 4 : 2;
+  const size_t c_bytes = static_cast<size_t>(((groups - 1) * (a->group_rows > 0 ? a->c_group_stride : 0)) +
+                                             (span_rows - 1) * a->ldc + a->n) * esz;
+  if (overlap(a->a, a_bytes, a->out, c_bytes))
+    return fail(DIT_EINVAL, "out overlaps the A operand");
+  if (a->bias && overlap(a->bias, static_cast<size_t>(a->n) * 2, a->out, c_bytes))
+    return fail(DIT_EINVAL, "out overlaps the bias");
+  if (a->epilogue == DIT_EPI_GATED_RES_F32) {
+    const size_t gate_bytes =
+        static_cast<size_t>(((a->m - 1) / a->gate_rows) * a->gate_stride + a->n) * 2;
+    if (overlap(a->gate, gate_bytes, a->out, c_bytes))
+      return fail(DIT_EINVAL, "out overlaps the gate rows");
   }
   return DIT_OK;
 }

@@ -26,6 +26,14 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
 
   float m = -INFINITY;
   for (int q = 0; q < p.parts; ++q) m = fmaxf(m, p.lses[q][lse_idx]);
+  if (m == -INFINITY) {
+    // every partial is empty (no valid key in any partition): the empty sum,
+    // weighted output 0 and log-denominator -inf, as an empty partial gives
+    const u32x2 z = {0u, 0u};
+    *reinterpret_cast<u32x2*>(p.out + row * p.out_stride + col) = z;
+    if (p.lse_out && e0 == 0) p.lse_out[lse_idx] = -INFINITY;
+    return;
+  }
   float den = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int q = 0; q < p.parts; ++q) {

@@ -145,8 +145,9 @@ dit_status dit_attention_partial(const dit_partial_desc* desc, const uint16_t* q
  *   outs, lses  host arrays of `parts` device pointers laid out as the out
  *               and lse of dit_attention_partial (part_row_stride for all)
  *   out         bf16 (b, i, h, e) at out + (b*n_q + i)*out_row_stride + h*head_dim + e
- * parts in [1, DIT_MAX_PARTS]; every (b, h, i) needs at least one partial
- * with a valid key (else its row is NaN).  Strides: part_row_stride a
+ * parts in [1, DIT_MAX_PARTS].  A (b, h, i) whose partials all hold no
+ * valid key (every lse_p = -inf) gets out = 0 and lse_out = -inf, the merge's
+ * neutral element (what an empty partial itself returns).  Strides: part_row_stride a
  * multiple of 4, out_row_stride a multiple of 8, both >= heads*head_dim.
  * out must not overlap any input. */
 typedef struct dit_merge_desc {
@@ -176,8 +177,9 @@ typedef enum dit_epilogue {
  *   bias  bf16 [n] or NULL.
  *   out   row r at out + (r / group_rows)*c_group_stride + (r % group_rows)*ldc;
  *         bf16 or fp32 by epilogue.  With DIT_EPI_GATED_RES_F32 and
- *         DIT_EPI_RES_F32 `out` is read and written (the residual stream); it
- *         must not overlap a (checked for every epilogue but the gated one).
+ *         DIT_EPI_RES_F32 `out` is read and written (the residual stream).
+ *         For every epilogue `out` must not overlap a, the bias or (gated)
+ *         the gate rows it reads (DIT_EINVAL, nothing enqueued).
  *   gate  bf16, DIT_EPI_GATED_RES_F32 only: row r uses gate + (r / gate_rows)
  *         * gate_stride (gate_rows >= 1).
  * Requires k % 64 == 0 (DIT_EUNSUPPORTED otherwise), lda/ldc/strides multiples

@@ -41,6 +41,7 @@ from .dit import (
     silu,
     denoise_step,
     step_tokens,
+    arithmetic,
 )
 from . import mmdit, stepcache, wan
 
@@ -48,5 +49,5 @@ __all__ = [
     "bf16_decode", "round_bf16", "adaln_modulate", "linear", "rms_norm_full",
     "token_positions", "rope_axial", "attention_probs", "attention_partial", "merge_partials", "joint_attention",
     "gelu_erf", "block_forward", "cfg_combine", "euler_update", "sigma_schedule",
-    "timestep_features", "silu", "denoise_step",
+    "timestep_features", "silu", "denoise_step", "arithmetic",
 ]

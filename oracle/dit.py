@@ -25,12 +25,49 @@ in the docstring of the function that implements it.
 
 from __future__ import annotations
 
+import contextlib
 import math
 
 import numpy as np
 from scipy.special import erf
 
 from .numerics import bf16_decode, round_bf16
+
+# Working precision between the bfloat16 rounding points.  The oracle is fp64;
+# ``arithmetic(np.float32)`` re-evaluates the same formulas with fp32 values
+# between the same rounding points.  That second evaluation is an instrument
+# for measuring how far two correct bf16-storing evaluations of a composite
+# (a block, a step) can drift apart, which is what the composite tolerance is
+# derived from; it is never the parity reference.
+_ARITH = np.float64
+
+
+@contextlib.contextmanager
+def arithmetic(dtype):
+    """Evaluate every oracle formula in ``dtype`` (np.float64 or np.float32)
+    inside the ``with`` block; bfloat16 rounding points are unchanged."""
+    global _ARITH
+    if dtype not in (np.float64, np.float32):
+        raise ValueError(f"unsupported working precision {dtype}")
+    old, _ARITH = _ARITH, dtype
+    try:
+        yield
+    finally:
+        _ARITH = old
+
+
+def _f(a):
+    """``a`` as an array in the working precision (no copy when it already is)."""
+    return np.asarray(a, dtype=_ARITH)
+
+
+def _rounder(round_points):
+    """The rounding applied at each bf16 storage point: round to the nearest
+    bfloat16 (ties to even) and carry on in the working precision; identity
+    for the unrounded evaluation."""
+    if round_points:
+        return lambda a: _f(round_bf16(a))
+    return _f
 
 
 # ----------------------------------------------------------------------------
@@ -43,7 +80,7 @@ def adaln_modulate(x, shift, scale, eps):
     biased variance and no learned affine, then apply the timestep
     modulation as x_hat * (1 + scale) + shift.  ``shift`` and ``scale``
     broadcast against ``x`` (one vector per batch row)."""
-    x = np.asarray(x, dtype=np.float64)
+    x = _f(x)
     mu = x.mean(axis=-1, keepdims=True)
     var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
     x_hat = (x - mu) / np.sqrt(var + eps)
@@ -53,7 +90,7 @@ def adaln_modulate(x, shift, scale, eps):
 def linear(a, w, b=None):
     """y = a W^T + b with W stored [out, in] ("ChunkFlow" Appendix B, the
     projection and MLP terms of equations (13) and (16))."""
-    y = np.asarray(a, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+    y = _f(a) @ _f(w).T
     if b is not None:
         y = y + b
     return y
@@ -64,7 +101,7 @@ def rms_norm_full(q, gain, eps):
     q / sqrt(mean(q^2) + eps) * gain.  The pages require the sum of squares
     to cover the whole projection, not each head shard ("Difflet Engineering
     Report", Wan attention head sharding and global RMS)."""
-    q = np.asarray(q, dtype=np.float64)
+    q = _f(q)
     ms = (q * q).mean(axis=-1, keepdims=True)
     return q / np.sqrt(ms + eps) * gain
 
@@ -72,12 +109,12 @@ def rms_norm_full(q, gain, eps):
 def gelu_erf(z):
     """GELU in its exact form z * Phi(z) = z * (1 + erf(z / sqrt 2)) / 2.
     The pages name the MLP but not its activation; the erf form is taken."""
-    z = np.asarray(z, dtype=np.float64)
+    z = _f(z)
     return z * 0.5 * (1.0 + erf(z / math.sqrt(2.0)))
 
 
 def silu(z):
-    z = np.asarray(z, dtype=np.float64)
+    z = _f(z)
     return z / (1.0 + np.exp(-z))
 
 
@@ -108,7 +145,7 @@ def rope_axial(x, pos, dims, theta):
     (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos).
     Base theta, interleaved pairing and the block order are the reading taken
     (the pages only name RoPE)."""
-    x = np.asarray(x, dtype=np.float64)
+    x = _f(x)
     pos = np.asarray(pos)
     d = x.shape[-1]
     pairs = x.reshape(x.shape[:-1] + (d // 2, 2))  # pair j of the head: dims (2j, 2j+1)
@@ -121,8 +158,8 @@ def rope_axial(x, pos, dims, theta):
         j = np.arange(n_a, dtype=np.float64)
         inv_freq = float(theta) ** (-2.0 * j / int(d_a))
         ang = pos[:, axis].astype(np.float64)[:, None] * inv_freq[None, :]  # [N, d_a/2]
-        c = np.cos(ang)[:, None, :]  # [N, 1, d_a/2] broadcast over heads
-        s = np.sin(ang)[:, None, :]
+        c = _f(np.cos(ang))[:, None, :]  # [N, 1, d_a/2] broadcast over heads
+        s = _f(np.sin(ang))[:, None, :]
         x0 = pairs[..., p0:p0 + n_a, 0]
         x1 = pairs[..., p0:p0 + n_a, 1]
         out[..., p0:p0 + n_a, 0] = x0 * c - x1 * s
@@ -145,13 +182,13 @@ def attention_probs(q, k, n_keys_valid, scale):
     ("Difflet", section 4.2 Representing Attention Mask).  Every query row is
     normalised by one softmax over all its valid keys, visual and text
     together ("Difflet", section 4, joint attention)."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
+    q = _f(q)
+    k = _f(k)
     nv = int(n_keys_valid)
     s = (q @ k[:nv].T) * scale
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
-    p = np.zeros((q.shape[0], k.shape[0]), dtype=np.float64)
+    p = np.zeros((q.shape[0], k.shape[0]), dtype=_ARITH)
     p[:, :nv] = e / e.sum(axis=1, keepdims=True)
     lse = (m + np.log(e.sum(axis=1, keepdims=True)))[:, 0]
     return p, lse
@@ -168,15 +205,15 @@ def joint_attention(q, k, v, n_vis, txt_valid, scale=None, chunk=1024):
     1/sqrt(d).  Returns (o [B, R, heads, d], lse [B, heads, R]) where lse is
     the natural log of each row's softmax denominator (max included).
     """
-    qsel = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+    qsel = _f(q)
+    k = _f(k)
+    v = _f(v)
     B, N, Hh, d = k.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     R = qsel.shape[1]
-    o = np.zeros((B, R, Hh, d), dtype=np.float64)
-    lse = np.zeros((B, Hh, R), dtype=np.float64)
+    o = np.zeros((B, R, Hh, d), dtype=_ARITH)
+    lse = np.zeros((B, Hh, R), dtype=_ARITH)
     for b in range(B):
         nk = int(n_vis) + int(txt_valid[b])
         for h in range(Hh):
@@ -232,16 +269,23 @@ def merge_partials(parts):
     partials; the merged output is the combined weighted sum divided by the
     combined exponential sum.  Returns (o [B, R, heads, d], lse [B, heads, R])
     with lse = M + log(sum_p exp(m_p - M) l_p), the natural log of the joint
-    softmax denominator."""
+    softmax denominator.  A query whose partials are all empty (no valid key
+    anywhere) gets the empty sum: o = 0 and lse = -inf, the same neutral
+    element an empty partial is."""
     M = np.max(np.stack([m for _, m, _ in parts]), axis=0)
     num = 0.0
     den = 0.0
     for acc, m, l in parts:
-        w = np.where(np.isfinite(m), np.exp(m - M), 0.0)  # [B, heads, R]
+        w = np.where(np.isfinite(m), np.exp(m - np.where(np.isfinite(M), M, 0.0)), 0.0)
         num = num + acc * np.transpose(w, (0, 2, 1))[..., None]
         den = den + w * l
-    o = num / np.transpose(den, (0, 2, 1))[..., None]
-    return o, M + np.log(den)
+    empty = den == 0.0  # [B, heads, R]
+    safe = np.where(empty, 1.0, den)
+    o = num / np.transpose(safe, (0, 2, 1))[..., None]
+    o = np.where(np.transpose(empty, (0, 2, 1))[..., None], 0.0, o)
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, M + np.log(safe))
+    return o, lse
 
 
 # ----------------------------------------------------------------------------
@@ -249,7 +293,7 @@ def merge_partials(parts):
 # ----------------------------------------------------------------------------
 
 def _dec(a):
-    return bf16_decode(a) if np.asarray(a).dtype == np.uint16 else np.asarray(a, np.float64)
+    return _f(bf16_decode(a) if np.asarray(a).dtype == np.uint16 else a)
 
 
 def block_forward(inp, shape, round_points=True, rows=None, keep=False):
@@ -280,7 +324,7 @@ def block_forward(inp, shape, round_points=True, rows=None, keep=False):
     per token, so the restricted result is exact for those rows.
     Returns x2 [B, R, D] (and the intermediates when ``keep``).
     """
-    R_ = round_bf16 if round_points else (lambda a: a)
+    R_ = _rounder(round_points)
     B, N, D = shape.batch, shape.n_tok, shape.hidden
     H, d = shape.heads, shape.head_dim
     x = _dec(inp["x"]).reshape(B, N, D)
@@ -327,8 +371,8 @@ def cfg_combine(v_cond, v_uncond, guidance):
     """Classifier-free guidance, applied once to the two predictions
     ("Difflet Engineering Report", CFG parallelism applies the guidance
     combination once): v_uncond + g (v_cond - v_uncond)."""
-    v_cond = np.asarray(v_cond, dtype=np.float64)
-    v_uncond = np.asarray(v_uncond, dtype=np.float64)
+    v_cond = _f(v_cond)
+    v_uncond = _f(v_uncond)
     return v_uncond + guidance * (v_cond - v_uncond)
 
 
@@ -338,7 +382,7 @@ def euler_update(x, v, sigma, sigma_next):
     ("Difflet", section 1 and section 3: the scheduler turns the velocity into
     a less noisy latent).  The latent is kept in full precision (fp32 on the
     GPU, "Difflet Engineering Report", Video output corrections)."""
-    return np.asarray(x, dtype=np.float64) + (sigma_next - sigma) * np.asarray(v, np.float64)
+    return _f(x) + (sigma_next - sigma) * _f(v)
 
 
 def timestep_features(t, dim):
@@ -349,7 +393,7 @@ def timestep_features(t, dim):
     half = dim // 2
     f = np.exp(-math.log(10000.0) * np.arange(half, dtype=np.float64) / half)
     a = float(t) * f
-    return np.concatenate([np.cos(a), np.sin(a)])
+    return _f(np.concatenate([np.cos(a), np.sin(a)]))
 
 
 # ----------------------------------------------------------------------------
@@ -362,7 +406,7 @@ def step_tokens(model, latent, sigma, round_points=True, t_scale=1000.0):
     ``denoise_step``): s = SiLU(SiLU(sinusoidal(t_scale * sigma) W_t1 + b_t1)
     W_t2 + b_t2) and, per batch row b, x[b] = [bf16(latent) W_in + b_in;
     text[b]].  Returns (s [D], x [B, N, D])."""
-    R_ = round_bf16 if round_points else (lambda a: a)
+    R_ = _rounder(round_points)
     shp = model.shape
     blk = shp.block
     B, nv, N, D = blk.batch, blk.n_vis, blk.n_tok, blk.hidden
@@ -370,9 +414,9 @@ def step_tokens(model, latent, sigma, round_points=True, t_scale=1000.0):
     f = R_(timestep_features(float(np.float32(t_scale)) * sig32, shp.freq_dim))
     c = R_(silu(linear(f, _dec(model.t_w1), _dec(model.t_b1))))
     s = R_(silu(linear(c, _dec(model.t_w2), _dec(model.t_b2))))
-    lat = np.asarray(latent, dtype=np.float64)
+    lat = _f(latent)
     xin = linear(R_(lat), _dec(model.in_w), _dec(model.in_b))  # [Bl, n_vis, D]
-    x = np.empty((B, N, D))
+    x = np.empty((B, N, D), dtype=_ARITH)
     for b in range(B):
         x[b, :nv] = xin[0 if shp.cfg else b]
         x[b, nv:] = _dec(model.text[b])
@@ -406,13 +450,13 @@ def denoise_step(model, latent, sigma, sigma_next, guidance, round_points=True, 
     tokens whose velocity and update are returned; it is only exact for a
     single-block model (a later block needs every row of the one before).
     Returns (new latent rows [Bl, R, C], v [B, R, C])."""
-    R_ = round_bf16 if round_points else (lambda a: a)
+    R_ = _rounder(round_points)
     shp = model.shape
     blk = shp.block
     B, nv, N, D = blk.batch, blk.n_vis, blk.n_tok, blk.hidden
     cfg = shp.cfg
     sig32 = float(np.float32(sigma))
-    lat = np.asarray(latent, dtype=np.float64)
+    lat = _f(latent)
     s, x = step_tokens(model, lat, sigma, round_points, t_scale)
     if shp.depth > 1 and rows is not None:
         raise ValueError("row subsets are only exact for a single block")

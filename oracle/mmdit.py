@@ -40,7 +40,7 @@ from __future__ import annotations
 import numpy as np
 
 from .dit import (_dec, adaln_modulate, gelu_erf, joint_attention, linear, rms_norm_full,
-                  rope_axial, round_bf16, token_positions)
+                  rope_axial, _rounder, token_positions)
 
 
 def _norm_rope(t, gain, pos, shape):
@@ -60,7 +60,7 @@ def double_block_forward(inp, shape, round_points=True, rows=None):
     indices of the joint sequence [0, S + L) (keys and values still use every
     token, so the restricted result is exact).  Returns (x_img', x_txt') for
     the selected image rows and text rows (all rows when ``rows`` is None)."""
-    R_ = round_bf16 if round_points else (lambda a: a)
+    R_ = _rounder(round_points)
     B, S, L, D = shape.batch, shape.n_vis, shape.n_txt, shape.hidden
     H, d = shape.heads, shape.head_dim
     xs = {"img": _dec(inp["x_img"]).reshape(B, S, D), "txt": _dec(inp["x_txt"]).reshape(B, L, D)}
@@ -115,7 +115,7 @@ def single_block_forward(inp, shape, round_points=True, rows=None):
       x' = x + gate * ([o | GELU(up)] w2^T + b2)
 
     ``rows`` restricts the output rows (exact, as in ``double_block_forward``)."""
-    R_ = round_bf16 if round_points else (lambda a: a)
+    R_ = _rounder(round_points)
     B, N, D, F = shape.batch, shape.n_tok, shape.hidden, shape.mlp
     H, d = shape.heads, shape.head_dim
     x = _dec(inp["x"]).reshape(B, N, D)

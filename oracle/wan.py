@@ -31,8 +31,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .dit import (_dec, adaln_modulate, gelu_erf, joint_attention, linear, rms_norm_full,
-                  rope_axial, round_bf16, token_positions)
+from .dit import (_dec, _f, adaln_modulate, gelu_erf, joint_attention, linear, rms_norm_full,
+                  rope_axial, _rounder, token_positions)
 
 
 def wan_block_forward(inp, shape, round_points=True, rows=None):
@@ -52,7 +52,7 @@ def wan_block_forward(inp, shape, round_points=True, rows=None):
     ``rows`` restricts the output to a subset of video tokens (exact: self
     keys/values use every token, cross keys/values come from the context).
     Returns x3 [B, R, D]."""
-    R_ = round_bf16 if round_points else (lambda a: a)
+    R_ = _rounder(round_points)
     B, S, L, D = shape.batch, shape.n_vis, shape.n_txt, shape.hidden
     H, d = shape.heads, shape.head_dim
     x = _dec(inp["x"]).reshape(B, S, D)
@@ -80,7 +80,7 @@ def wan_block_forward(inp, shape, round_points=True, rows=None):
     x1 = x[:, sel] + gate1 * linear(R_(o.reshape(B, len(sel), D)), W["w_o"], W["b_o"])
 
     # cross-attention to the valid context tokens
-    zero = np.zeros((1, 1, D))
+    zero = _f(np.zeros((1, 1, D)))
     hc = R_(adaln_modulate(x1, zero, zero, shape.ln_eps))
     qc = R_(heads(rms_norm_full(R_(linear(hc, W["w_cq"], W["b_cq"])), W["g_cq"], shape.rms_eps)))
     kvc = R_(linear(ctx, W["w_ckv"], W["b_ckv"]))

@@ -14,8 +14,13 @@ Tolerances:
 
 from __future__ import annotations
 
+import json
+import os
+
 import numpy as np
 import torch
+
+import oracle as O
 
 MAX_ABS = 2e-2
 REL_L2 = 5e-3
@@ -77,23 +82,76 @@ def assert_bf16_ulp(got, ref, what="", atol_rel=1e-4):
     assert rl <= REL_L2, f"{what}: rel-L2 {rl:.3e}"
 
 
-def assert_composite(got, ref, exact, what=""):
+# Composite bound factor: the GPU may sit at most TWIN_FACTOR times as far
+# from the bf16-storing fp64 oracle as the oracle's own fp32 twin does (see
+# assert_composite).  Measured on MI355X at full size: 0.88-1.38 times.
+TWIN_FACTOR = 1.5
+
+
+def oracle_evals(fn):
+    """Evaluate an oracle composite three ways: ``fn(round_points)`` in fp64
+    with bf16 rounding points (the reference), in fp64 unrounded (exact), and
+    in fp32 between the same rounding points (the twin).  Returns
+    (ref, exact, twin); tuples returned by ``fn`` are kept as tuples."""
+    ref = fn(True)
+    exact = fn(False)
+    with O.arithmetic(np.float32):
+        twin = fn(True)
+    as64 = lambda t: tuple(np.asarray(a, np.float64) for a in t) if isinstance(t, tuple) \
+        else np.asarray(t, np.float64)
+    return ref, exact, as64(twin)
+
+
+def _log_parity(record):
+    path = os.environ.get("DIT_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(record) + "\n")
+
+
+def assert_composite(got, ref, exact, what="", twin=None):
     """Parity of a composite output (a block, a denoising step, a loop).
 
-    Between bf16 storage points, one-ulp rounding flips of the intermediates
-    are amplified by the gates (|gate| up to ~4 with N(0, 1) modulation), so
-    two equally valid bf16 evaluations differ by more than 2e-2 at full size.
-    The bound is therefore max(2e-2, max|exact - ref|): the GPU may be no
-    further from the bf16-storing oracle (ref) than bf16 storage itself moves
-    the unrounded oracle (exact).  rel-L2 <= 5e-3 always applies."""
+    Between bf16 storage points, fp32 accumulation on the GPU and fp64 in the
+    oracle land some intermediates on different sides of a bf16 rounding
+    boundary; each such one-ulp flip is carried through the following GEMMs
+    and amplified by the gates (|gate| up to ~4 with N(0, 1) modulation), so
+    two equally valid bf16-storing evaluations differ by more than 2e-2 at
+    full size ("Difflet", section 7.4 sees the same between two correct bf16
+    parallelisations of one DiT).  The oracle measures the size of that
+    effect itself: ``twin`` is the same composite evaluated in fp32 between
+    the same rounding points (oracle.arithmetic), a second correct
+    evaluation of the kind the GPU performs.  The GPU adds rounding the twin
+    does not have (its softmax weights enter the value product as bf16, its
+    exp and erf are the hardware's), hence the factor TWIN_FACTOR on the
+    twin's spread.  The bound is also capped by the distance bf16 storage
+    moves the unrounded oracle (exact): max-abs <= max(2e-2,
+    min(TWIN_FACTOR * max|twin - ref|, max|exact - ref|)), rel-L2 <= 5e-3.
+    Without a twin the bound is max(2e-2, max|exact - ref|) (used only where
+    the oracle has no fp32 form: the guided cache state)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     exact = np.asarray(exact, np.float64)
     spread = float(np.abs(exact - ref).max())
-    bound = max(MAX_ABS, spread)
     cos = float((got * ref).sum() / (np.linalg.norm(got) * np.linalg.norm(ref)))
-    print(f"[composite] {what}: bf16-storage spread {spread:.3e} -> max-abs bound {bound:.3e}; "
-          f"cosine {cos:.7f}", flush=True)
+    ma, rl = errors(got, ref)
+    rec = {"what": what, "n": int(got.size), "max_abs": ma, "rel_l2": rl,
+           "over_2e-2": int((np.abs(got - ref) > MAX_ABS).sum()), "exact_spread": spread,
+           "cosine": cos, "max_abs_ref": float(np.abs(ref).max())}
+    if twin is not None:
+        twin = np.asarray(twin, np.float64)
+        tspread = float(np.abs(twin - ref).max())
+        bound = max(MAX_ABS, min(TWIN_FACTOR * tspread, spread))
+        rec.update(twin_spread=tspread, twin_rel_l2=errors(twin, ref)[1],
+                   twin_over_2e_2=int((np.abs(twin - ref) > MAX_ABS).sum()))
+        print(f"[composite] {what}: fp32-twin spread {tspread:.3e} (bf16-storage spread "
+              f"{spread:.3e}) -> max-abs bound {bound:.3e}; cosine {cos:.7f}", flush=True)
+    else:
+        bound = max(MAX_ABS, spread)
+        print(f"[composite] {what}: bf16-storage spread {spread:.3e} -> max-abs bound {bound:.3e}; "
+              f"cosine {cos:.7f}", flush=True)
+    rec["bound"] = bound
+    _log_parity(rec)
     assert_parity(got, ref, what, max_abs=bound, rel_l2=REL_L2)
 
 

@@ -117,6 +117,17 @@ def test_linear_argument_errors():
     _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, D.EPI_GATED_RES_F32, FAKE * 4, 8, stream=0)
     _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, D.EPI_BF16, FAKE + 64, 8, stream=0)
     _expect("DIT_EINVAL", f, None, 64, FAKE * 2, None, 4, 8, 64, D.EPI_BF16, FAKE * 4, 8, stream=0)
+    # the gated residual epilogue: out (fp32, 4 x 8 x 4 B = 128 B) may not overlap
+    # A (4 x 64 bf16 = 512 B), the bias (16 B) or the gate rows it reads
+    g = dict(gate=FAKE * 5, gate_stride=8, gate_rows=4)
+    _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, D.EPI_GATED_RES_F32, FAKE + 256, 8,
+            **g, stream=0)
+    _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, FAKE * 4 + 64, 4, 8, 64, D.EPI_GATED_RES_F32,
+            FAKE * 4, 8, **g, stream=0)
+    _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, D.EPI_GATED_RES_F32, FAKE * 5 - 64,
+            8, **g, stream=0)
+    _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, FAKE * 4 + 16, 4, 8, 64, D.EPI_BF16, FAKE * 4, 8,
+            stream=0)
     # m == 0 is a no-op that succeeds without touching the GPU
     f(FAKE, 64, FAKE * 2, None, 0, 8, 64, D.EPI_BF16, FAKE * 4, 8, stream=0)
 

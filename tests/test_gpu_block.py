@@ -16,7 +16,7 @@ import oracle as O
 from synthetic import configs as C
 from synthetic import gen as G
 from tests.gpu_util import (assert_composite, assert_parity, bits_of, dev_bf16,
-                            dev_f32_from_bf16, host)
+                            dev_f32_from_bf16, host, oracle_evals)
 from tests.sampling import sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -72,10 +72,9 @@ def _block_sampled(s, n_random):
     inp = G.block_inputs(s)
     got = host(run_block(s, inp))
     rows = sample_rows(s.n_vis, s.n_txt, inp["txt_valid"], n_random=n_random, seed=s.seed)
-    want = O.block_forward(inp, s, rows=rows)
-    exact = O.block_forward(inp, s, rows=rows, round_points=False)
+    want, exact, twin = oracle_evals(lambda r: O.block_forward(inp, s, rows=rows, round_points=r))
     print(f"{s.name}: valid {inp['txt_valid'].tolist()}, {len(rows)} sampled rows", flush=True)
-    assert_composite(got[:, rows], want, exact, f"{s.name} block (sampled rows)")
+    assert_composite(got[:, rows], want, exact, f"{s.name} block (sampled rows)", twin)
 
 
 @pytest.mark.slow

@@ -14,7 +14,7 @@ import diffusion_transformer_denoising_dit_amd as D
 from oracle import mmdit as M
 from synthetic import configs as C
 from synthetic import gen as G
-from tests.gpu_util import assert_composite, dev_bf16, dev_f32_from_bf16, host
+from tests.gpu_util import assert_composite, dev_bf16, dev_f32_from_bf16, host, oracle_evals
 from tests.sampling import sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -66,20 +66,19 @@ def _run_single(shape, inp):
 def test_double_block_small(shape):
     inp = G.double_block_inputs(shape)
     gi, gt = _run_double(shape, inp)
-    ri, rt = M.double_block_forward(inp, shape)
-    ei, et = M.double_block_forward(inp, shape, round_points=False)
-    assert_composite(gi, ri, ei, f"{shape.name} double block, image stream")
+    (ri, rt), (ei, et), (ti, tt) = oracle_evals(
+        lambda r: M.double_block_forward(inp, shape, round_points=r))
+    assert_composite(gi, ri, ei, f"{shape.name} double block, image stream", ti)
     if shape.n_txt:
-        assert_composite(gt, rt, et, f"{shape.name} double block, text stream")
+        assert_composite(gt, rt, et, f"{shape.name} double block, text stream", tt)
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: s.name)
 def test_single_block_small(shape):
     inp = G.single_block_inputs(shape)
     got = _run_single(shape, inp)
-    assert_composite(got, M.single_block_forward(inp, shape),
-                     M.single_block_forward(inp, shape, round_points=False),
-                     f"{shape.name} single block")
+    ref, exact, twin = oracle_evals(lambda r: M.single_block_forward(inp, shape, round_points=r))
+    assert_composite(got, ref, exact, f"{shape.name} single block", twin)
 
 
 def test_double_block_deterministic():
@@ -97,11 +96,11 @@ def test_double_block_c2_sampled():
     inp = G.double_block_inputs(shape)
     gi, gt = _run_double(shape, inp)
     rows = sample_rows(shape.n_vis, shape.n_txt, inp["txt_valid"], n_random=24, seed=5)
-    ri, rt = M.double_block_forward(inp, shape, rows=rows)
-    ei, et = M.double_block_forward(inp, shape, round_points=False, rows=rows)
+    (ri, rt), (ei, et), (ti, tt) = oracle_evals(
+        lambda r: M.double_block_forward(inp, shape, round_points=r, rows=rows))
     S = shape.n_vis
-    assert_composite(gi[:, rows[rows < S]], ri, ei, "c2 double block, image rows (sampled)")
-    assert_composite(gt[:, rows[rows >= S] - S], rt, et, "c2 double block, text rows (sampled)")
+    assert_composite(gi[:, rows[rows < S]], ri, ei, "c2 double block, image rows (sampled)", ti)
+    assert_composite(gt[:, rows[rows >= S] - S], rt, et, "c2 double block, text rows (sampled)", tt)
 
 
 @pytest.mark.slow
@@ -110,6 +109,6 @@ def test_single_block_c2_sampled():
     inp = G.single_block_inputs(shape)
     got = _run_single(shape, inp)
     rows = sample_rows(shape.n_vis, shape.n_txt, inp["txt_valid"], n_random=24, seed=6)
-    assert_composite(got[:, rows], M.single_block_forward(inp, shape, rows=rows),
-                     M.single_block_forward(inp, shape, round_points=False, rows=rows),
-                     "c2 single block (sampled)")
+    ref, exact, twin = oracle_evals(
+        lambda r: M.single_block_forward(inp, shape, rows=rows, round_points=r))
+    assert_composite(got[:, rows], ref, exact, "c2 single block (sampled)", twin)

@@ -104,6 +104,7 @@ def test_merge_formula_on_synthetic_partials():
     lses = (rng.standard_normal((P, B, H, N)) * 6).astype(np.float32)
     lses[1, 0] = -np.inf  # an empty partial in batch row 0
     lses[3, :, 1, :5] = -np.inf
+    lses[:, 1, 2, 7:10] = -np.inf  # three queries of one head with every partial empty
     parts = [(outs[p].reshape(B, N, H, d).astype(np.float64), lses[p].astype(np.float64),
               np.ones((B, H, N))) for p in range(P)]
     o_want, lse_want = O.merge_partials(parts)
@@ -113,8 +114,15 @@ def test_merge_formula_on_synthetic_partials():
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     D.dit_attention_merge(B, N, H, d, dev_o, H * d, dev_l, out, H * d, lse)
     torch.cuda.synchronize()
-    assert_parity(host(out).reshape(B, N, H, d), o_want, "merge formula")
-    assert_parity(host(lse), lse_want, "merge lse", max_abs=1e-4, rel_l2=1e-6)
+    empty = np.isneginf(lse_want)
+    assert empty.sum() == 3
+    lse_h = host(lse)
+    assert np.all(np.isneginf(lse_h[empty])), "all-empty rows: lse must be -inf"
+    out_h = host(out).reshape(B, N, H, d)
+    assert np.all(out_h[1, 7:10, 2] == 0.0), "all-empty rows: output must be 0"
+    assert_parity(out_h, o_want, "merge formula")
+    assert_parity(np.where(empty, 0.0, lse_h), np.where(empty, 0.0, lse_want), "merge lse",
+                  max_abs=1e-4, rel_l2=1e-6)
 
 
 @pytest.mark.slow

@@ -208,7 +208,9 @@ def _run_cached_loop(m, lat0, policy, check=True):
                 ref_x, v = O.denoise_step(m, x_before, sig[i], sig[i + 1], shp.guidance)
                 ex_x, ve = O.denoise_step(m, x_before, sig[i], sig[i + 1], shp.guidance,
                                           round_points=False)
-                assert_composite(x_after, ref_x, ex_x, f"latent after full step {i}")
+                with O.arithmetic(np.float32):
+                    tw_x, _ = O.denoise_step(m, x_before, sig[i], sig[i + 1], shp.guidance)
+                assert_composite(x_after, ref_x, ex_x, f"latent after full step {i}", tw_x)
                 _assert_guided(m, prev_after, v, ve, f"guided velocity step {i}")
             n_full += 1
         else:

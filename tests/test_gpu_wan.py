@@ -15,7 +15,7 @@ import diffusion_transformer_denoising_dit_amd as D
 from oracle import wan as W
 from synthetic import configs as C
 from synthetic import gen as G
-from tests.gpu_util import assert_composite, dev_bf16, dev_f32_from_bf16, host
+from tests.gpu_util import assert_composite, dev_bf16, dev_f32_from_bf16, host, oracle_evals
 from tests.sampling import sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -49,8 +49,8 @@ def _run(shape, inp):
 def test_wan_block_small(shape):
     inp = G.wan_block_inputs(shape)
     got = _run(shape, inp)
-    assert_composite(got, W.wan_block_forward(inp, shape),
-                     W.wan_block_forward(inp, shape, round_points=False), f"{shape.name} wan block")
+    ref, exact, twin = oracle_evals(lambda r: W.wan_block_forward(inp, shape, round_points=r))
+    assert_composite(got, ref, exact, f"{shape.name} wan block", twin)
 
 
 def test_wan_block_padded_context_ignored_bitwise():
@@ -71,6 +71,6 @@ def test_wan_block_c3_sampled():
     inp = G.wan_block_inputs(shape)
     got = _run(shape, inp)
     rows = sample_rows(shape.n_vis, 0, [0], n_random=32, seed=8)
-    assert_composite(got[:, rows], W.wan_block_forward(inp, shape, rows=rows),
-                     W.wan_block_forward(inp, shape, round_points=False, rows=rows),
-                     "c3 wan block (sampled)")
+    ref, exact, twin = oracle_evals(
+        lambda r: W.wan_block_forward(inp, shape, rows=rows, round_points=r))
+    assert_composite(got[:, rows], ref, exact, "c3 wan block (sampled)", twin)

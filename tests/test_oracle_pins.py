@@ -46,6 +46,40 @@ def test_round_bf16_matches_torch_on_float32_values():
     np.testing.assert_array_equal(O.round_bf16(x.astype(np.float64)), want)
 
 
+def _round_bf16_frexp(x):
+    """Round to the nearest bfloat16, ties to even, written from the format's
+    definition: x = m 2**e with 0.5 <= |m| < 1 (frexp); a normal bfloat16
+    keeps 8 significant bits, so round m * 2**8 to an integer (numpy rounds
+    halves to even) and scale back; below 2**-126 the spacing is fixed at
+    2**-133; beyond the largest finite bfloat16 the result is infinite."""
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)
+    r = np.ldexp(np.round(m * 256.0), e - 8)
+    sub = np.abs(x) < 2.0 ** -126
+    r[sub] = np.ldexp(np.round(np.ldexp(x[sub], 133)), -133)
+    big = np.abs(r) > (2.0 - 2.0 ** -7) * 2.0 ** 127
+    r[big] = np.copysign(np.inf, x[big])
+    return r
+
+
+def test_round_bf16_random_fp64_against_frexp_definition():
+    """fp64 inputs that are not float32 values: random mantissas over the
+    whole exponent range, exact ties between neighbouring bfloat16 values,
+    and values one fp64 ulp either side of a tie (where a detour through
+    float32 would round twice)."""
+    rng = np.random.default_rng(21)
+    n = 200000
+    x = rng.standard_normal(n) * np.ldexp(1.0, rng.integers(-140, 128, n))
+    b = O.bf16_decode(rng.integers(0, 0x7F7F, 20000, dtype=np.uint16)) * rng.choice([-1.0, 1.0], 20000)
+    ulp = np.ldexp(1.0, np.frexp(b)[1] - 8)
+    ulp[np.abs(b) < 2.0 ** -126] = 2.0 ** -133
+    ties = b + ulp / 2
+    x = np.concatenate([x, ties, np.nextafter(ties, np.inf), np.nextafter(ties, -np.inf)])
+    with np.errstate(over="ignore"):
+        assert not np.array_equal(x.astype(np.float32).astype(np.float64), x)
+    np.testing.assert_array_equal(O.round_bf16(x), _round_bf16_frexp(x))
+
+
 def test_input_generator_rounding_matches_torch():
     rng = np.random.default_rng(3)
     x = (rng.standard_normal(50000) * 3).astype(np.float32)
@@ -279,6 +313,22 @@ def test_gelu_values_and_torch():
     z = np.linspace(-8, 8, 1001)
     want = torch.nn.functional.gelu(torch.from_numpy(z), approximate="none").numpy()
     np.testing.assert_allclose(O.gelu_erf(z), want, rtol=1e-14, atol=1e-15)
+
+
+def test_silu_values_odd_identity_and_torch():
+    """SiLU(z) = z sigma(z): hand values, the identity SiLU(z) - SiLU(-z) = z
+    (sigma(z) + sigma(-z) = 1, which a sign or term error breaks), the limits
+    and torch's fp64 silu."""
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert abs(O.silu(np.array([1.0]))[0] - 0.7310585786300049) < 1e-15
+    assert abs(O.silu(np.array([-1.0]))[0] + 0.2689414213699951) < 1e-15
+    assert abs(O.silu(np.array([2.0]))[0] - 1.7615941559557646) < 1e-15
+    z = np.linspace(-30, 30, 6001)
+    np.testing.assert_allclose(O.silu(z) - O.silu(-z), z, rtol=1e-13, atol=1e-13)
+    assert abs(O.silu(np.array([40.0]))[0] - 40.0) < 1e-12
+    assert abs(O.silu(np.array([-40.0]))[0]) < 1e-15
+    want = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    np.testing.assert_allclose(O.silu(z), want, rtol=1e-14, atol=1e-300)
 
 
 def test_linear_explicit_loops():

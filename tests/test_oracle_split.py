@@ -91,3 +91,21 @@ def test_single_partial_normalises_to_softmax():
     p, lse = O.attention_probs(q[0, :, 0], k[0, :, 0], 6, 0.4)
     np.testing.assert_allclose(acc[0, :, 0] / l[0, 0][:, None], p @ v[0, :, 0], rtol=0, atol=1e-13)
     np.testing.assert_allclose(m[0, 0] + np.log(l[0, 0]), lse, rtol=0, atol=1e-13)
+
+
+def test_merge_of_only_empty_partials_is_the_empty_sum():
+    """A query none of whose partitions holds a valid key: every partial is
+    the neutral element (acc 0, m -inf, l 0), so the merge is the empty sum,
+    o = 0 with log-denominator -inf; adding one non-empty partial to them
+    gives exactly that partial's normalised output."""
+    q, k, v = _qkv(9, B=2, R=5, N=6)
+    scale = 0.25
+    empty = O.attention_partial(q, k, v, [0, 0], scale)
+    assert np.all(empty[0] == 0) and np.all(empty[1] == -np.inf) and np.all(empty[2] == 0)
+    o, lse = O.merge_partials([empty, empty])
+    assert np.all(o == 0.0) and np.all(lse == -np.inf)
+    full = O.attention_partial(q, k, v, [6, 4], scale)
+    o2, lse2 = O.merge_partials([empty, full, empty])
+    want_o, want_lse = O.joint_attention(q, k, v, 0, [6, 4], scale)
+    np.testing.assert_allclose(o2, want_o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse2, want_lse, rtol=1e-13, atol=1e-14)
