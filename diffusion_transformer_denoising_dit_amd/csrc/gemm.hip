@@ -211,20 +211,21 @@ namespace big {
 
 constexpr int kTM = 256;                          // token rows per workgroup
 constexpr int kTN = 256;                          // output features per workgroup
-constexpr int kBK = 64;                           // k per stage
-constexpr int kStages = 2;
+constexpr int kBK = 64;                           // k per slice
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowBytes = 2 * kBK;                // 128
+constexpr int kRowBytes = 2 * kBK;                // 128: one operand row of a slice
 constexpr int kChunks = kRowBytes / 16;           // 8 chunks of 16 bytes per row
 constexpr int kRowsPerLoad = 1024 / kRowBytes;    // 8 rows per wave-wide 16 B/lane load
-constexpr int kLoaders = 4;                       // waves 0-3 issue every load
-constexpr int kLoadsA = kTM / kRowsPerLoad / kLoaders;  // 8
-constexpr int kLoadsW = kTN / kRowsPerLoad / kLoaders;  // 8
-constexpr int kLoads = kLoadsA + kLoadsW;         // loads per loader wave per slice
-constexpr int kTileA = kTM * kRowBytes;
+constexpr int kHalfBytes = 128 * kRowBytes;       // 16 KB: 128 rows of one slice
+constexpr int kLoadsHalf = 128 / kRowsPerLoad / 4;  // 4 loads per wave fill 128 rows
+// LDS ring: W slices in 3 stages (32 KB each); the A rows of each group (the
+// 128 token rows it multiplies) in 2 stages of their own (16 KB each).
+constexpr int kWStages = 3;
+constexpr int kAStages = 2;
 constexpr int kTileW = kTN * kRowBytes;
-constexpr int kStageBytes = kTileA + kTileW;      // 64 KB
+constexpr int kOffA = kWStages * kTileW;                    // A half h, stage t at kOffA + (2h + t) * kHalfBytes
+constexpr int kLdsBytes = kOffA + 2 * kAStages * kHalfBytes;  // 160 KB
 constexpr int kGroupM = 8;
 
 // 16-byte chunk c of a 128-byte row r sits at chunk position c ^ swz(r).  LDS
@@ -235,6 +236,13 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Waits until at most 4 * items of this wave's loads are in flight.
+__device__ __forceinline__ void wait_items(int items) {
+  if (items <= 0) wait_vmcnt<0>();
+  else if (items == 1) wait_vmcnt<kLoadsHalf>();
+  else if (items == 2) wait_vmcnt<2 * kLoadsHalf>();
+  else wait_vmcnt<3 * kLoadsHalf>();
 }
 // Waits until every LDS access of this wave has completed.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
@@ -269,27 +277,37 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint3
 
 typedef __attribute__((address_space(3))) char* lds_char_ptr;
 
-// The 8 waves form two groups, one wave of each per SIMD: the loaders (waves
-// 0-3, token rows 0-127 of the tile) and the others (token rows 128-255), each
+// The 8 waves form two groups, one wave of each per SIMD: group 0 (waves
+// 0-3) multiplies token rows 0-127 of the tile, group 1 rows 128-255, each
 // wave 128 tokens x 64 features.  A wave alternates a memory phase (read the
-// 16 A and 8 W operand fragments of one 64-k slice from LDS into registers;
-// loaders also issue the loads of the next slice) and an MFMA phase (the 32
+// 16 A and 8 W operand fragments of one 64-k slice from LDS into registers,
+// and issue its share of later slices' loads) and an MFMA phase (the 32
 // MFMAs of that slice), the second group one phase behind the first, with a
-// workgroup barrier at every phase boundary.  On each SIMD one wave then
-// multiplies while the other moves data: a phase's 32 MFMAs issue back to
-// back from registers.  Slice s is read by the loaders in phase 2s and by the
-// others in phase 2s+1; its stage receives slice s+2 when the loaders start
-// phase 2s+2.
+// workgroup barrier at every phase boundary: on each SIMD one wave
+// multiplies while the other moves data.  Group 0 reads slice s in phase 2s,
+// group 1 in phase 2s+1.
+//
+// Loads.  Each group issues, after the barrier that opens its memory phase,
+// 4 wave-wide loads per wave of two 128-row pieces of later slices:
+//   phase 2s   (group 0): A rows 128-255 of slice s+1 ("A1"), then W rows
+//                         0-127 of slice s+2 ("W1")
+//   phase 2s+1 (group 1): A rows 0-127 of slice s+2 ("A0"), then W rows
+//                         128-255 of slice s+2 ("W2")
+// W has three stages and each A half two, so every piece has 3 phases (W1:
+// 4) between its issue and the barrier before its first reader -- a slot is
+// refilled as soon as both of its readers are done with it.  Before a
+// barrier a wave waits only for its own pieces that the next phase reads
+// (loads complete in order, so "at most n in flight" names them).  The LDS
+// ring fills all 160 KB of the CU.
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int hi = lane / 32;
   const int grp = wave / 4, wq = wave % 4;
-  const bool loader = grp == 0;
 
   // tile of this workgroup: XCD-contiguous ids, then groups of kGroupM token tiles
   int tm, tn;
@@ -310,56 +328,51 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
   const int64_t m0 = static_cast<int64_t>(tm) * kTM;
   const int n0 = tn * kTN;
 
-  // Loads (loader waves): wave w fills rows [(w*kLoads + n) * kRowsPerLoad,
-  // +kRowsPerLoad) of the A and W tiles; lane i lands at row i / kChunks,
-  // chunk position i % kChunks and fetches the chunk that swizzles there.
-  // Rows past m or n are clamped (computed, never stored).  Byte offsets from
-  // p.a and p.w fit 32 bits (checked by the launcher).
-  uint32_t a_vo[kLoadsA], w_vo[kLoadsW];
+  // This wave's loads: rows [(wq*4 + n) * 8, +8) of a 128-row piece; lane i
+  // lands at row i / 8, chunk position i % 8 and fetches the chunk that
+  // swizzles there.  Group 0 loads A rows 128-255 and W rows 0-127, group 1
+  // A rows 0-127 and W rows 128-255.  Rows past m or n are clamped (computed,
+  // never stored).  Byte offsets from p.a and p.w fit 32 bits (checked by the
+  // launcher).
+  const int a_half = 1 - grp, w_half = grp;
+  uint32_t a_vo[kLoadsHalf], w_vo[kLoadsHalf];
 #pragma unroll
-  for (int n = 0; n < kLoadsA; ++n) {
-    const int rr = (wq * kLoadsA + n) * kRowsPerLoad + lane / kChunks;
-    const int c = (lane % kChunks) ^ swz(rr);
-    int64_t m = m0 + rr;
+  for (int n = 0; n < kLoadsHalf; ++n) {
+    const int r = (wq * kLoadsHalf + n) * kRowsPerLoad + lane / kChunks;  // row within the piece
+    const int c = (lane % kChunks) ^ swz(r);
+    int64_t m = m0 + a_half * 128 + r;
     if (m > p.m - 1) m = p.m - 1;
     a_vo[n] = static_cast<uint32_t>(a_row_offset(p, m) * 2 + c * 16);
-  }
-#pragma unroll
-  for (int n = 0; n < kLoadsW; ++n) {
-    const int rr = (wq * kLoadsW + n) * kRowsPerLoad + lane / kChunks;
-    const int c = (lane % kChunks) ^ swz(rr);
-    const int nr = min(n0 + rr, p.n - 1);
+    const int nr = min(n0 + w_half * 128 + r, p.n - 1);
     w_vo[n] = static_cast<uint32_t>(static_cast<int64_t>(nr) * p.k * 2 + c * 16);
   }
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_ptr)smem));
-  auto issue = [&](int kt) {
-    const uint32_t st = lds_base + (kt % kStages) * kStageBytes;
-    const char* ba = reinterpret_cast<const char*>(p.a) + static_cast<int64_t>(kt) * kRowBytes;
-    const char* bw = reinterpret_cast<const char*>(p.w) + static_cast<int64_t>(kt) * kRowBytes;
+  const int k_tiles = p.k / kBK;
+  // A piece of slice kt into its stage (dst is that piece's first byte).
+  auto issue_a = [&](int kt) {
+    const uint32_t dst = lds_base + kOffA + (2 * a_half + kt % kAStages) * kHalfBytes;
+    const char* src = reinterpret_cast<const char*>(p.a) + static_cast<int64_t>(kt) * kRowBytes;
 #pragma unroll
-    for (int n = 0; n < kLoadsA; ++n) lds_dma16(ba, a_vo[n], st + (wq * kLoadsA + n) * 1024);
+    for (int n = 0; n < kLoadsHalf; ++n) lds_dma16(src, a_vo[n], dst + (wq * kLoadsHalf + n) * 1024);
+  };
+  auto issue_w = [&](int kt) {
+    const uint32_t dst = lds_base + (kt % kWStages) * kTileW + w_half * kHalfBytes;
+    const char* src = reinterpret_cast<const char*>(p.w) + static_cast<int64_t>(kt) * kRowBytes;
 #pragma unroll
-    for (int n = 0; n < kLoadsW; ++n) lds_dma16(bw, w_vo[n], st + kTileA + (wq * kLoadsW + n) * 1024);
+    for (int n = 0; n < kLoadsHalf; ++n) lds_dma16(src, w_vo[n], dst + (wq * kLoadsHalf + n) * 1024);
   };
 
-  const int k_tiles = p.k / kBK;
-  if (loader) {
-    issue(0);
-    if (k_tiles > 1) issue(1);
-  }
-
   // wave tile: 128 token rows (grp) x 64 features (wq).  Operand read offsets
-  // within a stage: row = base row + lane%32 (+32 per MFMA tile, an
-  // immediate); the swizzle depends on the row's bits 1..3, which the tile
+  // within the A piece / W stage: row = base row + lane%32 (+32 per MFMA tile,
+  // an immediate); the swizzle depends on the row's bits 1..3, which the tile
   // offsets do not change.
-  const int wm = grp, wn = wq;
   int a_off[4], w_off[4];
   {
     const int r = lane % 32;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      a_off[ks] = (wm * 128 + r) * kRowBytes + (((2 * ks + hi) ^ swz(r)) * 16);
-      w_off[ks] = kTileA + (wn * 64 + r) * kRowBytes + (((2 * ks + hi) ^ swz(r)) * 16);
+      a_off[ks] = r * kRowBytes + (((2 * ks + hi) ^ swz(r)) * 16);
+      w_off[ks] = (wq * 64 + r) * kRowBytes + (((2 * ks + hi) ^ swz(r)) * 16);
     }
   }
 
@@ -371,55 +384,87 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // The second group takes one extra barrier first (and the loaders one at
-  // the end), which puts it exactly one phase behind.  Before the barrier
-  // that opens phase 2s, each loader waits for its own loads of slice s
-  // (slices up to s are in flight then, up to s+1 at s = 0).
-  if (!loader) phase_barrier();
-  for (int s = 0; s < k_tiles; ++s) {
-    if (loader) {
-      if (s == 0 && k_tiles > 1)
-        wait_vmcnt<kLoads>();
-      else
-        wait_vmcnt<0>();
+  auto memory_phase = [&](int s, bf16x8 (&wf)[4][2], bf16x8 (&af)[4][4]) {
+    const char* ws = smem + (s % kWStages) * kTileW;
+    const char* as = smem + kOffA + (2 * grp + s % kAStages) * kHalfBytes;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        wf[ks][i] = *reinterpret_cast<const bf16x8*>(ws + w_off[ks] + i * 32 * kRowBytes);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        af[ks][j] = *reinterpret_cast<const bf16x8*>(as + a_off[ks] + j * 32 * kRowBytes);
     }
-    phase_barrier();
-    if (loader && s >= 1 && s + 1 < k_tiles) issue(s + 1);
-    bf16x8 wf[4][2], af[4][4];
-    {
-      const char* st = smem + (s % kStages) * kStageBytes;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          wf[ks][i] = *reinterpret_cast<const bf16x8*>(st + w_off[ks] + i * 32 * kRowBytes);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          af[ks][j] = *reinterpret_cast<const bf16x8*>(st + a_off[ks] + j * 32 * kRowBytes);
-      }
-    }
-    wait_lgkm0();  // this wave's reads of slice s are done before its stage is reused
-    phase_barrier();
+    wait_lgkm0();  // this wave's reads of slice s are done before its stage is refilled
+  };
+  auto mfma_phase = [&](const bf16x8 (&wf)[4][2], const bf16x8 (&af)[4][4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(wf[ks][i], af[ks][j], acc[i][j]);
+  };
+
+  if (grp == 0) {
+    // issue order: W1(0), A1(0), W1(1), then per slice s: A1(s+1), W1(s+2)
+    issue_w(0);
+    issue_a(0);
+    if (k_tiles > 1) issue_w(1);
+    for (int s = 0; s < k_tiles; ++s) {
+      // W1(s) (this wave's pieces of slice s that phase 2s reads) has landed;
+      // A1(s) and W1(s+1) may still be in flight
+      wait_items(1 + (s + 1 < k_tiles));
+      phase_barrier();  // phase 2s
+      if (s + 1 < k_tiles) issue_a(s + 1);
+      if (s + 2 < k_tiles) issue_w(s + 2);
+      bf16x8 wf[4][2], af[4][4];
+      memory_phase(s, wf, af);
+      // A1(s), read by group 1 in phase 2s+1, has landed; W1(s+1), A1(s+1)
+      // and W1(s+2) may still be in flight
+      wait_items(2 * (s + 1 < k_tiles) + (s + 2 < k_tiles));
+      phase_barrier();  // phase 2s+1
+      mfma_phase(wf, af);
+    }
+    phase_barrier();  // the second group's last phase
+  } else {
+    // issue order: A0(0), W2(0), A0(1), W2(1), then per slice s: A0(s+2), W2(s+2)
+    issue_a(0);
+    issue_w(0);
+    if (k_tiles > 1) {
+      issue_a(1);
+      issue_w(1);
+    }
+    // A0(0) and W2(0) have landed before group 0 reads slice 0
+    wait_items(k_tiles > 1 ? 2 : 0);
+    phase_barrier();  // phase 0
+    for (int s = 0; s < k_tiles; ++s) {
+      phase_barrier();  // phase 2s+1
+      if (s + 2 < k_tiles) {
+        issue_a(s + 2);
+        issue_w(s + 2);
+      }
+      bf16x8 wf[4][2], af[4][4];
+      memory_phase(s, wf, af);
+      // A0(s+1) and W2(s+1), read by group 0 in phase 2s+2, have landed
+      wait_items(s + 2 < k_tiles ? 2 : 0);
+      phase_barrier();  // phase 2s+2
+      mfma_phase(wf, af);
+    }
   }
-  if (loader) phase_barrier();
 
   // acc[i][j][4*g + e] is C[m, n] with
-  //   m = m0 + wm*128 + j*32 + lane%32,  n = n0 + wn*64 + i*32 + 8*g + 4*(lane/32) + e.
+  //   m = m0 + grp*128 + j*32 + lane%32,  n = n0 + wq*64 + i*32 + 8*g + 4*(lane/32) + e.
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t m = m0 + wm * 128 + j * 32 + (lane % 32);
+    const int64_t m = m0 + grp * 128 + j * 32 + (lane % 32);
     if (m >= p.m) continue;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 64 + i * 32 + 8 * g + 4 * hi;
+        const int n = n0 + wq * 64 + i * 32 + 8 * g + 4 * hi;
         if (n >= p.n) continue;
         float y[4];
 #pragma unroll

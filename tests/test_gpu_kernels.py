@@ -53,12 +53,13 @@ def test_linear_epilogues(M, N, K, epi):
 
 
 # Shapes with M >= 1024, N >= 256 and K >= 256 run the large-tile kernel
-# (256 x 256 workgroup tiles, 64-wide K slices streamed into two LDS stages):
-# ragged M and N, an even and an odd number of K slices, every epilogue,
-# bitwise-equal reruns.  (Smaller K falls to the small-tile kernel: the
+# (256 x 256 workgroup tiles, 64-wide K slices streamed through a 3-stage W
+# ring and 2-stage A rings): ragged M and N, 4 to 8 K slices (every residue of
+# the slice count modulo both ring depths), every epilogue, bitwise-equal
+# reruns.  (Smaller K falls to the small-tile kernel: the
 # (1031, 264, 64) shape checks that routing.)
 @pytest.mark.parametrize("M,N,K", [(1100, 520, 256), (1031, 264, 384), (2304, 512, 320),
-                                   (1031, 264, 64)])
+                                   (1100, 520, 448), (2304, 512, 512), (1031, 264, 64)])
 @pytest.mark.parametrize("epi", ["bf16", "gelu", "f32", "gated", "res"])
 def test_linear_large_tiles(M, N, K, epi):
     a, w, b = _gemm_case(200 + M + K, M, N, K)
