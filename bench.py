@@ -75,6 +75,9 @@ def parse():
     p.add_argument("--traffic-probe", action="store_true",
                    help="only launch c3 joint attention --steps times and a plain 1 GiB copy "
                         "--steps times (for hardware-counter runs), print nothing else")
+    p.add_argument("--hbm-probe", action="store_true",
+                   help="only launch the bandwidth-bound kernels at their workload sizes --steps "
+                        "times each and a plain 1 GiB copy --steps times (for counter runs)")
     p.add_argument("--gemm-only", action="store_true",
                    help="time only the block's GEMMs (ours and hipBLASLt) and print them")
     p.add_argument("--cpu-rows", type=int, default=64,
@@ -114,6 +117,83 @@ def timed(fn, reps, stream):
     stop.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / reps
+
+
+class ClockSampler:
+    """Samples the GPU's current shader clock (the starred level of the
+    driver's pp_dpm_sclk) every few ms on a background thread while a timed
+    region runs; the MI355X runs below its 2.4 GHz peak under load (power
+    limit), which the roofline fractions against the nominal peak include."""
+
+    def __init__(self, period_s=0.005):
+        import glob
+        self.path = next(iter(sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))), None)
+        self.period = period_s
+        self.samples = []
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().split("M")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def __enter__(self):
+        import threading
+        self.samples = []
+        self._stop = threading.Event()
+        if self.path:
+            def run():
+                while not self._stop.is_set():
+                    v = self._read()
+                    if v is not None:
+                        self.samples.append(v)
+                    self._stop.wait(self.period)
+            self._t = threading.Thread(target=run, daemon=True)
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path:
+            self._t.join()
+
+    def summary(self):
+        import numpy as np
+        busy = [v for v in self.samples if v >= 500]  # drop idle readings between launches
+        if not busy:
+            return None
+        a = np.asarray(busy, dtype=np.float64)
+        return {"median_mhz": int(np.median(a)), "p10_mhz": int(np.percentile(a, 10)),
+                "p90_mhz": int(np.percentile(a, 90)), "samples": len(busy)}
+
+
+def timed_stats(fn, reps, stream, drop_first=False):
+    """Per-call ms of `fn` over `reps` back-to-back calls (a HIP event between
+    consecutive calls on the launch stream): mean, median, p10, p90 (of the
+    calls after the first with drop_first), plus the shader clock sampled
+    while they ran."""
+    import numpy as np
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    with ClockSampler() as clk:
+        ev[0].record(stream)
+        for i in range(reps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+    per = np.asarray([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
+    total = ev[0].elapsed_time(ev[reps])
+    if drop_first:
+        per = per[1:]
+    return {"ms": round(total / reps, 4), "median_ms": round(float(np.median(per)), 4),
+            "p10_ms": round(float(np.percentile(per, 10)), 4),
+            "p90_ms": round(float(np.percentile(per, 90)), 4), "reps": reps,
+            "clock": clk.summary()}
 
 
 def cpu_baseline(shape, model, n_rows):
@@ -181,6 +261,94 @@ def traffic_probe(steps):
     torch.cuda.synchronize()
     print(f"[traffic-probe] {steps} attention launches + {steps} copies of 1 GiB done",
           file=sys.stderr, flush=True)
+
+
+HBM_KERNELS = ("adaln", "qk_rmsnorm_rope", "merge5", "change_score", "modulation_gemv", "euler_c5")
+
+
+def hbm_probe(steps, reps=None):
+    """The bandwidth-bound kernels at their c3 (Euler: c5) sizes, each
+    launched `steps` times, then a plain device copy of exactly 1 GiB read +
+    1 GiB written (the counter calibration).  With `reps`, time each kernel
+    (HIP events, mean of `reps` calls) and return algorithmic bytes and GB/s.
+    Algorithmic bytes per launch:
+      adaLN: fp32 x read + bf16 h written, 6 B per element of [33272, 5120];
+      Q/K RMSNorm + RoPE: q and k read and written in place, bf16, 8 B per
+        (q, k) element pair of [33272, 5120];
+      merge of 5 partials: 5 fp32 outputs read + bf16 written per element
+        ((4*5 + 2) B) plus 5 fp32 LSE per (row, head);
+      change score with update: bf16 current read, saved read and written
+        (6 B per element of [33272, 5120]);
+      modulation matrix-vector (one timestep row through the [30720, 5120]
+        modulation projection): the bf16 weight read once, 2 B per element;
+      CFG + Euler at the c5 latent (4096 x 64): v_c, v_u bf16 read, x fp32
+        read and written, 12 B per element."""
+    import torch
+
+    import diffusion_transformer_denoising_dit_amd as D
+    from synthetic import configs as C
+    blk = C.C3_STEP.block
+    M, HD = blk.batch * blk.n_tok, blk.hidden
+    g = torch.Generator("cuda").manual_seed(21)
+
+    def rnd(*shape, std=1.0):
+        return (torch.randn(shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+
+    x = torch.randn((M, HD), generator=g, device="cuda")
+    h = torch.empty((M, HD), dtype=torch.bfloat16, device="cuda")
+    mod = rnd(6, HD, std=0.1)
+    qkv = rnd(M, 3 * HD)
+    gq, gk = rnd(HD, std=0.02) + 1, rnd(HD, std=0.02) + 1
+    bdesc = D.block_desc(blk, [226], 0)
+    P = 5
+    outs = [torch.randn((M, HD), generator=g, device="cuda") for _ in range(P)]
+    lses = [torch.randn((blk.batch, blk.heads, blk.n_tok), generator=g, device="cuda") for _ in range(P)]
+    o = torch.empty((M, HD), dtype=torch.bfloat16, device="cuda")
+    feat = rnd(M * HD)
+    saved = rnd(M * HD)
+    sws = torch.empty(D.dit_change_score_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    score = torch.zeros(1, device="cuda")
+    wmod, bmod = rnd(6 * HD, HD, std=0.02), rnd(6 * HD, std=0.02)
+    srow, mrow = rnd(1, HD), torch.empty((1, 6 * HD), dtype=torch.bfloat16, device="cuda")
+    n_lat = 4096 * 64
+    vc, vu = rnd(n_lat), rnd(n_lat)
+    xl = torch.zeros(n_lat, device="cuda")
+    kern = {
+        "adaln": (lambda: D.dit_adaln_modulate(x, M, HD, blk.n_tok, mod[0], mod[1], 0, 1e-6, h),
+                  6.0 * M * HD),
+        "qk_rmsnorm_rope": (lambda: D.dit_qk_rmsnorm_rope(bdesc, qkv, 3 * HD, gq, gk), 8.0 * M * HD),
+        "merge5": (lambda: D.dit_attention_merge(blk.batch, blk.n_tok, blk.heads, blk.head_dim, outs,
+                                                 HD, lses, o, HD),
+                   (4.0 * P + 2) * M * HD + 4.0 * P * blk.batch * blk.heads * blk.n_tok),
+        "change_score": (lambda: D.dit_change_score(feat, saved, D.DTYPE_BF16, M * HD, 1, score, sws,
+                                                    sws.numel()), 6.0 * M * HD),
+        "modulation_gemv": (lambda: D.dit_linear(srow, HD, wmod, bmod, 1, 6 * HD, HD, D.EPI_BF16,
+                                                 mrow, 6 * HD), 2.0 * 6 * HD * HD),
+        "euler_c5": (lambda: D.dit_euler_step(xl, vc, vu, n_lat, 5.0, 0.5, 0.5 - 1.0 / 30),
+                     12.0 * n_lat),
+    }
+    result = {}
+    for name in HBM_KERNELS:
+        fn, nbytes = kern[name]
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        if reps:
+            ms = timed(fn, reps, torch.cuda.current_stream())
+            result[name] = {"us": round(ms * 1e3, 2), "algorithmic_bytes": int(nbytes),
+                            "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 8e12, 4)}
+    del x, h, qkv, outs, lses, o, feat, saved, wmod
+    torch.cuda.empty_cache()
+    if not reps:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[hbm-probe] {len(HBM_KERNELS)} kernels x {steps} launches + {steps} copies of 1 GiB "
+              "done", file=sys.stderr, flush=True)
+    return result
 
 
 def block_gemms(reps, stream):
@@ -355,11 +523,13 @@ def other_configs(reps, stream):
         D.dit_joint_attention(adesc, q, k, v, HD, o, HD)
 
     attn()
-    ms = timed(attn, max(3, reps // 2), stream)
+    st = timed_stats(attn, max(3, reps // 2), stream)
+    ms = st["ms"]
     fl = attention_flops(s.n_tok, s.n_vis + 300, s.heads, s.head_dim, s.batch)
     out["c4_attention"] = {"ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
                            "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                           "algorithmic_tflop": round(fl / 1e12, 3), "txt_valid": [300]}
+                           "algorithmic_tflop": round(fl / 1e12, 3), "txt_valid": [300],
+                           "timing": st}
     del q, k, v, o
 
     shape = C.C5
@@ -387,10 +557,36 @@ def other_configs(reps, stream):
             D.dit_denoise_step(desc, weights, lat, sig[i], sig[i + 1], shape.guidance, ws, nb)
 
     loop(2)
-    ms = timed(lambda: loop(shape.steps), 1, stream) / shape.steps
+    counter = {"i": 0}
+
+    def one_step():
+        i = counter["i"]
+        D.dit_denoise_step(desc, weights, lat, sig[i], sig[i + 1], shape.guidance, ws, nb)
+        counter["i"] += 1
+
+    # one 30-step loop, an event between steps; median and percentiles over
+    # the steps after the first (the pages' method: the first step is dropped)
+    st = timed_stats(one_step, shape.steps, stream, drop_first=True)
+    ms = st["ms"]
     assert torch.isfinite(lat).all(), "non-finite latent in the denoising loop"
+
+    # the CFG + Euler update alone at this latent size (launch-latency bound)
+    n_lat = b.n_vis * Cl
+    vc, vu = rnd(n_lat), rnd(n_lat)
+    xe = torch.zeros(n_lat, dtype=torch.float32, device="cuda")
+
+    def euler():
+        D.dit_euler_step(xe, vc, vu, n_lat, shape.guidance, 0.5, 0.5 - 1.0 / 30)
+
+    euler()
+    ms_e = timed(euler, 200, stream)
+    out["euler_step"] = {"us": round(ms_e * 1e3, 2), "n": n_lat, "cfg": True,
+                         "gbps": round(12 * n_lat / (ms_e * 1e-3) / 1e9, 1),
+                         "note": "mean per call over 200 back-to-back calls (launch-latency "
+                                 "bound: 12 B/element, 3.1 MB)"}
     fl = shape.depth * block_flops(b, valid)
     out["c5_loop"] = {"ms_per_step": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                      "timing": st,
                       "algorithmic_tflop_per_step": round(fl / 1e12, 3),
                       "steps": shape.steps, "depth": shape.depth, "guidance": shape.guidance,
                       "txt_valid": valid,
@@ -467,6 +663,9 @@ def main():
     if args.traffic_probe:
         traffic_probe(args.steps)
         return
+    if args.hbm_probe:
+        hbm_probe(args.steps)
+        return
     if args.gemm_only:
         print(json.dumps({"block_gemms": block_gemms(max(3, args.steps), torch.cuda.current_stream())}),
               flush=True)
@@ -503,7 +702,8 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ms_step = timed(step, args.steps, stream)
+    st_step = timed_stats(step, args.steps, stream)
+    ms_step = st_step["ms"]
     assert torch.isfinite(lat).all(), "non-finite latent"
 
     # step caching at the same shape: the block-0 probe, a cached (skipped)
@@ -572,7 +772,8 @@ def main():
         D.dit_block_forward(bdesc, bw, mod, x, bws, bws_bytes)
 
     block()
-    ms_block = timed(block, max(3, args.steps), stream)
+    st_block = timed_stats(block, max(3, args.steps), stream)
+    ms_block = st_block["ms"]
 
     # joint attention alone, q/k/v as column blocks of one [N, 3*H*d] buffer (the block layout)
     HD = blk.hidden
@@ -585,7 +786,15 @@ def main():
         D.dit_joint_attention(adesc, qkv, qkv[..., HD:], qkv[..., 2 * HD:], 3 * HD, o, HD)
 
     attn()
-    ms_attn = timed(attn, max(5, args.steps), stream)
+    st_attn = timed_stats(attn, max(5, args.steps), stream)
+    ms_attn = st_attn["ms"]
+    # peaked softmax rows: q scaled by 4 (exact in bf16), so the running
+    # maxima move more often and the O/l rescale is skipped less often
+    qkv[..., :HD].mul_(4.0)
+    attn()
+    st_attn_peaked = timed_stats(attn, max(5, args.steps), stream)
+    qkv[..., :HD].mul_(0.25)
+    attn()  # o back to the unscaled inputs' output (the split comparison reads it)
     valid = [int(v) for v in inp.txt_valid]
     a_flop = sum(attention_flops(blk.n_tok, blk.n_vis + L, blk.heads, blk.head_dim) for L in valid)
     a_dense = attention_flops(blk.n_tok, blk.n_tok, blk.heads, blk.head_dim) * blk.batch
@@ -627,6 +836,7 @@ def main():
     del p_out, p_lse, o_split
 
     gemms = block_gemms(max(3, args.steps // 2), stream)
+    hbm = hbm_probe(2, reps=max(10, args.steps))
     mm = mmdit_blocks(max(5, args.steps), stream)
     wan = wan_block(max(3, args.steps // 2), stream)
     others = other_configs(args.steps, stream)
@@ -653,12 +863,19 @@ def main():
         },
         "block_ms": round(ms_block, 3),
         "block_tflops": round(b_flop / (ms_block * 1e-3) / 1e12, 1),
+        "timing": {"step": st_step, "block": st_block},
         "attention": {
             "ms": round(ms_attn, 3),
             "tflops": round(a_tflops, 1),
             "frac_bf16_peak": round(a_tflops / PEAK_BF16_TFLOPS, 4),
             "algorithmic_tflop": round(a_flop / 1e12, 3),
             "dense_tflop": round(a_dense / 1e12, 3),
+            "inputs": "q, k, v N(0,1) bf16 (nearly flat softmax rows)",
+            "timing": st_attn,
+            "peaked": {"inputs": "q x 4 (peaked softmax rows)", "timing": st_attn_peaked,
+                       "tflops": round(a_flop / (st_attn_peaked["ms"] * 1e-3) / 1e12, 1),
+                       "frac_bf16_peak": round(a_flop / (st_attn_peaked["ms"] * 1e-3) / 1e12
+                                               / PEAK_BF16_TFLOPS, 4)},
         },
         "split_attention": {
             "partials": len(segs),
@@ -678,6 +895,7 @@ def main():
             "steps": shape.steps,
         },
         "block_gemms": gemms,
+        "hbm_kernels": hbm,
         "mmdit": mm,
         "wan_block": wan,
         "other_configs": others,
