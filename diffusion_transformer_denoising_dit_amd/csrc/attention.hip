@@ -16,8 +16,11 @@
 //    The waves form two groups that alternate between an MFMA phase and a
 //    softmax phase, one phase apart, with a workgroup barrier at every phase
 //    boundary: while one wave of a SIMD multiplies, the other exponentiates.
-//    (VALU work in another wave hides behind MFMAs; in the same wave it
-//    mostly does not.)
+//    The softmax work of a tile is split: the max, the running-max update
+//    and half of the exponentials in the softmax phase, the tile max and the
+//    other half of the exponentials between the MFMAs of the wave's own MFMA
+//    phase (a few independent VALU instructions per MFMA cost no MFMA time
+//    there; long dependent chains would).
 //  * K and V tiles (64 keys) stream from HBM/L2 straight into LDS with
 //    global_load_lds_dwordx4 (no VGPR staging) through a 4-stage ring, two
 //    tiles ahead of the math, issued by the group entering its softmax
@@ -152,11 +155,11 @@ struct WaveState {
   bf16x8 qf[kKS];     // Q fragments: Q[q][16*ks + 8*hi .. +7], q = lane%32
   f32x16 o[kDB];      // O^T accumulators: o[db][4g + e] = O[q][32db + 8g + 4*hi + e]
   f32x16 s[2];        // S^T of one tile: s[t][4g + e] = score of key 32t + 8g + 4*hi + e
+  f32x16 sh;          // s[1] of the last softmax'ed tile as s*c - m: exponentiated in the next MFMA phase
   bf16x8 pf[4];       // p of one tile as the B operand of four 16-key value steps
   float m_run;        // running max of the scaled scores (log2 domain)
-  float alpha;        // rescale of O still owed for the last raise of m_run
+  float m_tile;       // max of the scaled scores of the tile in s (this lane's query)
   float l_run;        // this lane's partial sum of p
-  bool rescale;       // wave-uniform: the last softmax phase raised m_run (O owes alpha)
   int k_off[kKS];     // K fragment byte offsets within a stage (row lane%32)
   int v_off[2][kDB];  // V^T transposing-read byte offsets (rows 8g + 4*hi + s16/4)
 };
@@ -181,60 +184,93 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 // MFMA phase: S^T of key tile j+1 (sK = its K stage; absent after the last
-// tile), then O^T = alpha O^T + V^T P^T for tile j (sV = its V stage; absent
-// before the first tile).  LDS reads and MFMAs, plus the O rescale owed by
-// the softmax phase, a few independent multiplies after each score MFMA so
-// the matrix pipe keeps its queue (as one block before the value MFMAs it
-// idled the pipe for the whole block).  Fragment reads run a fixed number of
-// steps ahead of their MFMA (scheduling fences keep the compiler from hoisting
-// all 32 of them, which would cost 128 VGPRs).
+// tile), then O^T += V^T P^T for tile j (sV = its V stage; absent before the
+// first tile).  LDS reads and MFMAs, with independent VALU work of this wave
+// placed between them, where it issues while the matrix pipe runs (measured
+// on gfx950: up to ~4 FP32 VALU instructions per 32x32x16 MFMA cost no MFMA
+// time): after each score MFMA one exponential (with its row sum and bf16
+// packing) of the second half of tile j, and after each value MFMA one step
+// of tile j+1's max.  Fragment reads run a fixed number of steps ahead of
+// their MFMA (scheduling fences keep the compiler from hoisting all 32 of
+// them, which would cost 128 VGPRs).
 template <int D, bool kPVPart, bool kQKPart>
-__device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, const char* sV) {
+__device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, const char* sV, float c) {
   using T = Tile<D>;
   using W = WaveState<D>;
   constexpr int kPV = 4 * W::kDB;  // value steps: (u, db)
   constexpr int kQK = 2 * W::kKS;  // score steps: (ks, t), t fastest: two accumulator chains
   constexpr int kAhead = 2;  // fragment reads in flight ahead of their MFMA
-  // The O rescale owed by the last softmax phase (skipped, wave-uniformly,
-  // when no running max of the wave moved) is spread over the score MFMAs,
-  // kDB*16/kQK multiplies after each, so the matrix pipe never waits for it.
-  constexpr int kMulsPerStep = W::kDB * 16 / kQK;
-  auto rescale_part = [&](int i) {
-#pragma unroll
-    for (int n = 0; n < kMulsPerStep; ++n) {
-      const int idx = i * kMulsPerStep + n;
-      st.o[idx / 16][idx % 16] *= st.alpha;
+  // The second half of the last softmax'ed tile (keys 32..63, held in sh as
+  // s*c - m) is exponentiated here, between the MFMAs -- its exponentials,
+  // row sums and bf16 packing are independent VALU work that issues while
+  // the matrix pipe runs -- and becomes pf[2], pf[3] before the value MFMAs
+  // that read them.  (With a value part there is always such a half.)
+  float ep[16];
+  float lp0, lp1;
+  auto finish_part = [&](int i) {
+    ep[i] = __builtin_amdgcn_exp2f(st.sh[i]);
+    if (i % 2 == 1) {
+      lp0 = i == 1 ? ep[0] : lp0 + ep[i - 1];
+      lp1 = i == 1 ? ep[1] : lp1 + ep[i];
+      u32x4 w = __builtin_bit_cast(u32x4, st.pf[2 + i / 8]);
+      w[(i % 8) / 2] = pack_bf16x2(ep[i - 1], ep[i]);
+      st.pf[2 + i / 8] = __builtin_bit_cast(bf16x8, w);
     }
   };
+  static_assert(kQK == 16 || !kQKPart || D != 128, "one pending score per score MFMA at head_dim 128");
   if constexpr (kQKPart) {
     auto kread = [&](int i) {
       const int t = i % 2, ks = i / 2;
       return *reinterpret_cast<const bf16x8*>(sK + 32 * t * T::kRowBytes + st.k_off[ks]);
     };
-    auto qk_loop = [&](auto with_rescale) {
-      bf16x8 kf[kQK];
+    bf16x8 kf[kQK];
 #pragma unroll
-      for (int i = 0; i < kAhead; ++i) kf[i] = kread(i);
-      const f32x16 zero = {};  // first step of each chain: an inline-constant 0 accumulator
+    for (int i = 0; i < kAhead; ++i) kf[i] = kread(i);
+    const f32x16 zero = {};  // first step of each chain: an inline-constant 0 accumulator
 #pragma unroll
-      for (int i = 0; i < kQK; ++i) {
-        if (i + kAhead < kQK) kf[i + kAhead] = kread(i + kAhead);
-        __builtin_amdgcn_sched_barrier(0);
-        st.s[i % 2] = mfma32x32x16(kf[i], st.qf[i / 2], i < 2 ? zero : st.s[i % 2]);
-        if constexpr (decltype(with_rescale)::value) rescale_part(i);
+    for (int i = 0; i < kQK; ++i) {
+      if (i + kAhead < kQK) kf[i + kAhead] = kread(i + kAhead);
+      __builtin_amdgcn_sched_barrier(0);
+      st.s[i % 2] = mfma32x32x16(kf[i], st.qf[i / 2], i < 2 ? zero : st.s[i % 2]);
+      if constexpr (kPVPart) {
+        // 16 pending scores over kQK score MFMAs
+        constexpr int kPer = 16 / kQK;
+#pragma unroll
+        for (int n = 0; n < kPer; ++n) finish_part(i * kPer + n);
       }
-    };
-    if (kPVPart && st.rescale)
-      qk_loop(std::true_type{});
-    else
-      qk_loop(std::false_type{});
+    }
   } else if constexpr (kPVPart) {
-    if (st.rescale) {
 #pragma unroll
-      for (int i = 0; i < kQK; ++i) rescale_part(i);
+    for (int i = 0; i < 16; ++i) finish_part(i);
+  }
+  // The new tile's max, 32 scores -> 1 in 16 v_max3 on four independent
+  // chains, one step after each value MFMA (there the wave has issue slots
+  // to spare); the softmax phase starts from it.  The tile that holds the
+  // bound needs no mask for this: its key rows past the bound were loaded
+  // as copies of the last valid key's row, so those scores repeat a valid
+  // one and leave the max unchanged (the softmax phase masks them before
+  // exponentiating).
+  float mx[4];
+  auto max_step = [&](int i) {
+    const int c4 = i % 4, k = i / 4;
+    const int t = c4 / 2, r0 = 8 * (c4 % 2);
+    if (k == 0) mx[c4] = vmax3(st.s[t][r0], st.s[t][r0 + 1], st.s[t][r0 + 2]);
+    else if (k == 1) mx[c4] = vmax3(mx[c4], st.s[t][r0 + 3], st.s[t][r0 + 4]);
+    else if (k == 2) mx[c4] = vmax3(mx[c4], st.s[t][r0 + 5], st.s[t][r0 + 6]);
+    else mx[c4] = vmax3(mx[c4], st.s[t][r0 + 7], st.s[t][r0 + 7]);
+    asm volatile("" : "+v"(mx[c4]));  // keep the step here, not sunk to the end of the phase
+  };
+  if constexpr (kQKPart) {
+    if constexpr (!kPVPart) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) max_step(i);
     }
   }
   if constexpr (kPVPart) {
+    st.l_run += lp0 + lp1;
+    // keep the sums here, between the MFMAs, rather than let the compiler
+    // sink them into the next softmax phase where l is read
+    asm volatile("" : "+v"(st.l_run));
     auto vread = [&](int i) {
       const int u = i / W::kDB, db = i % W::kDB;
       const char* vrow = sV + 16 * u * T::kRowBytes;
@@ -250,14 +286,25 @@ __device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, con
       if (i + kAhead < kPV) vf[i + kAhead] = vread(i + kAhead);
       __builtin_amdgcn_sched_barrier(0);
       st.o[i % W::kDB] = mfma32x32x16(vf[i], st.pf[i / W::kDB], st.o[i % W::kDB]);
+      if constexpr (kQKPart) {
+        constexpr int kPer = 16 / kPV;
+#pragma unroll
+        for (int n = 0; n < kPer; ++n) max_step(i * kPer + n);
+      }
     }
+  }
+  if constexpr (kQKPart) {
+    // c > 0 keeps the order
+    st.m_tile = max_halves(vmax3(mx[0], mx[1], vmax3(mx[2], mx[3], mx[3]))) * c;
   }
 }
 
-// Softmax phase for key tile j (keys j0 .. j0+63): mask past the bound (only
-// the tile that holds it), tile max, update of the running max with the
-// rescale of l (O's is owed to the next MFMA phase), p = exp2(s*c - m) into
-// the running sum and, rounded to bf16, into pf.  VALU only.
+// Softmax phase for key tile j (keys j0 .. j0+63), whose max the MFMA phase
+// already took: mask past the bound (only the tile that holds it), update of
+// the running max with the rescale of l and O when it rose, p = exp2(s*c - m)
+// of the first 32 keys into the running sum and, rounded to bf16, into
+// pf[0], pf[1]; the other 32 keys only as s*c - m (the next MFMA phase
+// exponentiates them).  VALU only.
 template <int D>
 __device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_valid, int hi, float c) {
   using W = WaveState<D>;
@@ -268,37 +315,33 @@ __device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_va
       for (int r = 0; r < 16; ++r)
         if (j0 + 32 * t + 8 * (r / 4) + 4 * hi + (r % 4) >= n_valid) st.s[t][r] = -INFINITY;
   }
-  // 32 scores -> 1 in 16 v_max3 (four independent chains)
-  float m[4];
-#pragma unroll
-  for (int c4 = 0; c4 < 4; ++c4) {
-    const int t = c4 / 2, r0 = 8 * (c4 % 2);
-    float x = vmax3(st.s[t][r0], st.s[t][r0 + 1], st.s[t][r0 + 2]);
-    x = vmax3(x, st.s[t][r0 + 3], st.s[t][r0 + 4]);
-    x = vmax3(x, st.s[t][r0 + 5], st.s[t][r0 + 6]);
-    m[c4] = vmax3(x, st.s[t][r0 + 7], st.s[t][r0 + 7]);
-  }
   // Running max.  When no query of the wave sees a score above its running
-  // max, alpha would be exactly 1: the rescale of l here and of O in the next
-  // MFMA phase are skipped, wave-uniformly (after the first tiles most tiles
-  // raise no max), and the result is bitwise the same as rescaling by 1.
-  const float m_tile = max_halves(vmax3(m[0], m[1], vmax3(m[2], m[3], m[3]))) * c;  // c > 0 keeps the order
-  st.rescale = __builtin_amdgcn_ballot_w64(m_tile > st.m_run) != 0;
-  if (st.rescale) {
+  // max, alpha would be exactly 1: the rescale of l and O is skipped,
+  // wave-uniformly (after the first tiles most tiles raise no max), and the
+  // result is bitwise the same as rescaling by 1.
+  const float m_tile = st.m_tile;
+  if (__builtin_amdgcn_ballot_w64(m_tile > st.m_run) != 0) {
     const float m_new = vmax3(st.m_run, m_tile, m_tile);
-    st.alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
     st.m_run = m_new;
-    st.l_run *= st.alpha;
+    st.l_run *= alpha;
+    // O holds the value sums up to the previous tile; the next MFMA phase
+    // adds this tile's, relative to the new maximum
+#pragma unroll
+    for (int db = 0; db < W::kDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.o[db][e] *= alpha;
   }
   const float nm = -st.m_run;
+  // keys 0..31 of the tile: exponentiate, sum, pack into pf[0], pf[1]
   float l0, l1;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < 2; ++u) {
     u32x4 w;
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
-      const float e0 = __builtin_amdgcn_exp2f(fmaf(st.s[u / 2][8 * (u % 2) + i], c, nm));
-      const float e1 = __builtin_amdgcn_exp2f(fmaf(st.s[u / 2][8 * (u % 2) + i + 1], c, nm));
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(st.s[0][8 * u + i], c, nm));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(st.s[0][8 * u + i + 1], c, nm));
       l0 = (u == 0 && i == 0) ? e0 : l0 + e0;
       l1 = (u == 0 && i == 0) ? e1 : l1 + e1;
       w[i / 2] = pack_bf16x2(e0, e1);
@@ -306,6 +349,9 @@ __device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_va
     st.pf[u] = __builtin_bit_cast(bf16x8, w);
   }
   st.l_run += l0 + l1;
+  // keys 32..63: only s*c - m here; the next MFMA phase exponentiates them
+#pragma unroll
+  for (int r = 0; r < 16; ++r) st.sh[r] = fmaf(st.s[1][r], c, nm);
 }
 
 // Issue the loads of tile j into its ring slot (clamping rows past the last
@@ -430,8 +476,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     for (int e = 0; e < 16; ++e) st.o[i][e] = 0.f;
   st.m_run = -INFINITY;
   st.l_run = 0.f;
-  st.alpha = 1.f;
-  st.rescale = false;
   // LDS read offsets.  A K fragment row is lane%32 (+32t) and a V^T read row
   // is 16u + 8g + 4*hi + s16/4; the swizzle depends only on row % 16, so t
   // and u only add immediate row offsets.
@@ -488,21 +532,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   if (!a_grp) phase_barrier(true, 0);
   phase_barrier(a_grp, 0);
   mfma_prio(true);
-  mfma_phase<D, false, true>(st, stage(0), nullptr);
+  mfma_phase<D, false, true>(st, stage(0), nullptr, c);
   mfma_prio(false);
   phase_barrier(!a_grp, 1);
   softmax_phase<D>(st, 0, n_valid, hi, c);
   for (int k = 0; k + 1 < n_tiles; ++k) {
     phase_barrier(a_grp, k + 1);
     mfma_prio(true);
-    mfma_phase<D, true, true>(st, stage(k + 1), stage(k) + T::kBytes);
+    mfma_phase<D, true, true>(st, stage(k + 1), stage(k) + T::kBytes, c);
     mfma_prio(false);
     phase_barrier(!a_grp, k + 2);
     softmax_phase<D>(st, (k + 1) * kBN, n_valid, hi, c);
   }
   phase_barrier(a_grp, n_tiles);
   mfma_prio(true);
-  mfma_phase<D, true, false>(st, nullptr, stage(n_tiles - 1) + T::kBytes);
+  mfma_phase<D, true, false>(st, nullptr, stage(n_tiles - 1) + T::kBytes, c);
   mfma_prio(false);
   if (a_grp) phase_barrier(false, 0);
 
