@@ -101,6 +101,109 @@ __device__ __forceinline__ void store_epilogue(const GemmParams& p, int64_t m, i
   }
 }
 
+// The epilogue of one wave's 128 (tokens) x 64 (features) block of a
+// 256 x 256 tile, acc[i][j][4*g + e] = C[m, n] with m = m_base + 32j +
+// lane%32 and n = n_base + 32i + 8g + 4*(lane/32) + e.  The loads it needs
+// are issued in batches before their uses -- the bias of all 8 feature
+// groups once, then per 32-row block the residual (and gate) values of all
+// 8 groups -- so a block costs one memory round trip rather than one per
+// group.  p.n is a multiple of 8, so whether a group's 8 features are in
+// range does not depend on the lane half.
+template <int EPI, bool kChecked>
+__device__ __forceinline__ void tile_epilogue_impl(const GemmParams& p, const f32x16 (&acc)[2][4],
+                                                   int64_t m_base, int n_base, int lane) {
+  constexpr bool kResid = EPI == EPI_GATED || EPI == EPI_RES;
+  const int hi = lane / 32;
+  u32x2 bias[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) bias[i][g] = u32x2{0u, 0u};
+  if (p.bias) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n_base + i * 32 + 8 * g + 4 * hi;
+        if (!kChecked || n < p.n) bias[i][g] = *reinterpret_cast<const u32x2*>(p.bias + n);
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t m = m_base + j * 32 + (lane % 32);
+    if (kChecked && m >= p.m) continue;
+    const int64_t crow = c_row_offset(p, m);
+    f32x4 xr[2][4];
+    u32x2 gt[2][4];
+    if constexpr (kResid) {
+      const uint16_t* grow = EPI == EPI_GATED ? p.gate + (m / p.gate_rows) * p.gate_stride : nullptr;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n_base + i * 32 + 8 * g + 4 * hi;
+          if (!kChecked || n < p.n) {
+            xr[i][g] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.out) + crow + n);
+            if constexpr (EPI == EPI_GATED) gt[i][g] = *reinterpret_cast<const u32x2*>(grow + n);
+          }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n_base + i * 32 + 8 * g + 4 * hi;
+        if (kChecked && n >= p.n) continue;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * g + e];
+        y[0] += __uint_as_float(bias[i][g][0] << 16);
+        y[1] += __uint_as_float(bias[i][g][0] & 0xffff0000u);
+        y[2] += __uint_as_float(bias[i][g][1] << 16);
+        y[3] += __uint_as_float(bias[i][g][1] & 0xffff0000u);
+        if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = 0.5f * y[e] * (1.f + erff(y[e] * 0.70710678118654752f));
+        } else if constexpr (EPI == EPI_SILU) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = y[e] / (1.f + expf(-y[e]));
+        }
+        if constexpr (EPI == EPI_F32 || kResid) {
+          f32x4 o;
+          if constexpr (EPI == EPI_RES) {
+            o = xr[i][g];
+            o[0] += y[0]; o[1] += y[1]; o[2] += y[2]; o[3] += y[3];
+          } else if constexpr (EPI == EPI_GATED) {
+            o = xr[i][g];
+            o[0] += __uint_as_float(gt[i][g][0] << 16) * y[0];
+            o[1] += __uint_as_float(gt[i][g][0] & 0xffff0000u) * y[1];
+            o[2] += __uint_as_float(gt[i][g][1] << 16) * y[2];
+            o[3] += __uint_as_float(gt[i][g][1] & 0xffff0000u) * y[3];
+          } else {
+            o[0] = y[0]; o[1] = y[1]; o[2] = y[2]; o[3] = y[3];
+          }
+          *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + crow + n) = o;
+        } else {
+          u32x2 o;
+          o[0] = pack_bf16x2(y[0], y[1]);
+          o[1] = pack_bf16x2(y[2], y[3]);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + crow + n) = o;
+        }
+      }
+  }
+}
+
+// Interior blocks (every row and feature in range, the common case) take a
+// branch-free path; edge blocks check each row and feature group.
+template <int EPI>
+__device__ __forceinline__ void tile_epilogue(const GemmParams& p, const f32x16 (&acc)[2][4],
+                                              int64_t m_base, int n_base, int lane) {
+  if (m_base + 128 <= p.m && n_base + 64 <= p.n)
+    tile_epilogue_impl<EPI, false>(p, acc, m_base, n_base, lane);
+  else
+    tile_epilogue_impl<EPI, true>(p, acc, m_base, n_base, lane);
+}
+
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[kTM * kLd];
@@ -454,24 +557,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
     }
   }
 
-  // acc[i][j][4*g + e] is C[m, n] with
-  //   m = m0 + grp*128 + j*32 + lane%32,  n = n0 + wq*64 + i*32 + 8*g + 4*(lane/32) + e.
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t m = m0 + grp * 128 + j * 32 + (lane % 32);
-    if (m >= p.m) continue;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wq * 64 + i * 32 + 8 * g + 4 * hi;
-        if (n >= p.n) continue;
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * g + e];
-        store_epilogue<EPI>(p, m, n, y);
-      }
-  }
+  tile_epilogue<EPI>(p, acc, m0 + grp * 128, n0 + wq * 64, lane);
 }
 
 }  // namespace big
