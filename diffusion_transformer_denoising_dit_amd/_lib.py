@@ -24,7 +24,8 @@ EXPORTED = (
     "dit_block_workspace_bytes", "dit_block_forward", "dit_euler_step",
     "dit_timestep_features", "dit_cast_f32_bf16", "dit_cast_bf16_f32", "dit_debug_positions",
     "dit_denoise_workspace_bytes", "dit_denoise_step",
-    "dit_change_score_workspace_bytes", "dit_change_score", "dit_cache_probe",
+    "dit_change_score_workspace_bytes", "dit_change_score", "dit_change_score_noalloc",
+    "dit_cache_probe",
     "dit_denoise_step_cached", "dit_cache_ctrl_init", "dit_cache_ctrl_decide",
     "dit_cache_ctrl_observe",
     "dit_double_block_workspace_bytes", "dit_double_block_forward",
@@ -163,6 +164,7 @@ def lib() -> ctypes.CDLL:
                                       f32, f32, vp, ctypes.c_size_t, vp]),
             "dit_change_score_workspace_bytes": (ctypes.c_size_t, []),
             "dit_change_score": (st, [vp, vp, i32, i64, i32, vp, vp, ctypes.c_size_t, vp]),
+            "dit_change_score_noalloc": (st, [vp, vp, i32, i64, i32, vp, vp]),
             "dit_cache_probe": (st, [ctypes.POINTER(ModelDesc), ctypes.POINTER(ModelWeights), vp, f32,
                                      vp, i32, vp, vp, ctypes.c_size_t, vp]),
             "dit_denoise_step_cached": (st, [ctypes.POINTER(ModelDesc), ctypes.POINTER(ModelWeights), vp,
@@ -380,6 +382,11 @@ def dit_change_score_workspace_bytes() -> int:
 def dit_change_score(cur, prev, dtype, n, update, score, workspace, workspace_bytes, stream=None):
     _check(lib().dit_change_score(_ptr(cur), _ptr(prev), dtype, n, int(update), _ptr(score),
                                   _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def dit_change_score_noalloc(cur, prev, dtype, n, update, score, stream=None):
+    _check(lib().dit_change_score_noalloc(_ptr(cur), _ptr(prev), dtype, n, int(update), _ptr(score),
+                                          _stream(stream)))
 
 
 def dit_cache_probe(desc, weights, latent, sigma, saved, have_saved, score, workspace,

@@ -1168,28 +1168,59 @@ dit_status dit_denoise_step(const dit_model_desc* desc, const dit_model_weights*
 
 size_t dit_change_score_workspace_bytes(void) { return dit::kScorePartialBytes; }
 
-dit_status dit_change_score(const void* cur, void* prev, int32_t dtype, int64_t n, int32_t update,
-                            float* score, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
+static_assert(DIT_CHANGE_SCORE_SCRATCH_BYTES == dit::kScorePartialBytes,
+              "the documented scratch size is the kernels' partial-sum size");
+
+// Checks shared by dit_change_score and dit_change_score_noalloc (the
+// workspace ones only when a workspace is passed).
+dit_status check_change_score(const void* cur, void* prev, int32_t dtype, int64_t n, int32_t update,
+                              float* score, const void* workspace, size_t workspace_bytes,
+                              bool has_workspace) {
   if (dtype != DIT_DTYPE_BF16 && dtype != DIT_DTYPE_F32)
     return fail(DIT_EINVAL, "dtype %d is neither DIT_DTYPE_BF16 nor DIT_DTYPE_F32", dtype);
   if (n < 1) return fail(DIT_EINVAL, "n %lld < 1", static_cast<long long>(n));
+  if (n > DIT_CHANGE_SCORE_MAX_N)
+    return fail(DIT_EINVAL, "n %lld > %lld", static_cast<long long>(n),
+                static_cast<long long>(DIT_CHANGE_SCORE_MAX_N));
   if (update != 0 && update != 1) return fail(DIT_EINVAL, "update must be 0 or 1");
-  if (!cur || !prev || !score || !workspace) return fail(DIT_EINVAL, "NULL cur, prev, score or workspace");
-  if (!aligned(cur, 16) || !aligned(prev, 16) || !aligned(score, 4) || !aligned(workspace, 16))
+  if (!cur || !prev || !score || (has_workspace && !workspace))
+    return fail(DIT_EINVAL, has_workspace ? "NULL cur, prev, score or workspace" : "NULL cur, prev or score");
+  if (!aligned(cur, 16) || !aligned(prev, 16) || !aligned(score, 4) ||
+      (has_workspace && !aligned(workspace, 16)))
     return fail(DIT_EINVAL, "cur, prev and workspace must be 16-byte aligned, score 4-byte");
-  if (workspace_bytes < dit::kScorePartialBytes)
+  if (has_workspace && workspace_bytes < dit::kScorePartialBytes)
     return fail(DIT_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, dit::kScorePartialBytes);
   const size_t bytes = static_cast<size_t>(n) * (dtype == DIT_DTYPE_BF16 ? 2 : 4);
   if (update && overlap(cur, bytes, prev, bytes))
     return fail(DIT_EINVAL, "cur and prev overlap (prev is overwritten)");
-  if (overlap(score, 4, cur, bytes) || overlap(score, 4, prev, bytes) ||
-      overlap(workspace, dit::kScorePartialBytes, cur, bytes) ||
-      overlap(workspace, dit::kScorePartialBytes, prev, bytes) ||
-      overlap(workspace, dit::kScorePartialBytes, score, 4))
-    return fail(DIT_EINVAL, "score or workspace overlaps an array");
+  if (overlap(score, 4, cur, bytes) || overlap(score, 4, prev, bytes))
+    return fail(DIT_EINVAL, "score overlaps an array");
+  if (has_workspace && (overlap(workspace, dit::kScorePartialBytes, cur, bytes) ||
+                        overlap(workspace, dit::kScorePartialBytes, prev, bytes) ||
+                        overlap(workspace, dit::kScorePartialBytes, score, 4)))
+    return fail(DIT_EINVAL, "workspace overlaps an array");
+  return DIT_OK;
+}
+
+dit_status dit_change_score(const void* cur, void* prev, int32_t dtype, int64_t n, int32_t update,
+                            float* score, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  dit_status st = check_change_score(cur, prev, dtype, n, update, score, workspace, workspace_bytes, true);
+  if (st != DIT_OK) return st;
   return hip_status(dit::launch_change_score(cur, prev, dtype == DIT_DTYPE_BF16, n, update != 0,
                                              static_cast<float*>(workspace), score, stream),
+                    "change-score launch");
+}
+
+dit_status dit_change_score_noalloc(const void* cur, void* prev, int32_t dtype, int64_t n,
+                                    int32_t update, float* score, hipStream_t stream) {
+  dit_status st = check_change_score(cur, prev, dtype, n, update, score, nullptr, 0, false);
+  if (st != DIT_OK) return st;
+  float* partials = nullptr;
+  st = hip_status(dit::change_score_scratch(&partials), "change-score scratch address");
+  if (st != DIT_OK) return st;
+  return hip_status(dit::launch_change_score(cur, prev, dtype == DIT_DTYPE_BF16, n, update != 0,
+                                             partials, score, stream),
                     "change-score launch");
 }
 

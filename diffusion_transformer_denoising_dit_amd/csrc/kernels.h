@@ -82,6 +82,9 @@ constexpr size_t kScorePartialBytes = 2 * kScoreBlocks * sizeof(float);
 // with update, prev <- cur in the same pass.
 hipError_t launch_change_score(const void* cur, void* prev, bool bf16, int64_t n, bool update,
                                float* partials, float* score, hipStream_t s);
+// Device address of the library's own partial-sum array on the current
+// device (kScorePartialBytes; shared by every call on that device).
+hipError_t change_score_scratch(float** out);
 // score = +inf (nothing to compare with).
 hipError_t launch_score_invalid(float* partials, float* score, hipStream_t s);
 // Full step (skip false): v = guided velocity, delta = v - prev and the change

@@ -12,6 +12,8 @@
 // at most kScoreBlocks workgroups, each thread owning a fixed set of 8-element
 // chunks, a fixed reduction tree inside the workgroup, per-workgroup partials
 // in a small workspace and one final workgroup adding them in double.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -282,6 +284,38 @@ hipError_t launch_change_score(const void* cur, void* prev, bool bf16, int64_t n
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(change_final_kernel, dim3(1), dim3(kThreads), 0, s, partials, blocks, 1, score);
   return hipGetLastError();
+}
+
+// Partial sums of the change score for callers that cannot allocate: a
+// file-scope device array, one copy per GPU, held until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host that name
+// is a stand-in, not a device address); it passes the address
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device on its first use and kept.  Every call on one GPU shares that
+// GPU's array: calls that overlap in time on one GPU race.
+static __device__ __align__(256) float scratch[2 * kScoreBlocks];
+static_assert(sizeof(scratch) == kScorePartialBytes, "scratch holds one pass's partial sums");
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t change_score_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_score_invalid(float* partials, float* score, hipStream_t s) {

@@ -445,11 +445,27 @@ typedef enum dit_dtype { DIT_DTYPE_BF16 = 0, DIT_DTYPE_F32 = 1 } dit_dtype;
  * pass (cur and prev must not overlap then).  The sum is deterministic: a
  * fixed partition of the elements that depends on n alone, fp32 partial sums,
  * a final sum in double.  cur, prev and workspace 16-byte aligned; workspace
- * >= dit_change_score_workspace_bytes() (partial sums; caller-owned). */
+ * >= dit_change_score_workspace_bytes() (partial sums; caller-owned).
+ * 1 <= n <= DIT_CHANGE_SCORE_MAX_N. */
+#define DIT_CHANGE_SCORE_MAX_N (INT64_C(1) << 40)
 size_t dit_change_score_workspace_bytes(void);
 dit_status dit_change_score(const void* cur, void* prev, int32_t dtype, int64_t n,
                             int32_t update, float* score, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
+
+/* dit_change_score without a workspace, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, result and errors as
+ * dit_change_score; the partial sums (DIT_CHANGE_SCORE_SCRATCH_BYTES = 8 KiB,
+ * enough for any n up to DIT_CHANGE_SCORE_MAX_N) live in a static device
+ * array of the library, one per GPU, held until the process ends; its
+ * address is looked up on the first call on each device.  No allocation of
+ * any kind.  All calls on one GPU share that array: calls whose executions
+ * overlap on one GPU (e.g. on two streams) race and must be ordered by the
+ * caller.  n > DIT_CHANGE_SCORE_MAX_N -> DIT_EINVAL. */
+#define DIT_CHANGE_SCORE_SCRATCH_BYTES 8192
+dit_status dit_change_score_noalloc(const void* cur, void* prev, int32_t dtype, int64_t n,
+                                    int32_t update, float* score, hipStream_t stream);
 
 /* The probe of calibrated adaptive caching: the change of block 0's modulated
  * input between this call and the previous one.  Runs the step's timestep
