@@ -84,7 +84,8 @@ def assert_bf16_ulp(got, ref, what="", atol_rel=1e-4):
 
 # Composite bound factor: the GPU may sit at most TWIN_FACTOR times as far
 # from the bf16-storing fp64 oracle as the oracle's own fp32 twin does (see
-# assert_composite).  Measured on MI355X at full size: 0.88-1.38 times.
+# assert_composite).  Measured on MI355X at every full-size composite:
+# 0.56-1.38 times in max-abs, up to 1.10 times in rel-L2.
 TWIN_FACTOR = 1.5
 
 
@@ -124,11 +125,16 @@ def assert_composite(got, ref, exact, what="", twin=None):
     evaluation of the kind the GPU performs.  The GPU adds rounding the twin
     does not have (its softmax weights enter the value product as bf16, its
     exp and erf are the hardware's), hence the factor TWIN_FACTOR on the
-    twin's spread.  The bound is also capped by the distance bf16 storage
-    moves the unrounded oracle (exact): max-abs <= max(2e-2,
-    min(TWIN_FACTOR * max|twin - ref|, max|exact - ref|)), rel-L2 <= 5e-3.
-    Without a twin the bound is max(2e-2, max|exact - ref|) (used only where
-    the oracle has no fp32 form: the guided cache state)."""
+    twin's spread:
+      max-abs <= max(2e-2, TWIN_FACTOR * T),  rel-L2 <= max(5e-3, TWIN_FACTOR * t),
+    with T and t the max-abs and rel-L2 distances of the twin from the
+    reference.  Only deep compositions reach the rel-L2 extension (24 live
+    blocks under guidance g = 5: the guided velocity is a small difference of
+    two nearly equal predictions, and the oracle's own fp64 and fp32
+    evaluations of it differ by 3.4 % rel-L2).  The distance of the unrounded
+    evaluation (exact) is logged beside it.  Without a twin the bound is
+    max(2e-2, max|exact - ref|) and rel-L2 5e-3 (used only where the oracle
+    has no fp32 form: the guided cache state)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     exact = np.asarray(exact, np.float64)
@@ -138,21 +144,26 @@ def assert_composite(got, ref, exact, what="", twin=None):
     rec = {"what": what, "n": int(got.size), "max_abs": ma, "rel_l2": rl,
            "over_2e-2": int((np.abs(got - ref) > MAX_ABS).sum()), "exact_spread": spread,
            "cosine": cos, "max_abs_ref": float(np.abs(ref).max())}
+    rel_bound = REL_L2
     if twin is not None:
         twin = np.asarray(twin, np.float64)
         tspread = float(np.abs(twin - ref).max())
-        bound = max(MAX_ABS, min(TWIN_FACTOR * tspread, spread))
-        rec.update(twin_spread=tspread, twin_rel_l2=errors(twin, ref)[1],
+        t_rel, e_rel = errors(twin, ref)[1], errors(exact, ref)[1]
+        bound = max(MAX_ABS, TWIN_FACTOR * tspread)
+        rel_bound = max(REL_L2, TWIN_FACTOR * t_rel)
+        rec.update(twin_spread=tspread, twin_rel_l2=t_rel, exact_rel_l2=e_rel,
                    twin_over_2e_2=int((np.abs(twin - ref) > MAX_ABS).sum()))
         print(f"[composite] {what}: fp32-twin spread {tspread:.3e} (bf16-storage spread "
-              f"{spread:.3e}) -> max-abs bound {bound:.3e}; cosine {cos:.7f}", flush=True)
+              f"{spread:.3e}) -> max-abs bound {bound:.3e}, rel-L2 bound {rel_bound:.2e}; "
+              f"cosine {cos:.7f}", flush=True)
     else:
         bound = max(MAX_ABS, spread)
         print(f"[composite] {what}: bf16-storage spread {spread:.3e} -> max-abs bound {bound:.3e}; "
               f"cosine {cos:.7f}", flush=True)
     rec["bound"] = bound
+    rec["rel_bound"] = rel_bound
     _log_parity(rec)
-    assert_parity(got, ref, what, max_abs=bound, rel_l2=REL_L2)
+    assert_parity(got, ref, what, max_abs=bound, rel_l2=rel_bound)
 
 
 def assert_composite_extrapolated(got, ref, exact, what=""):

@@ -4,13 +4,19 @@ against the oracle's denoising step, on the same seeded inputs.
 * tiny stack (2 blocks), all 30 steps free-running on both sides;
 * c5 shape with one block: one step at sigma indices 0, 15 and 29, compared
   on sampled visual rows (exact for a single block);
-* c5 at full depth (24 blocks, 30 steps): with every gate zero each block is
-  exactly the identity, so the whole trajectory equals the oracle's glue-only
-  loop -- checked on every latent element; and one step with a single live
-  layer (the last) equals the oracle's one-block step on sampled rows.
-Composite outputs use: rel-L2 <= 5e-3 and max-abs <= max(2e-2, the oracle's
-own bf16-storage spread on the same elements)."""
+* c5 at full depth (24 blocks, 30 steps): the first step with all 24 blocks
+  live against the oracle's step stored in tests/golden/c5_step0.npz (written
+  by tests/golden/make_c5_step0.py from the oracle alone), on every latent
+  element and on the guided velocity; with every gate zero each block is
+  exactly the identity, so the whole trajectory equals the oracle's
+  glue-only loop -- checked on every latent element; and one step with a
+  single live layer (the last) equals the oracle's one-block step on sampled
+  rows.
+Composite outputs use the bar of tests.gpu_util.assert_composite (rel-L2 <=
+5e-3, max-abs bounded by the oracle's own fp32-twin and bf16-storage
+spreads)."""
 
+import os
 import time
 
 import numpy as np
@@ -21,7 +27,7 @@ import diffusion_transformer_denoising_dit_amd as D
 import oracle as O
 from synthetic import configs as C
 from synthetic import gen as G
-from tests.gpu_util import assert_composite, dev_bf16, host
+from tests.gpu_util import assert_composite, dev_bf16, host, oracle_evals
 from tests.sampling import sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -102,11 +108,14 @@ def test_tiny_loop_free_running_30_steps():
     for i in range(shape.steps):
         m.gpu_step(x, float(sig[i]), float(sig[i + 1]))
     torch.cuda.synchronize()
-    ref, exact = lat0, lat0
-    for i in range(shape.steps):
-        ref, _ = O.denoise_step(m, ref, sig[i], sig[i + 1], shape.guidance)
-        exact, _ = O.denoise_step(m, exact, sig[i], sig[i + 1], shape.guidance, round_points=False)
-    assert_composite(host(x), ref, exact, "tiny loop, 30 steps")
+    def loop(r):
+        lat = lat0
+        for i in range(shape.steps):
+            lat, _ = O.denoise_step(m, lat, sig[i], sig[i + 1], shape.guidance, round_points=r)
+        return lat
+
+    ref, exact, twin = oracle_evals(loop)
+    assert_composite(host(x), ref, exact, "tiny loop, 30 steps", twin)
 
 
 @pytest.mark.slow
@@ -122,10 +131,9 @@ def test_c5_one_block_step_sampled(step):
     b = shape.block
     rows = sample_rows(b.n_vis, b.n_txt, m.txt_valid, n_random=48, seed=step)
     vis = rows[rows < b.n_vis]
-    ref, _ = O.denoise_step(m, lat0, sig[step], sig[step + 1], shape.guidance, rows=rows)
-    exact, _ = O.denoise_step(m, lat0, sig[step], sig[step + 1], shape.guidance, rows=rows,
-                              round_points=False)
-    assert_composite(host(x)[:, vis], ref, exact, f"c5 one-block step {step} (sampled)")
+    ref, exact, twin = oracle_evals(lambda r: O.denoise_step(
+        m, lat0, sig[step], sig[step + 1], shape.guidance, rows=rows, round_points=r)[0])
+    assert_composite(host(x)[:, vis], ref, exact, f"c5 one-block step {step} (sampled)", twin)
 
 
 def _c5_full(dead_all_but_last):
@@ -158,11 +166,14 @@ def test_c5_full_depth_zero_gates_trajectory():
     glue = Model(C.LoopShape("c5_glue", block=shape.block, depth=0, steps=shape.steps,
                              guidance=shape.guidance, latent_channels=shape.latent_channels,
                              seed=shape.seed))
-    ref, exact = lat0, lat0
-    for i in range(shape.steps):
-        ref, _ = O.denoise_step(glue, ref, sig[i], sig[i + 1], shape.guidance)
-        exact, _ = O.denoise_step(glue, exact, sig[i], sig[i + 1], shape.guidance, round_points=False)
-    assert_composite(host(x), ref, exact, "c5 24 blocks x 30 steps, zero gates")
+    def loop(r):
+        lat = lat0
+        for i in range(shape.steps):
+            lat, _ = O.denoise_step(glue, lat, sig[i], sig[i + 1], shape.guidance, round_points=r)
+        return lat
+
+    ref, exact, twin = oracle_evals(loop)
+    assert_composite(host(x), ref, exact, "c5 24 blocks x 30 steps, zero gates", twin)
 
 
 @pytest.mark.slow
@@ -183,7 +194,42 @@ def test_c5_full_depth_last_layer_live_step():
     b = shape.block
     rows = sample_rows(b.n_vis, b.n_txt, m.txt_valid, n_random=48, seed=7)
     vis = rows[rows < b.n_vis]
-    ref, _ = O.denoise_step(one, lat0, sig[0], sig[1], shape.guidance, rows=rows)
-    exact, _ = O.denoise_step(one, lat0, sig[0], sig[1], shape.guidance, rows=rows,
-                              round_points=False)
-    assert_composite(host(x)[:, vis], ref, exact, "c5 24 blocks, last layer live (sampled)")
+    ref, exact, twin = oracle_evals(lambda r: O.denoise_step(
+        one, lat0, sig[0], sig[1], shape.guidance, rows=rows, round_points=r)[0])
+    assert_composite(host(x)[:, vis], ref, exact, "c5 24 blocks, last layer live (sampled)", twin)
+
+
+GOLDEN_C5 = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "c5_step0.npz")
+
+
+@pytest.mark.slow
+def test_c5_full_depth_live_step0_against_golden():
+    """The c5 model with all 24 blocks live (random N(0, 0.02) weights, CFG
+    batch 2, g = 5), first step sigma 1 -> 29/30 from the seeded latent.  The
+    oracle's three evaluations of the same step (fp64 with bf16 rounding
+    points, fp64 unrounded, fp32 twin) are read from the golden file; the new
+    latent and the guided velocity are formed from them with the oracle's
+    guidance and Euler formulas."""
+    shape = C.C5
+    g = np.load(GOLDEN_C5)
+    m = Model(shape).upload()
+    np.testing.assert_array_equal(np.asarray(m.txt_valid), g["txt_valid"])
+    lat0 = O.bf16_decode(m.inp.latent)[None]  # [1, n_vis, C]
+    sig = O.sigma_schedule(shape.steps)
+    assert float(g["sigma"]) == sig[0] and float(g["sigma_next"]) == sig[1]
+    x = torch.from_numpy(lat0.astype(np.float32)).cuda()
+    m.gpu_step(x, float(sig[0]), float(sig[1]))
+    torch.cuda.synchronize()
+    got = host(x)
+    s32, n32 = float(np.float32(sig[0])), float(np.float32(sig[1]))
+    dt = float(np.float32(n32) - np.float32(s32))
+    v = {"ref": O.bf16_decode(g["v_ref"]), "exact": g["v_exact"].astype(np.float64),
+         "twin": O.bf16_decode(g["v_twin"])}
+    vhat = {k: O.cfg_combine(a[0:1], a[1:2], shape.guidance) for k, a in v.items()}
+    lat = {k: O.euler_update(lat0, a, s32, n32) for k, a in vhat.items()}
+    assert_composite(got, lat["ref"], lat["exact"], "c5 24 live blocks, step 0: latent", lat["twin"])
+    # the guided velocity the GPU applied, recovered from its fp32 latent update
+    # (fp32 rounding of x moves it by <= 2**-24 |x| / |dt|, ~1e-5 here)
+    v_gpu = (got - lat0) / dt
+    assert_composite(v_gpu, vhat["ref"], vhat["exact"], "c5 24 live blocks, step 0: guided velocity",
+                     vhat["twin"])
