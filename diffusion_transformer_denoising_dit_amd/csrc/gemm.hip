@@ -10,11 +10,14 @@
 //
 // Large GEMMs (the block's projections and MLP): a workgroup of 8 waves (two
 // per SIMD) computes a 256 (tokens) x 256 (features) tile, each wave 128 x 64
-// = 4 x 2 MFMA 32x32 tiles with the accumulators in registers.  A 256 x 256 tile
-// moves 64 bytes of operands from L2 per 2 x 256 x 256 flops, half of what a
-// 128 x 256 tile needs, which keeps L2 below its bandwidth at full MFMA
-// rate.  K slices of 64 stream from HBM/L2 straight into LDS with
-// global_load_lds_dwordx4 into two 64 KB stages; each operand row of a slice
+// = 8 x 4 MFMA 16x16x32 tiles with the accumulators in registers.  The
+// 16x16x32 shape does the same work per cycle as 32x32x16 but draws less
+// power: under sustained load on every CU the shader clock settles ~12 %
+// higher with it (1.88 against 1.68 GHz, register operands, same flops).
+// A 256 x 256 tile moves 64 bytes of operands from L2 per 2 x 256 x 256
+// flops, half of what a 128 x 256 tile needs, which keeps L2 below its
+// bandwidth at full MFMA rate.  K slices of 64 stream from HBM/L2 straight
+// into a 160 KB LDS ring with global_load_lds_dwordx4; each operand row of a slice
 // is one full 128-byte line, stored unpadded with its 16-byte chunks
 // XOR-swizzled by row so the operand reads of a wave hit distinct bank
 // groups.  The two waves of a SIMD take turns: one multiplies a whole slice
@@ -45,6 +48,10 @@ constexpr int kAChunks = kTM * kBK / 8 / kThreads;  // 16-byte chunks per thread
 constexpr int kWChunks = kTN * kBK / 8 / kThreads;  // 4
 
 enum { EPI_BF16 = 0, EPI_GELU = 1, EPI_SILU = 2, EPI_F32 = 3, EPI_GATED = 4, EPI_RES = 5 };
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ int64_t a_row_offset(const GemmParams& p, int64_t r) {
   return p.group_rows > 0 ? (r / p.group_rows) * p.a_group_stride + (r % p.group_rows) * p.lda
@@ -102,65 +109,65 @@ __device__ __forceinline__ void store_epilogue(const GemmParams& p, int64_t m, i
 }
 
 // The epilogue of one wave's 128 (tokens) x 64 (features) block of a
-// 256 x 256 tile, acc[i][j][4*g + e] = C[m, n] with m = m_base + 32j +
-// lane%32 and n = n_base + 32i + 8g + 4*(lane/32) + e.  The loads it needs
-// are issued in batches before their uses -- the bias of all 8 feature
-// groups once, then per 32-row block the residual (and gate) values of all
-// 8 groups -- so a block costs one memory round trip rather than one per
-// group.  p.n is a multiple of 8, so whether a group's 8 features are in
-// range does not depend on the lane half.
+// 256 x 256 tile, acc[i][j][e] = C[m, n] with m = m_base + 16j + lane%16 and
+// n = n_base + 16i + 4*(lane/16) + e.  The loads it needs are issued in
+// batches before their uses -- the bias of all 4 feature groups once, then
+// per pair of 16-row blocks the residual (and gate) values of both -- so a
+// pair costs one memory round trip rather than one per group.  p.n is a
+// multiple of 8, so a lane's 4 features are all in range or all out.
 template <int EPI, bool kChecked>
-__device__ __forceinline__ void tile_epilogue_impl(const GemmParams& p, const f32x16 (&acc)[2][4],
+__device__ __forceinline__ void tile_epilogue_impl(const GemmParams& p, const f32x4 (&acc)[4][8],
                                                    int64_t m_base, int n_base, int lane) {
   constexpr bool kResid = EPI == EPI_GATED || EPI == EPI_RES;
-  const int hi = lane / 32;
-  u32x2 bias[2][4];
+  const int nq = 4 * (lane / 16);
+  u32x2 bias[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) bias[i][g] = u32x2{0u, 0u};
+  for (int i = 0; i < 4; ++i) bias[i] = u32x2{0u, 0u};
   if (p.bias) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n_base + i * 32 + 8 * g + 4 * hi;
-        if (!kChecked || n < p.n) bias[i][g] = *reinterpret_cast<const u32x2*>(p.bias + n);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int n = n_base + i * 16 + nq;
+      if (!kChecked || n < p.n) bias[i] = *reinterpret_cast<const u32x2*>(p.bias + n);
+    }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t m = m_base + j * 32 + (lane % 32);
-    if (kChecked && m >= p.m) continue;
-    const int64_t crow = c_row_offset(p, m);
+  for (int jp = 0; jp < 4; ++jp) {
+    int64_t crow[2];
+    bool row_ok[2];
     f32x4 xr[2][4];
     u32x2 gt[2][4];
-    if constexpr (kResid) {
-      const uint16_t* grow = EPI == EPI_GATED ? p.gate + (m / p.gate_rows) * p.gate_stride : nullptr;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int h = 0; h < 2; ++h) {
+      const int64_t m = m_base + (2 * jp + h) * 16 + (lane % 16);
+      row_ok[h] = !kChecked || m < p.m;
+      crow[h] = c_row_offset(p, row_ok[h] ? m : 0);
+      if constexpr (kResid) {
+        const uint16_t* grow =
+            EPI == EPI_GATED ? p.gate + ((row_ok[h] ? m : 0) / p.gate_rows) * p.gate_stride : nullptr;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n_base + i * 32 + 8 * g + 4 * hi;
-          if (!kChecked || n < p.n) {
-            xr[i][g] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.out) + crow + n);
-            if constexpr (EPI == EPI_GATED) gt[i][g] = *reinterpret_cast<const u32x2*>(grow + n);
+        for (int i = 0; i < 4; ++i) {
+          const int n = n_base + i * 16 + nq;
+          if (row_ok[h] && (!kChecked || n < p.n)) {
+            xr[h][i] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.out) + crow[h] + n);
+            if constexpr (EPI == EPI_GATED) gt[h][i] = *reinterpret_cast<const u32x2*>(grow + n);
           }
         }
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int h = 0; h < 2; ++h) {
+      if (!row_ok[h]) continue;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n_base + i * 32 + 8 * g + 4 * hi;
+      for (int i = 0; i < 4; ++i) {
+        const int n = n_base + i * 16 + nq;
         if (kChecked && n >= p.n) continue;
         float y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * g + e];
-        y[0] += __uint_as_float(bias[i][g][0] << 16);
-        y[1] += __uint_as_float(bias[i][g][0] & 0xffff0000u);
-        y[2] += __uint_as_float(bias[i][g][1] << 16);
-        y[3] += __uint_as_float(bias[i][g][1] & 0xffff0000u);
+        for (int e = 0; e < 4; ++e) y[e] = acc[i][2 * jp + h][e];
+        y[0] += __uint_as_float(bias[i][0] << 16);
+        y[1] += __uint_as_float(bias[i][0] & 0xffff0000u);
+        y[2] += __uint_as_float(bias[i][1] << 16);
+        y[3] += __uint_as_float(bias[i][1] & 0xffff0000u);
         if constexpr (EPI == EPI_GELU) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[e] = 0.5f * y[e] * (1.f + erff(y[e] * 0.70710678118654752f));
@@ -171,32 +178,33 @@ __device__ __forceinline__ void tile_epilogue_impl(const GemmParams& p, const f3
         if constexpr (EPI == EPI_F32 || kResid) {
           f32x4 o;
           if constexpr (EPI == EPI_RES) {
-            o = xr[i][g];
+            o = xr[h][i];
             o[0] += y[0]; o[1] += y[1]; o[2] += y[2]; o[3] += y[3];
           } else if constexpr (EPI == EPI_GATED) {
-            o = xr[i][g];
-            o[0] += __uint_as_float(gt[i][g][0] << 16) * y[0];
-            o[1] += __uint_as_float(gt[i][g][0] & 0xffff0000u) * y[1];
-            o[2] += __uint_as_float(gt[i][g][1] << 16) * y[2];
-            o[3] += __uint_as_float(gt[i][g][1] & 0xffff0000u) * y[3];
+            o = xr[h][i];
+            o[0] += __uint_as_float(gt[h][i][0] << 16) * y[0];
+            o[1] += __uint_as_float(gt[h][i][0] & 0xffff0000u) * y[1];
+            o[2] += __uint_as_float(gt[h][i][1] << 16) * y[2];
+            o[3] += __uint_as_float(gt[h][i][1] & 0xffff0000u) * y[3];
           } else {
             o[0] = y[0]; o[1] = y[1]; o[2] = y[2]; o[3] = y[3];
           }
-          *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + crow + n) = o;
+          *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + crow[h] + n) = o;
         } else {
           u32x2 o;
           o[0] = pack_bf16x2(y[0], y[1]);
           o[1] = pack_bf16x2(y[2], y[3]);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + crow + n) = o;
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + crow[h] + n) = o;
         }
       }
+    }
   }
 }
 
 // Interior blocks (every row and feature in range, the common case) take a
 // branch-free path; edge blocks check each row and feature group.
 template <int EPI>
-__device__ __forceinline__ void tile_epilogue(const GemmParams& p, const f32x16 (&acc)[2][4],
+__device__ __forceinline__ void tile_epilogue(const GemmParams& p, const f32x4 (&acc)[4][8],
                                               int64_t m_base, int n_base, int lane) {
   if (m_base + 128 <= p.m && n_base + 64 <= p.n)
     tile_epilogue_impl<EPI, false>(p, acc, m_base, n_base, lane);
@@ -384,7 +392,7 @@ typedef __attribute__((address_space(3))) char* lds_char_ptr;
 // 0-3) multiplies token rows 0-127 of the tile, group 1 rows 128-255, each
 // wave 128 tokens x 64 features.  A wave alternates a memory phase (read the
 // 16 A and 8 W operand fragments of one 64-k slice from LDS into registers,
-// and issue its share of later slices' loads) and an MFMA phase (the 32
+// and issue its share of later slices' loads) and an MFMA phase (the 64
 // MFMAs of that slice), the second group one phase behind the first, with a
 // workgroup barrier at every phase boundary: on each SIMD one wave
 // multiplies while the other moves data.  Group 0 reads slice s in phase 2s,
@@ -409,7 +417,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int hi = lane / 32;
   const int grp = wave / 4, wq = wave % 4;
 
   // tile of this workgroup: XCD-contiguous ids, then groups of kGroupM token tiles
@@ -465,49 +472,50 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
     for (int n = 0; n < kLoadsHalf; ++n) lds_dma16(src, w_vo[n], dst + (wq * kLoadsHalf + n) * 1024);
   };
 
-  // wave tile: 128 token rows (grp) x 64 features (wq).  Operand read offsets
-  // within the A piece / W stage: row = base row + lane%32 (+32 per MFMA tile,
-  // an immediate); the swizzle depends on the row's bits 1..3, which the tile
-  // offsets do not change.
-  int a_off[4], w_off[4];
+  // wave tile: 128 token rows (grp) x 64 features (wq), 8 x 4 MFMA 16x16
+  // tiles.  Operand read offsets within the A piece / W stage: row = base row
+  // + lane%16 (+16 per MFMA tile, an immediate), 16-byte chunk 4*ks + lane/16
+  // of the row's 8 (k step ks of 32); the swizzle depends on the row's bits
+  // 1..3, which the tile offsets do not change.
+  int a_off[2], w_off[2];
   {
-    const int r = lane % 32;
+    const int r = lane % 16, q = lane / 16;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      a_off[ks] = r * kRowBytes + (((2 * ks + hi) ^ swz(r)) * 16);
-      w_off[ks] = (wq * 64 + r) * kRowBytes + (((2 * ks + hi) ^ swz(r)) * 16);
+    for (int ks = 0; ks < 2; ++ks) {
+      a_off[ks] = r * kRowBytes + (((4 * ks + q) ^ swz(r)) * 16);
+      w_off[ks] = (wq * 64 + r) * kRowBytes + (((4 * ks + q) ^ swz(r)) * 16);
     }
   }
 
-  f32x16 acc[2][4];
+  f32x4 acc[4][8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
 
-  auto memory_phase = [&](int s, bf16x8 (&wf)[4][2], bf16x8 (&af)[4][4]) {
+  auto memory_phase = [&](int s, bf16x8 (&wf)[2][4], bf16x8 (&af)[2][8]) {
     const char* ws = smem + (s % kWStages) * kTileW;
     const char* as = smem + kOffA + (2 * grp + s % kAStages) * kHalfBytes;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        wf[ks][i] = *reinterpret_cast<const bf16x8*>(ws + w_off[ks] + i * 32 * kRowBytes);
+      for (int i = 0; i < 4; ++i)
+        wf[ks][i] = *reinterpret_cast<const bf16x8*>(ws + w_off[ks] + i * 16 * kRowBytes);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        af[ks][j] = *reinterpret_cast<const bf16x8*>(as + a_off[ks] + j * 32 * kRowBytes);
+      for (int j = 0; j < 8; ++j)
+        af[ks][j] = *reinterpret_cast<const bf16x8*>(as + a_off[ks] + j * 16 * kRowBytes);
     }
     wait_lgkm0();  // this wave's reads of slice s are done before its stage is refilled
   };
-  auto mfma_phase = [&](const bf16x8 (&wf)[4][2], const bf16x8 (&af)[4][4]) {
+  auto mfma_phase = [&](const bf16x8 (&wf)[2][4], const bf16x8 (&af)[2][8]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(wf[ks][i], af[ks][j], acc[i][j]);
+        for (int j = 0; j < 8; ++j) acc[i][j] = mfma16x16x32(wf[ks][i], af[ks][j], acc[i][j]);
   };
 
   if (grp == 0) {
@@ -522,7 +530,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
       phase_barrier();  // phase 2s
       if (s + 1 < k_tiles) issue_a(s + 1);
       if (s + 2 < k_tiles) issue_w(s + 2);
-      bf16x8 wf[4][2], af[4][4];
+      bf16x8 wf[2][4], af[2][8];
       memory_phase(s, wf, af);
       // A1(s), read by group 1 in phase 2s+1, has landed; W1(s+1), A1(s+1)
       // and W1(s+2) may still be in flight
@@ -548,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
         issue_a(s + 2);
         issue_w(s + 2);
       }
-      bf16x8 wf[4][2], af[4][4];
+      bf16x8 wf[2][4], af[2][8];
       memory_phase(s, wf, af);
       // A0(s+1) and W2(s+1), read by group 0 in phase 2s+2, have landed
       wait_items(s + 2 < k_tiles ? 2 : 0);
