@@ -49,6 +49,27 @@ constexpr int kWChunks = kTN * kBK / 8 / kThreads;  // 4
 
 enum { EPI_BF16 = 0, EPI_GELU = 1, EPI_SILU = 2, EPI_F32 = 3, EPI_GATED = 4, EPI_RES = 5 };
 
+// GELU in its exact form x * Phi(x) = x (1 + erf(x / sqrt 2)) / 2, with erf
+// from the rational approximation of Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (after Hastings): for z >= 0,
+// erf(z) = 1 - q(t) exp(-z^2), t = 1 / (1 + p z), q a degree-5 polynomial in
+// t with no constant term, |error| <= 1.5e-7.  1 + erf(x / sqrt 2) is then
+// 2 - q e for x >= 0 and q e for x < 0 (no cancellation in the negative
+// tail).  About 12 branch-free VALU instructions per value; against exact
+// GELU the fp32 result is within 5e-7 absolute, far below the bf16 rounding
+// of the stored output.
+__device__ __forceinline__ float gelu(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.f));
+  float q = fmaf(t, 1.061405429f, -1.453152027f);
+  q = fmaf(t, q, 1.421413741f);
+  q = fmaf(t, q, -0.284496736f);
+  q = fmaf(t, q, 0.254829592f);
+  q *= t;
+  const float qe = q * __builtin_amdgcn_exp2f(-(z * z) * 1.4426950408889634f);
+  return 0.5f * x * (x >= 0.f ? 2.f - qe : qe);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -76,7 +97,7 @@ __device__ __forceinline__ void store_epilogue(const GemmParams& p, int64_t m, i
   }
   if (EPI == EPI_GELU) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = 0.5f * y[e] * (1.f + erff(y[e] * 0.70710678118654752f));
+    for (int e = 0; e < 4; ++e) y[e] = gelu(y[e]);
   } else if (EPI == EPI_SILU) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = y[e] / (1.f + expf(-y[e]));
@@ -112,13 +133,17 @@ __device__ __forceinline__ void store_epilogue(const GemmParams& p, int64_t m, i
 // 256 x 256 tile, acc[i][j][e] = C[m, n] with m = m_base + 16j + lane%16 and
 // n = n_base + 16i + 4*(lane/16) + e.  The loads it needs are issued in
 // batches before their uses -- the bias of all 4 feature groups once, then
-// per pair of 16-row blocks the residual (and gate) values of both -- so a
-// pair costs one memory round trip rather than one per group.  p.n is a
+// per kEpiRows 16-row blocks the residual (and gate) values of all of them
+// (the operand registers of the main loop are free by now) -- so a batch
+// costs one memory round trip rather than one per group.  p.n is a
 // multiple of 8, so a lane's 4 features are all in range or all out.
 template <int EPI, bool kChecked>
 __device__ __forceinline__ void tile_epilogue_impl(const GemmParams& p, const f32x4 (&acc)[4][8],
                                                    int64_t m_base, int n_base, int lane) {
   constexpr bool kResid = EPI == EPI_GATED || EPI == EPI_RES;
+  // 16-row blocks per batch (of 8); the gated residual's gate values would
+  // not fit beside 4 blocks' residuals without spilling
+  constexpr int kEpiRows = EPI == EPI_GATED ? 2 : 4;
   const int nq = 4 * (lane / 16);
   u32x2 bias[4];
 #pragma unroll
@@ -131,14 +156,14 @@ __device__ __forceinline__ void tile_epilogue_impl(const GemmParams& p, const f3
     }
   }
 #pragma unroll
-  for (int jp = 0; jp < 4; ++jp) {
-    int64_t crow[2];
-    bool row_ok[2];
-    f32x4 xr[2][4];
-    u32x2 gt[2][4];
+  for (int jp = 0; jp < 8 / kEpiRows; ++jp) {
+    int64_t crow[kEpiRows];
+    bool row_ok[kEpiRows];
+    f32x4 xr[kEpiRows][4];
+    u32x2 gt[kEpiRows][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t m = m_base + (2 * jp + h) * 16 + (lane % 16);
+    for (int h = 0; h < kEpiRows; ++h) {
+      const int64_t m = m_base + (kEpiRows * jp + h) * 16 + (lane % 16);
       row_ok[h] = !kChecked || m < p.m;
       crow[h] = c_row_offset(p, row_ok[h] ? m : 0);
       if constexpr (kResid) {
@@ -155,7 +180,7 @@ __device__ __forceinline__ void tile_epilogue_impl(const GemmParams& p, const f3
       }
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < kEpiRows; ++h) {
       if (!row_ok[h]) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -163,14 +188,14 @@ __device__ __forceinline__ void tile_epilogue_impl(const GemmParams& p, const f3
         if (kChecked && n >= p.n) continue;
         float y[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = acc[i][2 * jp + h][e];
+        for (int e = 0; e < 4; ++e) y[e] = acc[i][kEpiRows * jp + h][e];
         y[0] += __uint_as_float(bias[i][0] << 16);
         y[1] += __uint_as_float(bias[i][0] & 0xffff0000u);
         y[2] += __uint_as_float(bias[i][1] << 16);
         y[3] += __uint_as_float(bias[i][1] & 0xffff0000u);
         if constexpr (EPI == EPI_GELU) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = 0.5f * y[e] * (1.f + erff(y[e] * 0.70710678118654752f));
+          for (int e = 0; e < 4; ++e) y[e] = gelu(y[e]);
         } else if constexpr (EPI == EPI_SILU) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) y[e] = y[e] / (1.f + expf(-y[e]));
