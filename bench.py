@@ -353,9 +353,10 @@ def hbm_probe(steps, reps=None):
 
 def block_gemms(reps, stream):
     """The DiT block's four large GEMMs at the c3 shape (33,272 tokens, hidden
-    5120, MLP 13824), each through dit_linear with the epilogue the block uses,
-    and beside each the same product as a plain torch matmul (hipBLASLt, no
-    epilogue) for reference.  Seeded N(0,1) activations, N(0, 0.02) weights."""
+    5120, MLP 13824), each through dit_linear with the epilogue and the K-split
+    scratch the block uses, and beside each the same product as a plain torch
+    matmul (hipBLASLt, no epilogue) for reference.  Seeded N(0,1) activations,
+    N(0, 0.02) weights."""
     import torch
 
     import diffusion_transformer_denoising_dit_amd as D
@@ -363,6 +364,8 @@ def block_gemms(reps, stream):
     blk = C.C3_STEP.block
     M, Dh, F = blk.batch * blk.n_tok, blk.hidden, blk.mlp
     g = torch.Generator("cuda").manual_seed(13)
+    wsb = D.dit_linear_workspace_bytes()
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     out = {}
     for name, n, k, epi in (("qkv", 3 * Dh, Dh, D.EPI_BF16), ("out_proj", Dh, Dh, D.EPI_GATED_RES_F32),
                             ("mlp_up", F, Dh, D.EPI_GELU_BF16), ("mlp_down", Dh, F, D.EPI_GATED_RES_F32)):
@@ -374,7 +377,8 @@ def block_gemms(reps, stream):
         gate = torch.randn((1, n), generator=g, device="cuda").to(torch.bfloat16) if gated else None
 
         def ours():
-            D.dit_linear(a, k, w, bias, M, n, k, epi, y, n, gate=gate, gate_stride=n, gate_rows=M)
+            D.dit_linear(a, k, w, bias, M, n, k, epi, y, n, gate=gate, gate_stride=n, gate_rows=M,
+                         workspace=ws, workspace_bytes=wsb)
 
         wt = w.t()
 
@@ -391,6 +395,7 @@ def block_gemms(reps, stream):
                      "hipblaslt_ms": round(ms_r, 3),
                      "hipblaslt_tflops": round(flop / (ms_r * 1e-3) / 1e12, 1)}
         del a, w, bias, y, gate, wt
+    del ws
     torch.cuda.empty_cache()
     return out
 

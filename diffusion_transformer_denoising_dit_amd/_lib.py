@@ -20,7 +20,8 @@ STATUS = {0: "DIT_OK", 1: "DIT_EINVAL", 2: "DIT_EUNSUPPORTED", 3: "DIT_EWORKSPAC
 EPI_BF16, EPI_GELU_BF16, EPI_SILU_BF16, EPI_F32, EPI_GATED_RES_F32, EPI_RES_F32 = range(6)
 
 EXPORTED = (
-    "dit_joint_attention", "dit_attention_partial", "dit_attention_merge", "dit_linear", "dit_adaln_modulate", "dit_qk_rmsnorm_rope",
+    "dit_joint_attention", "dit_attention_partial", "dit_attention_merge", "dit_linear_workspace_bytes",
+    "dit_linear", "dit_adaln_modulate", "dit_qk_rmsnorm_rope",
     "dit_block_workspace_bytes", "dit_block_forward", "dit_euler_step",
     "dit_timestep_features", "dit_cast_f32_bf16", "dit_cast_bf16_f32", "dit_debug_positions",
     "dit_denoise_workspace_bytes", "dit_denoise_step",
@@ -84,7 +85,8 @@ class LinearArgs(ctypes.Structure):
                 ("k", ctypes.c_int32), ("epilogue", ctypes.c_int32), ("out", ctypes.c_void_p),
                 ("ldc", ctypes.c_int64), ("gate", ctypes.c_void_p), ("gate_stride", ctypes.c_int64),
                 ("gate_rows", ctypes.c_int64), ("group_rows", ctypes.c_int64),
-                ("a_group_stride", ctypes.c_int64), ("c_group_stride", ctypes.c_int64)]
+                ("a_group_stride", ctypes.c_int64), ("c_group_stride", ctypes.c_int64),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class ModelDesc(ctypes.Structure):
@@ -148,6 +150,7 @@ def lib() -> ctypes.CDLL:
                                            vp, f32, vp]),
             "dit_attention_merge": (st, [ctypes.POINTER(MergeDesc), ctypes.POINTER(vp), i64,
                                          ctypes.POINTER(vp), vp, i64, vp, vp]),
+            "dit_linear_workspace_bytes": (ctypes.c_size_t, []),
             "dit_linear": (st, [ctypes.POINTER(LinearArgs), vp]),
             "dit_adaln_modulate": (st, [vp, i64, i32, i64, vp, vp, i64, f32, vp, vp]),
             "dit_qk_rmsnorm_rope": (st, [ctypes.POINTER(BlockDesc), vp, i64, vp, vp, vp]),
@@ -271,10 +274,16 @@ def dit_attention_merge(batch, n_q, heads, head_dim, outs, part_row_stride, lses
                                      out_row_stride, _ptr(lse_out), _stream(stream)))
 
 
+def dit_linear_workspace_bytes() -> int:
+    return int(lib().dit_linear_workspace_bytes())
+
+
 def dit_linear(a, lda, w, bias, m, n, k, epilogue, out, ldc, gate=None, gate_stride=0, gate_rows=1,
-               group_rows=0, a_group_stride=0, c_group_stride=0, stream=None):
+               group_rows=0, a_group_stride=0, c_group_stride=0, workspace=None, workspace_bytes=0,
+               stream=None):
     args = LinearArgs(_ptr(a), lda, _ptr(w), _ptr(bias), m, n, k, epilogue, _ptr(out), ldc,
-                      _ptr(gate), gate_stride, gate_rows, group_rows, a_group_stride, c_group_stride)
+                      _ptr(gate), gate_stride, gate_rows, group_rows, a_group_stride, c_group_stride,
+                      _ptr(workspace), workspace_bytes)
     _check(lib().dit_linear(ctypes.byref(args), _stream(stream)))
 
 

@@ -134,17 +134,24 @@ constexpr int64_t kMaxQkvRowStride = int64_t{1} << 24;
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct WsLayout {
-  size_t h_off, big_off, total;
+  size_t h_off, big_off, split_off, total;
 };
 
+// Block workspace: h/o/h2, then qkv/the MLP hidden, then (for token counts
+// that reach the large GEMM kernel) the scratch of its K-split last round.
 WsLayout ws_layout(const dit_block_desc* d) {
   const size_t M = static_cast<size_t>(d->attn.batch) * (d->attn.n_vis + d->attn.n_txt);
   const size_t D = d->hidden, F = d->mlp;
   WsLayout w;
   w.h_off = 0;
   w.big_off = align256(M * D * 2);
-  w.total = w.big_off + align256(M * (3 * D > F ? 3 * D : F) * 2);
+  w.split_off = w.big_off + align256(M * (3 * D > F ? 3 * D : F) * 2);
+  w.total = w.split_off + (M >= 1024 ? dit::kSplitWsBytes : 0);
   return w;
+}
+
+float* split_scratch(char* ws, const WsLayout& L) {
+  return L.total > L.split_off ? reinterpret_cast<float*>(ws + L.split_off) : nullptr;
 }
 
 dit_status check_linear(const dit_linear_args* a) {
@@ -189,11 +196,22 @@ dit_status check_linear(const dit_linear_args* a) {
     return fail(DIT_EINVAL, "out overlaps the A operand");
   if (a->bias && overlap(a->bias, static_cast<size_t>(a->n) * 2, a->out, c_bytes))
     return fail(DIT_EINVAL, "out overlaps the bias");
+  size_t gate_bytes = 0;
   if (a->epilogue == DIT_EPI_GATED_RES_F32) {
-    const size_t gate_bytes =
-        static_cast<size_t>(((a->m - 1) / a->gate_rows) * a->gate_stride + a->n) * 2;
+    gate_bytes = static_cast<size_t>(((a->m - 1) / a->gate_rows) * a->gate_stride + a->n) * 2;
     if (overlap(a->gate, gate_bytes, a->out, c_bytes))
       return fail(DIT_EINVAL, "out overlaps the gate rows");
+  }
+  if (a->workspace) {
+    if (!aligned(a->workspace, 256)) return fail(DIT_EINVAL, "workspace not 256-byte aligned");
+    if (a->workspace_bytes < dit::kSplitWsBytes)
+      return fail(DIT_EWORKSPACE, "workspace %zu bytes < %zu needed", a->workspace_bytes, dit::kSplitWsBytes);
+    const size_t wb = dit::kSplitWsBytes;
+    if (overlap(a->workspace, wb, a->a, a_bytes) || overlap(a->workspace, wb, a->out, c_bytes) ||
+        overlap(a->workspace, wb, a->w, static_cast<size_t>(a->n) * a->k * 2) ||
+        (a->bias && overlap(a->workspace, wb, a->bias, static_cast<size_t>(a->n) * 2)) ||
+        (gate_bytes && overlap(a->workspace, wb, a->gate, gate_bytes)))
+      return fail(DIT_EINVAL, "workspace overlaps an operand or the output");
   }
   return DIT_OK;
 }
@@ -215,6 +233,7 @@ dit::GemmParams gemm_params(const dit_linear_args* a) {
   p.group_rows = a->group_rows;
   p.a_group_stride = a->a_group_stride;
   p.c_group_stride = a->c_group_stride;
+  p.split_ws = static_cast<float*>(a->workspace);
   return p;
 }
 
@@ -229,6 +248,7 @@ hipError_t block_launch(const dit_block_desc* desc, const dit_block_weights* w, 
   const WsLayout L = ws_layout(desc);
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + L.h_off);   // h, then o, then h2
   uint16_t* big = reinterpret_cast<uint16_t*>(ws + L.big_off);  // qkv, then the MLP hidden
+  float* split = split_scratch(ws, L);
 
   hipError_t e;
   // 1. h = adaLN(x; shift1, scale1)
@@ -237,7 +257,7 @@ hipError_t block_launch(const dit_block_desc* desc, const dit_block_weights* w, 
   // 2. qkv = h W_qkv^T + b_qkv
   dit::GemmParams g{};
   g.a = hbuf; g.lda = D; g.w = w->w_qkv; g.bias = w->b_qkv; g.m = M; g.n = 3 * D; g.k = D;
-  g.out = big; g.ldc = 3 * D; g.gate_rows = 1;
+  g.out = big; g.ldc = 3 * D; g.gate_rows = 1; g.split_ws = split;
   e = dit::launch_gemm(g, DIT_EPI_BF16, stream);
   if (e != hipSuccess) { *what = "block: qkv gemm"; return e; }
   // 3. q, k <- RoPE(RMSNorm(.) * g)
@@ -259,7 +279,7 @@ hipError_t block_launch(const dit_block_desc* desc, const dit_block_weights* w, 
   // 5. x += gate1 * (o W_o^T + b_o)
   g = dit::GemmParams{};
   g.a = hbuf; g.lda = D; g.w = w->w_o; g.bias = w->b_o; g.m = M; g.n = D; g.k = D;
-  g.out = x; g.ldc = D; g.gate = mod + 2 * D; g.gate_stride = ms; g.gate_rows = N;
+  g.out = x; g.ldc = D; g.gate = mod + 2 * D; g.gate_stride = ms; g.gate_rows = N; g.split_ws = split;
   e = dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream);
   if (e != hipSuccess) { *what = "block: out-proj gemm"; return e; }
   // 6. h2 = adaLN(x; shift2, scale2)
@@ -268,13 +288,13 @@ hipError_t block_launch(const dit_block_desc* desc, const dit_block_weights* w, 
   // 7. u = GELU(h2 W_up^T + b_up)
   g = dit::GemmParams{};
   g.a = hbuf; g.lda = D; g.w = w->w_up; g.bias = w->b_up; g.m = M; g.n = F; g.k = D;
-  g.out = big; g.ldc = F; g.gate_rows = 1;
+  g.out = big; g.ldc = F; g.gate_rows = 1; g.split_ws = split;
   e = dit::launch_gemm(g, DIT_EPI_GELU_BF16, stream);
   if (e != hipSuccess) { *what = "block: mlp-up gemm"; return e; }
   // 8. x += gate2 * (u W_dn^T + b_dn)
   g = dit::GemmParams{};
   g.a = big; g.lda = F; g.w = w->w_dn; g.bias = w->b_dn; g.m = M; g.n = D; g.k = F;
-  g.out = x; g.ldc = D; g.gate = mod + 5 * D; g.gate_stride = ms; g.gate_rows = N;
+  g.out = x; g.ldc = D; g.gate = mod + 5 * D; g.gate_stride = ms; g.gate_rows = N; g.split_ws = split;
   e = dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream);
   if (e != hipSuccess) { *what = "block: mlp-down gemm"; return e; }
   return hipSuccess;
@@ -339,10 +359,10 @@ dit_status check_block_weights(const dit_block_weights* w) {
 }
 
 dit::GemmParams gemm(const uint16_t* a, int64_t lda, const uint16_t* w, const uint16_t* bias, int64_t m,
-                     int n, int k, void* out, int64_t ldc) {
+                     int n, int k, void* out, int64_t ldc, float* split = nullptr) {
   dit::GemmParams g{};
   g.a = a; g.lda = lda; g.w = w; g.bias = bias; g.m = m; g.n = n; g.k = k;
-  g.out = out; g.ldc = ldc; g.gate_rows = 1;
+  g.out = out; g.ldc = ldc; g.gate_rows = 1; g.split_ws = split;
   return g;
 }
 
@@ -532,6 +552,8 @@ dit_status dit_attention_merge(const dit_merge_desc* desc, const float* const* o
   return hip_status(dit::launch_attention_merge(p, stream), "attention merge launch");
 }
 
+size_t dit_linear_workspace_bytes(void) { return dit::kSplitWsBytes; }
+
 dit_status dit_linear(const dit_linear_args* args, hipStream_t stream) {
   dit_status s = check_linear(args);
   if (s != DIT_OK) return s;
@@ -702,6 +724,7 @@ dit_status dit_double_block_forward(const dit_block_desc* desc, const dit_block_
   char* ws = static_cast<char*>(workspace);
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + WL.h_off);   // h per stream, o (joint), h2 per stream
   uint16_t* big = reinterpret_cast<uint16_t*>(ws + WL.big_off);  // qkv (joint), MLP hidden per stream
+  float* split = split_scratch(ws, WL);
   uint16_t* h_txt = hbuf + static_cast<int64_t>(B) * S * D;
   uint16_t* u_txt = big + static_cast<int64_t>(B) * S * F;
   struct Stream {
@@ -729,6 +752,7 @@ dit_status dit_double_block_forward(const dit_block_desc* desc, const dit_block_
     g.group_rows = t.rows;
     g.a_group_stride = static_cast<int64_t>(t.rows) * D;
     g.c_group_stride = N * 3 * D;
+    g.split_ws = split;
     DIT_TRY(dit::launch_gemm(g, DIT_EPI_BF16, stream), "double block: qkv gemm");
   }
   // Q/K RMSNorm with each stream's gains + RoPE (image rows at their grid
@@ -767,6 +791,7 @@ dit_status dit_double_block_forward(const dit_block_desc* desc, const dit_block_
     g.a_group_stride = N * D;
     g.c_group_stride = static_cast<int64_t>(t.rows) * D;
     g.gate = t.mod + 2 * D; g.gate_stride = ms; g.gate_rows = t.rows;
+    g.split_ws = split;
     DIT_TRY(dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream), "double block: out-proj gemm");
   }
   // per stream: x += gate2 (GELU(adaLN(x; shift2, scale2) W_up^T + b_up) W_dn^T + b_dn)
@@ -775,10 +800,12 @@ dit_status dit_double_block_forward(const dit_block_desc* desc, const dit_block_
     const int64_t M = static_cast<int64_t>(B) * t.rows;
     DIT_TRY(dit::launch_adaln(t.x, M, D, t.rows, t.mod + 3 * D, t.mod + 4 * D, ms, desc->ln_eps, t.h, stream),
             "double block: adaln 2");
-    DIT_TRY(dit::launch_gemm(gemm(t.h, D, t.w->w_up, t.w->b_up, M, F, D, t.u, F), DIT_EPI_GELU_BF16, stream),
-            "double block: mlp-up gemm");
+    dit::GemmParams gu = gemm(t.h, D, t.w->w_up, t.w->b_up, M, F, D, t.u, F);
+    gu.split_ws = split;
+    DIT_TRY(dit::launch_gemm(gu, DIT_EPI_GELU_BF16, stream), "double block: mlp-up gemm");
     dit::GemmParams g = gemm(t.u, F, t.w->w_dn, t.w->b_dn, M, D, F, t.x, D);
     g.gate = t.mod + 5 * D; g.gate_stride = ms; g.gate_rows = t.rows;
+    g.split_ws = split;
     DIT_TRY(dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream), "double block: mlp-down gemm");
   }
   return ok();
@@ -786,7 +813,7 @@ dit_status dit_double_block_forward(const dit_block_desc* desc, const dit_block_
 
 namespace {
 struct SingleWs {
-  size_t h, qkv, cat, total;
+  size_t h, qkv, cat, split, total;
 };
 SingleWs single_ws(const dit_block_desc* d) {
   const size_t M = static_cast<size_t>(d->attn.batch) * (d->attn.n_vis + d->attn.n_txt);
@@ -795,7 +822,8 @@ SingleWs single_ws(const dit_block_desc* d) {
   w.h = 0;
   w.qkv = align256(M * D * 2);
   w.cat = w.qkv + align256(M * 3 * D * 2);
-  w.total = w.cat + align256(M * (D + F) * 2);
+  w.split = w.cat + align256(M * (D + F) * 2);
+  w.total = w.split + (M >= 1024 ? dit::kSplitWsBytes : 0);
   return w;
 }
 }  // namespace
@@ -831,14 +859,15 @@ dit_status dit_single_block_forward(const dit_block_desc* desc, const dit_single
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + WL.h);
   uint16_t* qkv = reinterpret_cast<uint16_t*>(ws + WL.qkv);
   uint16_t* cat = reinterpret_cast<uint16_t*>(ws + WL.cat);  // [o | GELU(up)], row stride D + F
+  float* split = WL.total > WL.split ? reinterpret_cast<float*>(ws + WL.split) : nullptr;
   const int64_t ldcat = static_cast<int64_t>(D) + F;
   // h = adaLN(x; shift, scale)
   DIT_TRY(dit::launch_adaln(x, M, D, N, mod, mod + D, ms, desc->ln_eps, h, stream), "single block: adaln");
   // linear1: rows [0, 3D) of w1 -> q|k|v, rows [3D, 3D + F) -> GELU(up) into the right of cat
-  DIT_TRY(dit::launch_gemm(gemm(h, D, w->w1, w->b1, M, 3 * D, D, qkv, 3 * D), DIT_EPI_BF16, stream),
+  DIT_TRY(dit::launch_gemm(gemm(h, D, w->w1, w->b1, M, 3 * D, D, qkv, 3 * D, split), DIT_EPI_BF16, stream),
           "single block: linear1 qkv");
   DIT_TRY(dit::launch_gemm(gemm(h, D, w->w1 + static_cast<int64_t>(3) * D * D, w->b1 + 3 * D, M, F, D,
-                                cat + D, ldcat),
+                                cat + D, ldcat, split),
                            DIT_EPI_GELU_BF16, stream),
           "single block: linear1 mlp");
   DIT_TRY(dit::launch_qk_rmsnorm_rope(rope_params(desc, qkv, 3 * D, w->g_q, w->g_k), stream),
@@ -857,7 +886,7 @@ dit_status dit_single_block_forward(const dit_block_desc* desc, const dit_single
     DIT_TRY(dit::launch_attention(ap, stream), "single block: attention");
   }
   // linear2 on [o | GELU(up)], gated residual
-  dit::GemmParams g = gemm(cat, ldcat, w->w2, w->b2, M, D, D + F, x, D);
+  dit::GemmParams g = gemm(cat, ldcat, w->w2, w->b2, M, D, D + F, x, D, split);
   g.gate = mod + 2 * D; g.gate_stride = ms; g.gate_rows = N;
   DIT_TRY(dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream), "single block: linear2");
 #undef DIT_TRY
@@ -870,7 +899,7 @@ dit_status dit_single_block_forward(const dit_block_desc* desc, const dit_single
 
 namespace {
 struct WanWs {
-  size_t h, big, ckv, total;
+  size_t h, big, ckv, split, total;
 };
 WanWs wan_ws(const dit_block_desc* d) {
   const size_t B = d->attn.batch, S = d->attn.n_vis, L = d->attn.n_txt;
@@ -879,7 +908,8 @@ WanWs wan_ws(const dit_block_desc* d) {
   w.h = 0;
   w.big = align256(B * S * D * 2);
   w.ckv = w.big + align256(B * S * (3 * D > F ? 3 * D : F) * 2);
-  w.total = w.ckv + align256(B * L * 2 * D * 2);
+  w.split = w.ckv + align256(B * L * 2 * D * 2);
+  w.total = w.split + (B * S >= 1024 ? dit::kSplitWsBytes : 0);
   return w;
 }
 
@@ -935,6 +965,7 @@ dit_status dit_wan_block_forward(const dit_block_desc* desc, const dit_wan_block
   uint16_t* hbuf = reinterpret_cast<uint16_t*>(ws + WL.h);  // h, o, LN(x1), cross o, h2
   uint16_t* big = reinterpret_cast<uint16_t*>(ws + WL.big);  // self q|k|v, cross q, MLP hidden
   uint16_t* ckv = reinterpret_cast<uint16_t*>(ws + WL.ckv);  // context k|v [B*L, 2D]
+  float* split = WL.total > WL.split ? reinterpret_cast<float*>(ws + WL.split) : nullptr;
 #define DIT_TRY(expr, what)                            \
   do {                                                 \
     const hipError_t e_ = (expr);                      \
@@ -942,7 +973,7 @@ dit_status dit_wan_block_forward(const dit_block_desc* desc, const dit_wan_block
   } while (0)
   // self-attention over the video tokens
   DIT_TRY(dit::launch_adaln(x, M, D, S, mod, mod + D, ms, desc->ln_eps, hbuf, stream), "wan block: adaln 1");
-  DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_qkv, w->b_qkv, M, 3 * D, D, big, 3 * D), DIT_EPI_BF16, stream),
+  DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_qkv, w->b_qkv, M, 3 * D, D, big, 3 * D, split), DIT_EPI_BF16, stream),
           "wan block: qkv gemm");
   {
     dit::RopeParams rp = rope_params(desc, big, 3 * D, w->g_q, w->g_k);
@@ -960,13 +991,13 @@ dit_status dit_wan_block_forward(const dit_block_desc* desc, const dit_wan_block
             "wan block: self-attention");
   }
   {
-    dit::GemmParams g = gemm(hbuf, D, w->w_o, w->b_o, M, D, D, x, D);
+    dit::GemmParams g = gemm(hbuf, D, w->w_o, w->b_o, M, D, D, x, D, split);
     g.gate = mod + 2 * D; g.gate_stride = ms; g.gate_rows = S;
     DIT_TRY(dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream), "wan block: out-proj gemm");
   }
   // cross-attention: q from LN(x), k|v from the context, keys [0, txt_valid[b])
   DIT_TRY(dit::launch_adaln(x, M, D, S, nullptr, nullptr, 0, desc->ln_eps, hbuf, stream), "wan block: layernorm");
-  DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_cq, w->b_cq, M, D, D, big, D), DIT_EPI_BF16, stream),
+  DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_cq, w->b_cq, M, D, D, big, D, split), DIT_EPI_BF16, stream),
           "wan block: cross q gemm");
   {
     // RMSNorm over D with the cross gains; position 0 for every row makes the
@@ -988,15 +1019,15 @@ dit_status dit_wan_block_forward(const dit_block_desc* desc, const dit_wan_block
                                             desc->attn, desc->attn.txt_valid),
                                 stream),
           "wan block: cross-attention");
-  DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_co, w->b_co, M, D, D, x, D), DIT_EPI_RES_F32, stream),
+  DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_co, w->b_co, M, D, D, x, D, split), DIT_EPI_RES_F32, stream),
           "wan block: cross out-proj gemm");
   // MLP
   DIT_TRY(dit::launch_adaln(x, M, D, S, mod + 3 * D, mod + 4 * D, ms, desc->ln_eps, hbuf, stream),
           "wan block: adaln 2");
-  DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_up, w->b_up, M, F, D, big, F), DIT_EPI_GELU_BF16, stream),
+  DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_up, w->b_up, M, F, D, big, F, split), DIT_EPI_GELU_BF16, stream),
           "wan block: mlp-up gemm");
   {
-    dit::GemmParams g = gemm(big, F, w->w_dn, w->b_dn, M, D, F, x, D);
+    dit::GemmParams g = gemm(big, F, w->w_dn, w->b_dn, M, D, F, x, D, split);
     g.gate = mod + 5 * D; g.gate_stride = ms; g.gate_rows = S;
     DIT_TRY(dit::launch_gemm(g, DIT_EPI_GATED_RES_F32, stream), "wan block: mlp-down gemm");
   }

@@ -33,6 +33,9 @@
 // at a time, the next slice fetched into registers while the current one is
 // multiplied.  Matrix-vector products (at most 8 token rows: the timestep MLP
 // and the modulation projections) stream W once without tiles.
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -364,6 +367,14 @@ constexpr int kOffA = kWStages * kTileW;                    // A half h, stage t
 constexpr int kLdsBytes = kOffA + 2 * kAStages * kHalfBytes;  // 160 KB
 constexpr int kGroupM = 8;
 
+// The grid of a large GEMM: `whole` workgroups of one whole tile each, then
+// `parts` workgroups per each of the remaining tiles, each with a contiguous
+// share of K (partials: fp32 scratch of parts * (tiles - whole) tiles).
+struct SplitPlan {
+  int whole, parts;
+  float* partials;
+};
+
 // 16-byte chunk c of a 128-byte row r sits at chunk position c ^ swz(r).  LDS
 // serves 16 bank groups of 16 bytes per clock; rows r and r+2 start in the
 // same bank group, and swz separates the 16 rows one operand read touches.
@@ -435,8 +446,21 @@ typedef __attribute__((address_space(3))) char* lds_char_ptr;
 // barrier a wave waits only for its own pieces that the next phase reads
 // (loads complete in order, so "at most n in flight" names them).  The LDS
 // ring fills all 160 KB of the CU.
+// Tile t of the grouped order: groups of kGroupM token tiles that sweep all
+// feature tiles, so the workgroups running together share operand slices.
+__device__ __forceinline__ void tile_of(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = kGroupM * tiles_n;
+  const int g = t / per_group;
+  const int first_m = g * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in_g = t - g * per_group;
+  tm = first_m + in_g % gsize;
+  tn = in_g / gsize;
+}
+
 template <int EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int tiles_m, int tiles_n,
+                                                           SplitPlan sp) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -444,21 +468,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int grp = wave / 4, wq = wave % 4;
 
-  // tile of this workgroup: XCD-contiguous ids, then groups of kGroupM token tiles
-  int tm, tn;
+  // Tile of this workgroup.  The first sp.whole workgroups each take a whole
+  // tile, their ids renumbered XCD-contiguously (the dispatcher deals ids
+  // round-robin over the 8 XCDs, each with its own L2) before the grouped
+  // order.  The remaining workgroups split each of the last tiles into
+  // sp.parts contiguous K ranges and store fp32 partial tiles.
+  int tm, tn, part = -1, tail = 0;
+  int k_begin = 0, k_tiles = p.k / kBK;
   {
-    const int total = tiles_m * tiles_n;
     const int id = blockIdx.x;
-    const int xcd = id % 8, slot = id / 8;
-    const int q = total / 8, r = total % 8;
-    const int nid = xcd * q + min(xcd, r) + slot;
-    const int per_group = kGroupM * tiles_n;
-    const int g = nid / per_group;
-    const int first_m = g * kGroupM;
-    const int gsize = min(tiles_m - first_m, kGroupM);
-    const int in_g = nid - g * per_group;
-    tm = first_m + in_g % gsize;
-    tn = in_g / gsize;
+    if (id < sp.whole) {
+      const int xcd = id % 8, slot = id / 8;
+      const int q = sp.whole / 8, r = sp.whole % 8;
+      tile_of(xcd * q + min(xcd, r) + slot, tiles_m, tiles_n, tm, tn);
+    } else {
+      tail = (id - sp.whole) / sp.parts;
+      part = (id - sp.whole) % sp.parts;
+      tile_of(sp.whole + tail, tiles_m, tiles_n, tm, tn);
+      k_begin = part * k_tiles / sp.parts;
+      k_tiles = (part + 1) * k_tiles / sp.parts - k_begin;
+    }
   }
   const int64_t m0 = static_cast<int64_t>(tm) * kTM;
   const int n0 = tn * kTN;
@@ -482,17 +511,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
     w_vo[n] = static_cast<uint32_t>(static_cast<int64_t>(nr) * p.k * 2 + c * 16);
   }
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char_ptr)smem));
-  const int k_tiles = p.k / kBK;
-  // A piece of slice kt into its stage (dst is that piece's first byte).
+  // A piece of slice kt (of this workgroup's K range) into its stage (dst is
+  // that piece's first byte).
   auto issue_a = [&](int kt) {
     const uint32_t dst = lds_base + kOffA + (2 * a_half + kt % kAStages) * kHalfBytes;
-    const char* src = reinterpret_cast<const char*>(p.a) + static_cast<int64_t>(kt) * kRowBytes;
+    const char* src = reinterpret_cast<const char*>(p.a) + static_cast<int64_t>(k_begin + kt) * kRowBytes;
 #pragma unroll
     for (int n = 0; n < kLoadsHalf; ++n) lds_dma16(src, a_vo[n], dst + (wq * kLoadsHalf + n) * 1024);
   };
   auto issue_w = [&](int kt) {
     const uint32_t dst = lds_base + (kt % kWStages) * kTileW + w_half * kHalfBytes;
-    const char* src = reinterpret_cast<const char*>(p.w) + static_cast<int64_t>(kt) * kRowBytes;
+    const char* src = reinterpret_cast<const char*>(p.w) + static_cast<int64_t>(k_begin + kt) * kRowBytes;
 #pragma unroll
     for (int n = 0; n < kLoadsHalf; ++n) lds_dma16(src, w_vo[n], dst + (wq * kLoadsHalf + n) * 1024);
   };
@@ -590,7 +619,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p, int til
     }
   }
 
-  tile_epilogue<EPI>(p, acc, m0 + grp * 128, n0 + wq * 64, lane);
+  if (part < 0) {
+    tile_epilogue<EPI>(p, acc, m0 + grp * 128, n0 + wq * 64, lane);
+  } else {
+    // partial tile, row-major 256 x 256 fp32: row grp*128 + 16j + lane%16,
+    // columns wq*64 + 16i + 4*(lane/16) .. +3
+    float* dst = sp.partials + static_cast<int64_t>(tail * sp.parts + part) * (kTM * kTN) +
+                 (grp * 128 + lane % 16) * kTN + wq * 64 + 4 * (lane / 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(dst + j * 16 * kTN + i * 16) = acc[i][j];
+  }
+}
+
+// Sum of the K-split partial tiles of the last tiles, in K order (fixed:
+// deterministic), then the tile epilogue.  One thread per 4 adjacent output
+// features of one token row; 64 workgroups of 256 threads per tile.
+template <int EPI>
+__global__ __launch_bounds__(256) void split_fixup_kernel(GemmParams p, int tiles_m, int tiles_n, SplitPlan sp) {
+  const int tail = blockIdx.x / 64;
+  const int idx = (blockIdx.x % 64) * 256 + threadIdx.x;  // 0 .. 16383
+  const int r = idx / (kTN / 4), c = (idx % (kTN / 4)) * 4;
+  int tm, tn;
+  tile_of(sp.whole + tail, tiles_m, tiles_n, tm, tn);
+  const int64_t m = static_cast<int64_t>(tm) * kTM + r;
+  const int n = tn * kTN + c;
+  if (m >= p.m || n >= p.n) return;
+  const float* src = sp.partials + static_cast<int64_t>(tail * sp.parts) * (kTM * kTN) + r * kTN + c;
+  f32x4 sum = *reinterpret_cast<const f32x4*>(src);
+  for (int q = 1; q < sp.parts; ++q) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(q) * (kTM * kTN));
+    sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
+  }
+  float y[4] = {sum[0], sum[1], sum[2], sum[3]};
+  store_epilogue<EPI>(p, m, n, y);
 }
 
 }  // namespace big
@@ -680,6 +743,21 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int compute_units() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int cu = cached[dev].load(std::memory_order_relaxed);
+  if (cu == 0) {
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+      return 0;
+    cached[dev].store(cu, std::memory_order_relaxed);
+  }
+  return cu;
+}
+
 hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s) {
   if (p.m == 0) return hipSuccess;
   if (p.k <= 0 || p.k % 64 != 0) return hipErrorInvalidValue;  // the tiled kernels step K by 64
@@ -708,15 +786,41 @@ hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s) {
   if (p.m >= 4 * big::kTM && p.n >= big::kTN && p.k >= 256 && offsets_fit) {
     const int tiles_m = static_cast<int>((p.m + big::kTM - 1) / big::kTM);
     const int tiles_n = (p.n + big::kTN - 1) / big::kTN;
-    dim3 grid(tiles_m * tiles_n);
+    const int total = tiles_m * tiles_n;
+    // One workgroup per CU (160 KB of LDS each): a last round of f < CUs/2
+    // tiles would leave most CUs idle, so with scratch those f tiles are
+    // split along K over up to CUs/f workgroups (each >= 2 slices, at most 8
+    // parts) and a second kernel sums the partials in K order.
+    big::SplitPlan sp{total, 1, nullptr};
+    const int slots = compute_units();
+    const int f = slots > 0 ? total % slots : 0;
+    if (p.split_ws && f > 0 && 2 * f <= slots) {
+      int parts = std::min({slots / f, p.k / big::kBK / 2, 8, kMaxSplitParts / f});
+      if (parts >= 2) sp = big::SplitPlan{total - f, parts, p.split_ws};
+    }
+    const int n_wg = sp.whole + (total - sp.whole) * sp.parts;
+    dim3 grid(n_wg);
     dim3 block(big::kThreads);
     switch (epilogue) {
-      case EPI_BF16: hipLaunchKernelGGL(big::gemm_kernel<EPI_BF16>, grid, block, 0, s, p, tiles_m, tiles_n); break;
-      case EPI_GELU: hipLaunchKernelGGL(big::gemm_kernel<EPI_GELU>, grid, block, 0, s, p, tiles_m, tiles_n); break;
-      case EPI_SILU: hipLaunchKernelGGL(big::gemm_kernel<EPI_SILU>, grid, block, 0, s, p, tiles_m, tiles_n); break;
-      case EPI_F32: hipLaunchKernelGGL(big::gemm_kernel<EPI_F32>, grid, block, 0, s, p, tiles_m, tiles_n); break;
-      case EPI_GATED: hipLaunchKernelGGL(big::gemm_kernel<EPI_GATED>, grid, block, 0, s, p, tiles_m, tiles_n); break;
-      case EPI_RES: hipLaunchKernelGGL(big::gemm_kernel<EPI_RES>, grid, block, 0, s, p, tiles_m, tiles_n); break;
+      case EPI_BF16: hipLaunchKernelGGL(big::gemm_kernel<EPI_BF16>, grid, block, 0, s, p, tiles_m, tiles_n, sp); break;
+      case EPI_GELU: hipLaunchKernelGGL(big::gemm_kernel<EPI_GELU>, grid, block, 0, s, p, tiles_m, tiles_n, sp); break;
+      case EPI_SILU: hipLaunchKernelGGL(big::gemm_kernel<EPI_SILU>, grid, block, 0, s, p, tiles_m, tiles_n, sp); break;
+      case EPI_F32: hipLaunchKernelGGL(big::gemm_kernel<EPI_F32>, grid, block, 0, s, p, tiles_m, tiles_n, sp); break;
+      case EPI_GATED: hipLaunchKernelGGL(big::gemm_kernel<EPI_GATED>, grid, block, 0, s, p, tiles_m, tiles_n, sp); break;
+      case EPI_RES: hipLaunchKernelGGL(big::gemm_kernel<EPI_RES>, grid, block, 0, s, p, tiles_m, tiles_n, sp); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (sp.whole == total) return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 fgrid((total - sp.whole) * 64);
+    switch (epilogue) {
+      case EPI_BF16: hipLaunchKernelGGL(big::split_fixup_kernel<EPI_BF16>, fgrid, dim3(256), 0, s, p, tiles_m, tiles_n, sp); break;
+      case EPI_GELU: hipLaunchKernelGGL(big::split_fixup_kernel<EPI_GELU>, fgrid, dim3(256), 0, s, p, tiles_m, tiles_n, sp); break;
+      case EPI_SILU: hipLaunchKernelGGL(big::split_fixup_kernel<EPI_SILU>, fgrid, dim3(256), 0, s, p, tiles_m, tiles_n, sp); break;
+      case EPI_F32: hipLaunchKernelGGL(big::split_fixup_kernel<EPI_F32>, fgrid, dim3(256), 0, s, p, tiles_m, tiles_n, sp); break;
+      case EPI_GATED: hipLaunchKernelGGL(big::split_fixup_kernel<EPI_GATED>, fgrid, dim3(256), 0, s, p, tiles_m, tiles_n, sp); break;
+      case EPI_RES: hipLaunchKernelGGL(big::split_fixup_kernel<EPI_RES>, fgrid, dim3(256), 0, s, p, tiles_m, tiles_n, sp); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -19,7 +19,14 @@ struct GemmParams {
   const uint16_t* gate;
   int64_t gate_stride, gate_rows;
   int64_t group_rows, a_group_stride, c_group_stride;
+  // Optional fp32 scratch for splitting the last, partly filled round of
+  // large-GEMM tiles along K (null: no split).  kSplitWsBytes at least.
+  float* split_ws;
 };
+// Scratch for the K-split tail of the large GEMM: up to kMaxSplitParts
+// partial 256 x 256 fp32 tiles.
+constexpr int kMaxSplitParts = 256;
+constexpr size_t kSplitWsBytes = static_cast<size_t>(kMaxSplitParts) * 256 * 256 * 4;
 hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s);
 
 struct AttnParams {

@@ -182,6 +182,15 @@ typedef enum dit_epilogue {
  *         the gate rows it reads (DIT_EINVAL, nothing enqueued).
  *   gate  bf16, DIT_EPI_GATED_RES_F32 only: row r uses gate + (r / gate_rows)
  *         * gate_stride (gate_rows >= 1).
+ *   workspace  optional device scratch (NULL, or >= dit_linear_workspace_bytes()
+ *         bytes, 256-byte aligned, overlapping none of the other buffers;
+ *         DIT_EINVAL / DIT_EWORKSPACE otherwise).  With it, when the last
+ *         round of 256 x 256 output tiles would fill fewer than half of the
+ *         GPU's compute units, those tiles are split along K over several
+ *         workgroups and their fp32 partial sums added in K order by a second
+ *         kernel (deterministic; the summation order differs from the
+ *         unsplit path's).  Its contents are scratch: overwritten, not read
+ *         across calls; calls that share it must be ordered on one stream.
  * Requires k % 64 == 0 (DIT_EUNSUPPORTED otherwise), lda/ldc/strides multiples
  * of 8, pointers 16-byte aligned.  m, n >= 1 (m == 0 is a no-op). */
 typedef struct dit_linear_args {
@@ -197,8 +206,12 @@ typedef struct dit_linear_args {
   const uint16_t* gate;
   int64_t gate_stride, gate_rows;
   int64_t group_rows, a_group_stride, c_group_stride;
+  void* workspace;
+  size_t workspace_bytes;
 } dit_linear_args;
 
+/* Bytes of the optional dit_linear workspace (64 MiB: 256 partial tiles). */
+size_t dit_linear_workspace_bytes(void);
 dit_status dit_linear(const dit_linear_args* args, hipStream_t stream);
 
 /* Adaptive LayerNorm ("Difflet Engineering Report", Terms used in this

@@ -128,6 +128,20 @@ def test_linear_argument_errors():
             8, **g, stream=0)
     _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, FAKE * 4 + 16, 4, 8, 64, D.EPI_BF16, FAKE * 4, 8,
             stream=0)
+    # the optional K-split scratch: 256-byte aligned, at least
+    # dit_linear_workspace_bytes(), overlapping none of the operands or out
+    wsb = D.dit_linear_workspace_bytes()
+    assert wsb == 256 * 256 * 256 * 4
+    far = FAKE * 64
+    _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, D.EPI_BF16, FAKE * 4, 8,
+            workspace=far + 16, workspace_bytes=wsb, stream=0)
+    _expect("DIT_EWORKSPACE", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, D.EPI_BF16, FAKE * 4, 8,
+            workspace=far, workspace_bytes=wsb - 256, stream=0)
+    for clash in (FAKE, FAKE * 2, FAKE * 4):  # A, W, out inside the workspace's range
+        _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, D.EPI_BF16, FAKE * 4, 8,
+                workspace=clash - 256, workspace_bytes=wsb, stream=0)
+    _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, D.EPI_GATED_RES_F32, FAKE * 4, 8,
+            **g, workspace=FAKE * 5 - 256, workspace_bytes=wsb, stream=0)
     # m == 0 is a no-op that succeeds without touching the GPU
     f(FAKE, 64, FAKE * 2, None, 0, 8, 64, D.EPI_BF16, FAKE * 4, 8, stream=0)
 

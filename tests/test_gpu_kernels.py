@@ -109,6 +109,66 @@ def test_linear_large_tiles(M, N, K, epi):
     assert torch.equal(outs[0], outs[1]), "large-tile GEMM rerun differs"
 
 
+# With the optional workspace, the tiles of a last round that would fill fewer
+# than half of the compute units are split along K (up to 8 parts of >= 2
+# slices) and their fp32 partials summed in K order by a second kernel.  The
+# shape is chosen from the device's CU count so that 6-10 tiles spill into a
+# last round (266 tiles of 256 x 256 on 256 CUs; ragged M and N); K = 1024
+# splits each tail tile 8 ways, K = 320 (5 slices) into uneven parts of 2 and
+# 3.  Every epilogue against the oracle, bitwise-equal reruns, and the split
+# result compared with the unsplit one (same values up to fp32 summation
+# order; the f32 output must differ somewhere, i.e. the split path ran).
+@pytest.mark.parametrize("K", [1024, 320])
+@pytest.mark.parametrize("epi", ["bf16", "gelu", "f32", "gated", "res"])
+def test_linear_k_split_tail(K, epi):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles_n = 14
+    tiles_m = (cus + 6 + tiles_n - 1) // tiles_n
+    f = tiles_m * tiles_n % cus
+    assert 0 < 2 * f <= cus, (cus, tiles_m, f)
+    M, N = tiles_m * 256 - 40, tiles_n * 256 - 8
+    a, w, b = _gemm_case(500 + K, M, N, K)
+    y = O.linear(_dec(a), _dec(w), _dec(b))
+    da, dw, db = dev_bf16(a), dev_bf16(w), dev_bf16(b)
+    wsb = D.dit_linear_workspace_bytes()
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    code = {"bf16": D.EPI_BF16, "gelu": D.EPI_GELU_BF16, "f32": D.EPI_F32, "gated": D.EPI_GATED_RES_F32,
+            "res": D.EPI_RES_F32}[epi]
+    rows_g = M // 2 + 1
+    gate = G.normal_bf16(21, (2, N))
+    x0 = G.normal_bf16(22, (M, N))
+    if epi == "gated":
+        want = _dec(x0) + _dec(gate)[np.arange(M) // rows_g] * y
+    elif epi == "res":
+        want = _dec(x0) + y
+    else:
+        want = {"bf16": y, "gelu": O.gelu_erf(y), "f32": y}[epi]
+
+    def run(workspace):
+        if epi in ("gated", "res", "f32"):
+            out = dev_f32_from_bf16(x0) if epi != "f32" else torch.empty((M, N), device="cuda")
+        else:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        kw = dict(gate=dev_bf16(gate), gate_stride=N, gate_rows=rows_g) if epi == "gated" else {}
+        D.dit_linear(da, K, dw, db, M, N, K, code, out, N, workspace=workspace,
+                     workspace_bytes=wsb if workspace is not None else 0, **kw)
+        return out
+
+    split1, split2, whole = run(ws), run(ws), run(None)
+    torch.cuda.synchronize()
+    got = host(split1)
+    if epi in ("bf16", "gelu"):
+        assert_bf16_ulp(got, want, f"k-split {epi} {M}x{N}x{K}")
+    else:
+        assert_parity(got, want, f"k-split {epi} {M}x{N}x{K}", max_abs=1e-4 * np.abs(want).max(),
+                      rel_l2=1e-5)
+    assert torch.equal(split1, split2), "k-split rerun differs"
+    d = (split1.float() - whole.float()).abs().max().item()
+    assert d <= 1e-4 * float(np.abs(want).max()) + (2 ** -7 * float(np.abs(want).max()) if epi in ("bf16", "gelu") else 0)
+    if epi == "f32":
+        assert not torch.equal(split1, whole), "the split path did not run"
+
+
 # M <= 8 token rows (the conditioning MLP and modulation projections) run the
 # matrix-vector kernel: every epilogue, row counts 1..8, K below and above one
 # 512-wide wave step, grouped rows, bitwise-equal reruns.
