@@ -334,10 +334,11 @@ def hbm_probe(steps, reps=None):
             fn()
         torch.cuda.synchronize()
         if reps:
-            ms = timed(fn, reps, torch.cuda.current_stream())
+            st = timed_stats(fn, reps, torch.cuda.current_stream())
+            ms = st["ms"]
             result[name] = {"us": round(ms * 1e3, 2), "algorithmic_bytes": int(nbytes),
                             "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 8e12, 4)}
+                            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 8e12, 4), "timing": st}
     del x, h, qkv, outs, lses, o, feat, saved, wmod
     torch.cuda.empty_cache()
     if not reps:
@@ -388,12 +389,14 @@ def block_gemms(reps, stream):
         ours()
         ref()
         flop = 2.0 * M * n * k
-        ms_o = timed(ours, reps, stream)
-        ms_r = timed(ref, reps, stream)
+        st_o = timed_stats(ours, reps, stream)
+        st_r = timed_stats(ref, reps, stream)
+        ms_o, ms_r = st_o["ms"], st_r["ms"]
         out[name] = {"m": M, "n": n, "k": k, "ms": round(ms_o, 3),
                      "tflops": round(flop / (ms_o * 1e-3) / 1e12, 1),
                      "hipblaslt_ms": round(ms_r, 3),
-                     "hipblaslt_tflops": round(flop / (ms_r * 1e-3) / 1e12, 1)}
+                     "hipblaslt_tflops": round(flop / (ms_r * 1e-3) / 1e12, 1),
+                     "timing": st_o, "hipblaslt_timing": st_r}
         del a, w, bias, y, gate, wt
     del ws
     torch.cuda.empty_cache()
@@ -441,11 +444,12 @@ def mmdit_blocks(reps, stream):
         D.dit_double_block_forward(desc, bwi, bwt, mi, mt, xi, xt, ws, nb)
 
     dbl()
-    ms = timed(dbl, reps, stream)
+    st = timed_stats(dbl, reps, stream)
+    ms = st["ms"]
     M = B * (S + L)
     fl = 2.0 * M * Dh * 4 * Dh + 2.0 * M * Dh * F * 2 + attn
     out["double_block"] = {"ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-                           "algorithmic_tflop": round(fl / 1e12, 3)}
+                           "algorithmic_tflop": round(fl / 1e12, 3), "timing": st}
     del wi, wt, bwi, bwt, xi, xt, ws
     # single stream
     desc = D.block_desc(s, valid, 3 * Dh)
@@ -462,10 +466,11 @@ def mmdit_blocks(reps, stream):
         D.dit_single_block_forward(desc, sw, mod, x, ws, nb)
 
     sgl()
-    ms = timed(sgl, reps, stream)
+    st = timed_stats(sgl, reps, stream)
+    ms = st["ms"]
     fl = 2.0 * M * Dh * (3 * Dh + F) + 2.0 * M * (Dh + F) * Dh + attn
     out["single_block"] = {"ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-                           "algorithmic_tflop": round(fl / 1e12, 3)}
+                           "algorithmic_tflop": round(fl / 1e12, 3), "timing": st}
     out["shape"] = ("FLUX-like 1024x1024: 4096 image + 512 text tokens (valid 77, 512), hidden 3072, "
                     "24x128, MLP 12288, batch 2")
     return out
@@ -512,10 +517,11 @@ def other_configs(reps, stream):
             D.dit_block_forward(desc, w, mod, x, ws, nb)
 
         blk()
-        ms = timed(blk, max(10, reps), stream)
+        st = timed_stats(blk, max(10, reps), stream)
+        ms = st["ms"]
         fl = block_flops(s, valid)
         out[key] = {"ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-                    "algorithmic_tflop": round(fl / 1e12, 4), "txt_valid": valid}
+                    "algorithmic_tflop": round(fl / 1e12, 4), "txt_valid": valid, "timing": st}
         del w, mod, x, ws
 
     s = C.C4
@@ -639,13 +645,14 @@ def wan_block(reps, stream):
         D.dit_wan_block_forward(desc, ww, mod, x, ctx, ws, nb)
 
     run()
-    ms = timed(run, reps, stream)
+    st = timed_stats(run, reps, stream)
+    ms = st["ms"]
     M = B * S
     fl = (2.0 * M * Dh * 4 * Dh + attention_flops(S, S, s.heads, s.head_dim, B)
           + 2.0 * M * Dh * 2 * Dh + 2.0 * B * L * Dh * 2 * Dh
           + sum(attention_flops(S, v, s.heads, s.head_dim) for v in valid) + 2.0 * M * Dh * F * 2)
     return {"ms": round(ms, 3), "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-            "algorithmic_tflop": round(fl / 1e12, 3),
+            "algorithmic_tflop": round(fl / 1e12, 3), "timing": st,
             "shape": "Wan 480p: 32760 video tokens, 512 context slots (226 valid), hidden 5120, "
                      "40x128, MLP 13824, batch 1"}
 
@@ -733,8 +740,9 @@ def main():
     cached(0, D.STEP_FULL, 0)
     cached(1, D.STEP_FULL, 1)
     probe()
-    ms_probe = timed(probe, max(5, args.steps), stream)
-    ms_skip = timed(lambda: cached(2, D.STEP_SKIP, 1), max(5, args.steps), stream)
+    st_probe = timed_stats(probe, max(5, args.steps), stream)
+    st_skip = timed_stats(lambda: cached(2, D.STEP_SKIP, 1), max(5, args.steps), stream)
+    ms_probe, ms_skip = st_probe["ms"], st_skip["ms"]
     feat_n = blk.batch * blk.n_tok * blk.hidden
     cur_f = torch.randn(feat_n, generator=torch.Generator("cuda").manual_seed(6),
                         device="cuda").to(torch.bfloat16)
@@ -744,7 +752,8 @@ def main():
         D.dit_change_score(cur_f, saved, D.DTYPE_BF16, feat_n, 1, pscore, sws, sws.numel())
 
     change_score()
-    ms_score = timed(change_score, max(5, args.steps), stream)
+    st_score = timed_stats(change_score, max(5, args.steps), stream)
+    ms_score = st_score["ms"]
     score_bytes = 3 * feat_n * 2  # read current and saved, write saved
 
     def cadence_loop():
@@ -836,8 +845,9 @@ def main():
     split()
     torch.cuda.synchronize()
     split_err = (o_split.float() - o.float()).abs().max().item()
-    ms_split = timed(split, max(3, args.steps // 2), stream)
-    ms_merge = timed(split_merge, max(5, args.steps), stream)
+    st_split = timed_stats(split, max(3, args.steps // 2), stream)
+    st_merge = timed_stats(split_merge, max(5, args.steps), stream)
+    ms_split, ms_merge = st_split["ms"], st_merge["ms"]
     del p_out, p_lse, o_split
 
     gemms = block_gemms(max(3, args.steps // 2), stream)
@@ -888,6 +898,7 @@ def main():
             "merge_ms": round(ms_merge, 3),
             "tflops": round(a_flop / (ms_split * 1e-3) / 1e12, 1),
             "max_abs_vs_unsplit": round(split_err, 5),
+            "timing": st_split, "merge_timing": st_merge,
         },
         "step_cache": {
             "probe_ms": round(ms_probe, 3),
@@ -898,6 +909,7 @@ def main():
             "cadence2_loop_ms_per_step": round(ms_loop, 3),
             "cadence2_full_steps": int(n_full_loop),
             "steps": shape.steps,
+            "timing": {"probe": st_probe, "skip_step": st_skip, "change_score": st_score},
         },
         "block_gemms": gemms,
         "hbm_kernels": hbm,
