@@ -278,7 +278,10 @@ size_t dit_block_workspace_bytes(const dit_block_desc* desc);
  * batch row, row stride desc->mod_stride (0 = one vector for all rows).
  * Activations h, qkv, o, h2 and the MLP hidden are bf16 in `workspace`
  * (>= dit_block_workspace_bytes(desc), 256-byte aligned); the residual stream
- * stays fp32. */
+ * stays fp32.  For B * N >= 1024 the workspace also holds the 64 MiB of
+ * scratch the GEMMs use to split an under-filled last round of tiles along K
+ * (see dit_linear); the double, single and Wan blocks' workspaces do the
+ * same. */
 dit_status dit_block_forward(const dit_block_desc* desc,
                              const dit_block_weights* w, const uint16_t* mod,
                              float* x, void* workspace, size_t workspace_bytes,
