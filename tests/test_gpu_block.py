@@ -87,6 +87,42 @@ def test_block_c3_sampled():
     _block_sampled(C.C3, 32)
 
 
+def _attention_sampled_strided(s, n_random, q_scale):
+    """Joint attention at a full-size shape with q, k, v as the column blocks
+    of one [B, N, 3*H*d] buffer (the block's layout, as the bench times it),
+    compared on sampled query rows with the fp64 oracle at the strict bar."""
+    inp = G.attention_inputs(s, q_scale=q_scale)
+    B, N, H, d = s.batch, s.n_tok, s.heads, s.head_dim
+    HD = H * d
+    qkv = torch.empty((B, N, 3 * HD), dtype=torch.bfloat16, device="cuda")
+    for i, name in enumerate(("q", "k", "v")):
+        qkv[..., i * HD:(i + 1) * HD].copy_(dev_bf16(inp[name]))
+    out = torch.empty((B, N, HD), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    desc = D.attn_desc(B, s.n_vis, s.n_txt, H, d, inp["txt_valid"])
+    D.dit_joint_attention(desc, qkv, qkv[..., HD:], qkv[..., 2 * HD:], 3 * HD, out, HD, lse)
+    torch.cuda.synchronize()
+    rows = sample_rows(s.n_vis, s.n_txt, inp["txt_valid"], n_random=n_random, seed=s.seed)
+    qo = O.bf16_decode(inp["q"][:, rows]).reshape(B, len(rows), H, d)
+    ko = O.bf16_decode(inp["k"]).reshape(B, N, H, d)
+    vo = O.bf16_decode(inp["v"]).reshape(B, N, H, d)
+    o, l = O.joint_attention(qo, ko, vo, s.n_vis, inp["txt_valid"])
+    what = f"{s.name} attention, q x {q_scale:g} (sampled)"
+    print(f"{what}: {len(rows)} sampled rows", flush=True)
+    assert_parity(host(out)[:, rows], o.reshape(B, len(rows), HD), what)
+    assert_parity(host(lse)[:, :, rows], l, f"{s.name} lse, q x {q_scale:g} (sampled)", max_abs=1e-3,
+                  rel_l2=1e-5)
+
+
+# The bench's headline attention: c3 (32,760 + 512 tokens, 226 valid, 40 x 128)
+# in the block's strided QKV layout, with N(0, 1) q (nearly flat softmax rows)
+# and with q x 4 (peaked rows, more running-max rescales).
+@pytest.mark.slow
+@pytest.mark.parametrize("q_scale", [1.0, 4.0])
+def test_attention_c3_sampled(q_scale):
+    _attention_sampled_strided(C.C3.attn(), 24, q_scale)
+
+
 @pytest.mark.slow
 def test_attention_c4_sampled():
     s = C.C4
