@@ -59,6 +59,16 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;        // keys per tile
 constexpr int kStages = 4;     // LDS ring depth
 constexpr int kBM = kWaves * 32;  // queries per workgroup (32 per wave)
+// Value MFMAs of an MFMA phase issued after the barrier that ends it.  A wave
+// reaches a workgroup barrier only once its issued MFMAs have drained, so
+// with the phase's last MFMAs on the far side the matrix pipe stays busy
+// across the hand-over to the other wave of the SIMD (measured: a two-wave
+// ping-pong of 32 MFMAs per phase loses 97 cycles per barrier with 0
+// trailing MFMAs, 53 with 2, 91 with 4).
+#ifndef DIT_ATTN_TRAIL
+#define DIT_ATTN_TRAIL 2
+#endif
+constexpr int kTrail = DIT_ATTN_TRAIL;
 
 template <int D>
 struct Tile {
@@ -159,6 +169,8 @@ struct WaveState {
   bf16x8 pf[4];       // p of one tile as the B operand of four 16-key value steps
   float m_run;        // running max of the scaled scores (log2 domain)
   float m_tile;       // max of the scaled scores of the tile in s (this lane's query)
+  float mx[4];        // the four partial max chains of the tile in s
+  bf16x8 vt[kTrail > 0 ? kTrail : 1];  // V^T fragments of the value MFMAs issued after the phase barrier
   float l_run;        // this lane's partial sum of p
   int k_off[kKS];     // K fragment byte offsets within a stage (row lane%32)
   int v_off[2][kDB];  // V^T transposing-read byte offsets (rows 8g + 4*hi + s16/4)
@@ -183,6 +195,25 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Step i (0..15) of the tile max: 32 scores -> 1 in 16 v_max3 on four
+// independent chains (chain i % 4 covers 8 scores of one 16-row group).
+template <int D>
+__device__ __forceinline__ void tile_max_step(WaveState<D>& st, int i) {
+  const int c4 = i % 4, k = i / 4;
+  const int t = c4 / 2, r0 = 8 * (c4 % 2);
+  if (k == 0) st.mx[c4] = vmax3(st.s[t][r0], st.s[t][r0 + 1], st.s[t][r0 + 2]);
+  else if (k == 1) st.mx[c4] = vmax3(st.mx[c4], st.s[t][r0 + 3], st.s[t][r0 + 4]);
+  else if (k == 2) st.mx[c4] = vmax3(st.mx[c4], st.s[t][r0 + 5], st.s[t][r0 + 6]);
+  else st.mx[c4] = vmax3(st.mx[c4], st.s[t][r0 + 7], st.s[t][r0 + 7]);
+  asm volatile("" : "+v"(st.mx[c4]));  // keep the step here, not sunk to the end of the phase
+}
+
+template <int D>
+__device__ __forceinline__ void tile_max_finish(WaveState<D>& st, float c) {
+  // c > 0 keeps the order
+  st.m_tile = max_halves(vmax3(st.mx[0], st.mx[1], vmax3(st.mx[2], st.mx[3], st.mx[3]))) * c;
+}
+
 // MFMA phase: S^T of key tile j+1 (sK = its K stage; absent after the last
 // tile), then O^T += V^T P^T for tile j (sV = its V stage; absent before the
 // first tile).  LDS reads and MFMAs, with independent VALU work of this wave
@@ -193,7 +224,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 // of tile j+1's max.  Fragment reads run a fixed number of steps ahead of
 // their MFMA (scheduling fences keep the compiler from hoisting all 32 of
 // them, which would cost 128 VGPRs).
-template <int D, bool kPVPart, bool kQKPart>
+template <int D, bool kPVPart, bool kQKPart, int kTr = 0>
 __device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, const char* sV, float c) {
   using T = Tile<D>;
   using W = WaveState<D>;
@@ -250,16 +281,7 @@ __device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, con
   // as copies of the last valid key's row, so those scores repeat a valid
   // one and leave the max unchanged (the softmax phase masks them before
   // exponentiating).
-  float mx[4];
-  auto max_step = [&](int i) {
-    const int c4 = i % 4, k = i / 4;
-    const int t = c4 / 2, r0 = 8 * (c4 % 2);
-    if (k == 0) mx[c4] = vmax3(st.s[t][r0], st.s[t][r0 + 1], st.s[t][r0 + 2]);
-    else if (k == 1) mx[c4] = vmax3(mx[c4], st.s[t][r0 + 3], st.s[t][r0 + 4]);
-    else if (k == 2) mx[c4] = vmax3(mx[c4], st.s[t][r0 + 5], st.s[t][r0 + 6]);
-    else mx[c4] = vmax3(mx[c4], st.s[t][r0 + 7], st.s[t][r0 + 7]);
-    asm volatile("" : "+v"(mx[c4]));  // keep the step here, not sunk to the end of the phase
-  };
+  auto max_step = [&](int i) { tile_max_step(st, i); };
   if constexpr (kQKPart) {
     if constexpr (!kPVPart) {
 #pragma unroll
@@ -281,8 +303,9 @@ __device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, con
     bf16x8 vf[kPV];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) vf[i] = vread(i);
+    static_assert(kTr <= kAhead, "trailing fragments must already be read");
 #pragma unroll
-    for (int i = 0; i < kPV; ++i) {
+    for (int i = 0; i < kPV - kTr; ++i) {
       if (i + kAhead < kPV) vf[i + kAhead] = vread(i + kAhead);
       __builtin_amdgcn_sched_barrier(0);
       st.o[i % W::kDB] = mfma32x32x16(vf[i], st.pf[i / W::kDB], st.o[i % W::kDB]);
@@ -292,11 +315,30 @@ __device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, con
         for (int n = 0; n < kPer; ++n) max_step(i * kPer + n);
       }
     }
+#pragma unroll
+    for (int j = 0; j < kTr; ++j) st.vt[j] = vf[kPV - kTr + j];
   }
-  if constexpr (kQKPart) {
-    // c > 0 keeps the order
-    st.m_tile = max_halves(vmax3(mx[0], mx[1], vmax3(mx[2], mx[3], mx[3]))) * c;
+  if constexpr (kQKPart && kTr == 0) tile_max_finish(st, c);
+}
+
+// The last kTr value MFMAs of an MFMA phase (their V^T fragments already in
+// st.vt), issued right after the barrier that ends the phase, then the rest
+// of the tile max.
+template <int D, bool kQKPart, int kTr>
+__device__ __forceinline__ void mfma_tail(WaveState<D>& st, float c) {
+  using W = WaveState<D>;
+  constexpr int kPV = 4 * W::kDB;
+#pragma unroll
+  for (int j = 0; j < kTr; ++j) {
+    const int i = kPV - kTr + j;
+    st.o[i % W::kDB] = mfma32x32x16(st.vt[j], st.pf[i / W::kDB], st.o[i % W::kDB]);
+    if constexpr (kQKPart) {
+      constexpr int kPer = 16 / kPV;
+#pragma unroll
+      for (int n = 0; n < kPer; ++n) tile_max_step(st, i * kPer + n);
+    }
   }
+  if constexpr (kQKPart) tile_max_finish(st, c);
 }
 
 // Softmax phase for key tile j (keys j0 .. j0+63), whose max the MFMA phase
@@ -508,14 +550,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // tile m (issued at phase 2m-4; only tile m+1's are newer) before barrier
   // 2m.
   constexpr int L4 = 2 * T::kLoads4;  // loads per loading wave per tile
-  auto phase_barrier = [&](bool duty, int m) {
+  auto barrier_wait = [&](bool duty, int m) {
     duty = duty && !a_grp_c;
     if (duty && m >= 3 && m < n_tiles) {
       if (m + 1 < n_tiles) wait_vmcnt<L4>(); else wait_vmcnt<0>();
     }
     __builtin_amdgcn_s_barrier();
+  };
+  auto barrier_issue = [&](bool duty, int m) {
+    duty = duty && !a_grp_c;
     if (duty && m >= 1 && m + 2 < n_tiles)
       issue_tile<D, T::kLoads4>(kg0, vg0, stride_bytes, m + 2, n_valid, lds_base, wave % 4, lane, voff4);
+  };
+  auto phase_barrier = [&](bool duty, int m) {
+    barrier_wait(duty, m);
+    barrier_issue(duty, m);
   };
   auto stage = [&](int j) { return smem + (j % kStages) * T::kStageBytes; };
   // A wave in its MFMA phase runs at raised issue priority: when both waves
@@ -539,9 +588,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   for (int k = 0; k + 1 < n_tiles; ++k) {
     phase_barrier(a_grp, k + 1);
     mfma_prio(true);
-    mfma_phase<D, true, true>(st, stage(k + 1), stage(k) + T::kBytes, c);
+    mfma_phase<D, true, true, kTrail>(st, stage(k + 1), stage(k) + T::kBytes, c);
+    barrier_wait(!a_grp, k + 2);
+    mfma_tail<D, true, kTrail>(st, c);  // keeps the matrix pipe busy across the hand-over
     mfma_prio(false);
-    phase_barrier(!a_grp, k + 2);
+    barrier_issue(!a_grp, k + 2);
     softmax_phase<D>(st, (k + 1) * kBN, n_valid, hi, c);
   }
   phase_barrier(a_grp, n_tiles);
