@@ -41,9 +41,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
 # WRITE x1.0); summary and commands in profiles/attn_c3_hbm_traffic.md.  Valid
 # only for the kernel source they were taken on.
 ATTN_TRAFFIC = {
-    "source_sha256": "6156725ca5379de8faf8a1f8f9f28a3bf9e10d4384f2673c1dcb1b61aadf15ac",
-    "fetch_bytes": 3.7189e9,
-    "write_bytes": 0.3410e9,
+    "source_sha256": "b1ad8034477eac8432016ba028e4228f96d872c5a4c716e76c5ca925f7bacef2",
+    "fetch_bytes": 3.7195e9,
+    "write_bytes": 0.3409e9,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     "profile": "profiles/attn_c3_hbm_traffic.md",
