@@ -35,11 +35,15 @@
 // and the modulation projections) stream W once without tiles.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
 
 namespace dit {
+
+int compute_units();
+
 namespace {
 
 constexpr int kTN = 128;  // W rows (output features) per workgroup
@@ -86,18 +90,11 @@ __device__ __forceinline__ int64_t c_row_offset(const GemmParams& p, int64_t r) 
                           : r * p.ldc;
 }
 
-// y[0..3] = acc for output features n..n+3 of token row m: add the bias, apply
-// the epilogue and store (8-byte bf16 or 16-byte fp32 accesses).
+// Features n..n+3 of token row m (output row offset crow) from y[0..3], the
+// bias already added: apply the epilogue and store (8-byte bf16 or 16-byte
+// fp32 accesses).
 template <int EPI>
-__device__ __forceinline__ void store_epilogue(const GemmParams& p, int64_t m, int n, float (&y)[4]) {
-  const int64_t crow = c_row_offset(p, m);
-  if (p.bias) {
-    const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
-    y[0] += __uint_as_float(bb[0] << 16);
-    y[1] += __uint_as_float(bb[0] & 0xffff0000u);
-    y[2] += __uint_as_float(bb[1] << 16);
-    y[3] += __uint_as_float(bb[1] & 0xffff0000u);
-  }
+__device__ __forceinline__ void store_row(const GemmParams& p, int64_t m, int64_t crow, int n, float (&y)[4]) {
   if (EPI == EPI_GELU) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = gelu(y[e]);
@@ -130,6 +127,20 @@ __device__ __forceinline__ void store_epilogue(const GemmParams& p, int64_t m, i
     o[1] = pack_bf16x2(y[2], y[3]);
     *reinterpret_cast<u32x2*>(dst) = o;
   }
+}
+
+// y[0..3] = acc for output features n..n+3 of token row m: add the bias, apply
+// the epilogue and store.
+template <int EPI>
+__device__ __forceinline__ void store_epilogue(const GemmParams& p, int64_t m, int n, float (&y)[4]) {
+  if (p.bias) {
+    const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
+    y[0] += __uint_as_float(bb[0] << 16);
+    y[1] += __uint_as_float(bb[0] & 0xffff0000u);
+    y[2] += __uint_as_float(bb[1] << 16);
+    y[3] += __uint_as_float(bb[1] & 0xffff0000u);
+  }
+  store_row<EPI>(p, m, c_row_offset(p, m), n, y);
 }
 
 // The epilogue of one wave's 128 (tokens) x 64 (features) block of a
@@ -741,6 +752,304 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
 
 }  // namespace gemv
 
+// ---------------------------------------------------------------------------
+// Few output features (N <= 64) over a long K: the projection of the final
+// hidden states to the latent channels.  The product is a stream over A (the
+// W rows are L2-resident), so the kernel is built to read A once at HBM rate:
+// a workgroup takes TG x 16 token rows and all (up to 64) features, its 4
+// waves split K in four contiguous ranges, and each wave streams its range of
+// A and W straight into registers (no LDS staging), the next 64-k chunk in
+// flight while the current one is multiplied.  The four fp32 partial tiles
+// are then summed through LDS in wave order (fixed: deterministic).
+namespace thin_n {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLdP = 64 + 4;  // padded partial row (floats): row r starts 4 bank groups after row r-1
+
+template <int EPI, int TG>
+__global__ __launch_bounds__(kThreads, TG > 4 ? 1 : 2) void gemm_kernel(GemmParams p) {
+  constexpr int kRows = 16 * TG;
+  __shared__ __attribute__((aligned(16))) float part[kWaves * kRows * kLdP];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int r = lane % 16, q = lane / 16;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kRows;
+
+  // Operand rows of this lane: token m0 + 16j + r (clamped: rows past m are
+  // computed, never stored), feature 16i + r (clamped likewise); 16-byte
+  // chunk q of each 32-k step.
+  const int kw = p.k / kWaves;  // a multiple of 64
+  const int64_t kb = static_cast<int64_t>(wave) * kw;
+  const uint16_t* arow[TG];
+#pragma unroll
+  for (int j = 0; j < TG; ++j) {
+    int64_t m = m0 + 16 * j + r;
+    if (m > p.m - 1) m = p.m - 1;
+    arow[j] = p.a + a_row_offset(p, m) + kb + 8 * q;
+  }
+  const uint16_t* wrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wrow[i] = p.w + static_cast<int64_t>(min(16 * i + r, p.n - 1)) * p.k + kb + 8 * q;
+
+  f32x4 acc[4][TG];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  bf16x8 a0[2][TG], w0[2][4], a1[2][TG], w1[2][4];
+  auto load = [&](bf16x8 (&af)[2][TG], bf16x8 (&wf)[2][4], int c) {
+    const int ko = 64 * c;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int j = 0; j < TG; ++j) af[ks][j] = *reinterpret_cast<const bf16x8*>(arow[j] + ko + 32 * ks);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wf[ks][i] = *reinterpret_cast<const bf16x8*>(wrow[i] + ko + 32 * ks);
+    }
+  };
+  auto mma = [&](const bf16x8 (&af)[2][TG], const bf16x8 (&wf)[2][4]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TG; ++j) acc[i][j] = mfma16x16x32(wf[ks][i], af[ks][j], acc[i][j]);
+  };
+  const int chunks = kw / 64;
+  load(a0, w0, 0);
+  int c = 0;
+  for (; c + 2 <= chunks; c += 2) {
+    load(a1, w1, c + 1);
+    mma(a0, w0);
+    if (c + 2 < chunks) load(a0, w0, c + 2);
+    mma(a1, w1);
+  }
+  if (c < chunks) mma(a0, w0);
+
+  // Partial tile of this wave: acc[i][j][e] = sum over its K range for token
+  // row 16j + r and feature 16i + 4q + e.
+  float* mine = part + wave * kRows * kLdP;
+#pragma unroll
+  for (int j = 0; j < TG; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(mine + (16 * j + r) * kLdP + 16 * i + 4 * q) = acc[i][j];
+  __syncthreads();
+
+  // Sum in wave (K) order and store: thread t takes row t / (256 / kRows)
+  // and kFeat consecutive features of it.
+  static_assert(kThreads % kRows == 0, "whole rows per thread group");
+  constexpr int kPerRow = kThreads / kRows;  // threads per row: 2, 4 or 8
+  constexpr int kFeat = 64 / kPerRow;        // features per thread: 32, 16 or 8
+  const int row = threadIdx.x / kPerRow;
+  const int f0 = (threadIdx.x % kPerRow) * kFeat;
+  const int64_t m = m0 + row;
+  if (m >= p.m) return;
+  const int64_t crow = c_row_offset(p, m);
+#pragma unroll
+  for (int g = 0; g < kFeat / 4; ++g) {
+    const int n = f0 + 4 * g;
+    if (n >= p.n) break;
+    const float* src = part + row * kLdP + n;
+    f32x4 s = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + w * kRows * kLdP);
+      s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+    }
+    float y[4] = {s[0], s[1], s[2], s[3]};
+    if (p.bias) {
+      const u32x2 bb = *reinterpret_cast<const u32x2*>(p.bias + n);
+      y[0] += __uint_as_float(bb[0] << 16);
+      y[1] += __uint_as_float(bb[0] & 0xffff0000u);
+      y[2] += __uint_as_float(bb[1] << 16);
+      y[3] += __uint_as_float(bb[1] & 0xffff0000u);
+    }
+    store_row<EPI>(p, m, crow, n, y);
+  }
+}
+
+template <int EPI>
+hipError_t launch(const GemmParams& p, hipStream_t s) {
+  // The largest workgroup (128, 64 or 32 rows) of which there are at least
+  // as many as compute units: every wave's W fragments serve more rows.
+  const int64_t cu = compute_units() > 0 ? compute_units() : 256;
+  if ((p.m + 127) / 128 >= cu) {
+    hipLaunchKernelGGL((gemm_kernel<EPI, 8>), dim3(static_cast<unsigned>((p.m + 127) / 128)), dim3(kThreads), 0, s, p);
+  } else if ((p.m + 63) / 64 >= cu) {
+    hipLaunchKernelGGL((gemm_kernel<EPI, 4>), dim3(static_cast<unsigned>((p.m + 63) / 64)), dim3(kThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<EPI, 2>), dim3(static_cast<unsigned>((p.m + 31) / 32)), dim3(kThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace thin_n
+
+// ---------------------------------------------------------------------------
+// A short K (64 or 128) onto many output features: the input projection of
+// the latent channels to the hidden width.  The product is a stream of
+// stores (the fp32 output is ~64x larger than the operands), so the kernel
+// is built to keep the stores flowing.  A workgroup takes a contiguous range
+// of 32-row token blocks and 256 output features: it first copies the A rows
+// of its whole range into LDS (at most 40 KB), then each wave, holding the W
+// rows of its 64 features in registers for the whole kernel, walks the
+// blocks: fragments from LDS, MFMAs, stores.  The loop issues no global
+// loads, so no wait in it ever covers the stores (the vector-memory counter
+// completes in issue order, loads and stores alike).
+namespace thin_k {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLdsBytes = 40 * 1024;
+
+// A and C offsets of token row m (m < 2^31, checked by the launcher: 32-bit
+// row arithmetic).
+__device__ __forceinline__ void row_offsets(const GemmParams& p, uint32_t m, int64_t& a_off, int64_t& c_off) {
+  if (p.group_rows > 0) {
+    const uint32_t g = m / static_cast<uint32_t>(p.group_rows);
+    const uint32_t i = m - g * static_cast<uint32_t>(p.group_rows);
+    a_off = g * p.a_group_stride + static_cast<int64_t>(i) * p.lda;
+    c_off = g * p.c_group_stride + static_cast<int64_t>(i) * p.ldc;
+  } else {
+    a_off = static_cast<int64_t>(m) * p.lda;
+    c_off = static_cast<int64_t>(m) * p.ldc;
+  }
+}
+
+// LDS position of 16-byte chunk c of staged row R (rows of KS * 64 bytes):
+// chunks are XOR-swizzled by row so that the 16 rows one fragment read
+// touches fall in distinct bank groups (16 bytes each, 16 per clock).
+template <int KS>
+__device__ __forceinline__ int lds_chunk(int R, int c) {
+  return KS == 2 ? (c ^ ((R >> 1) & 7)) : (c ^ (R & 15));
+}
+
+template <int EPI, int KS>  // KS = K / 32
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p, int m_blocks, int per_wg) {
+  constexpr int kRowBytes = KS * 64;
+  constexpr int kChunks = kRowBytes / 16;  // 8 or 16 per row
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int r = lane % 16, q = lane / 16;
+  const int b0 = blockIdx.y * per_wg;
+  const int nb = min(per_wg, m_blocks - b0);
+
+  // Stage the A rows of blocks b0 .. b0 + nb - 1 (rows past m clamped: computed, never stored).
+  {
+    const int chunks = nb * 32 * kChunks;
+    for (int c0 = 0; c0 < chunks; c0 += kThreads * 4) {
+      u32x4 v[4];
+      int pos[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + u * kThreads + threadIdx.x;
+        pos[u] = -1;
+        if (c < chunks) {
+          const int R = c / kChunks, ch = c % kChunks;
+          const uint32_t m = static_cast<uint32_t>(min(static_cast<int64_t>(b0) * 32 + R, p.m - 1));
+          int64_t a_off, c_off;
+          row_offsets(p, m, a_off, c_off);
+          v[u] = *reinterpret_cast<const u32x4*>(p.a + a_off + ch * 8);
+          pos[u] = R * kRowBytes + lds_chunk<KS>(R, ch) * 16;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (pos[u] >= 0) *reinterpret_cast<u32x4*>(smem + pos[u]) = v[u];
+    }
+  }
+  __syncthreads();
+
+  const int n_base = (blockIdx.x * kWaves + wave) * 64;
+  if (n_base >= p.n) return;  // no barriers below: a wave past n just ends
+  const bool n_full = n_base + 64 <= p.n;
+
+  bf16x8 wf[4][KS];
+  u32x2 bias[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t nr = min(n_base + 16 * i + r, p.n - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) wf[i][ks] = *reinterpret_cast<const bf16x8*>(p.w + nr * p.k + 32 * ks + 8 * q);
+    const int n = n_base + 16 * i + 4 * q;
+    bias[i] = (p.bias && n < p.n) ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0u, 0u};
+  }
+
+  // Block t of the range: acc[i][jj][e] is token row 32(b0 + t) + 16jj + r,
+  // feature n_base + 16i + 4q + e.  kChecked: rows past m and features past
+  // n are skipped (the last block, a wave at the end of n).
+  auto block = [&](int t, auto checked) {
+    constexpr bool kChecked = decltype(checked)::value;
+    bf16x8 af[2][KS];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int R = t * 32 + 16 * jj + r;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        af[jj][ks] = *reinterpret_cast<const bf16x8*>(smem + R * kRowBytes + lds_chunk<KS>(R, 4 * ks + q) * 16);
+    }
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        acc[i][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc[i][jj] = mfma16x16x32(wf[i][ks], af[jj][ks], acc[i][jj]);
+      }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int64_t m = static_cast<int64_t>(b0 + t) * 32 + 16 * jj + r;
+      if (kChecked && m >= p.m) continue;
+      int64_t a_off, c_off;
+      row_offsets(p, static_cast<uint32_t>(m), a_off, c_off);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n_base + 16 * i + 4 * q;
+        if (kChecked && n >= p.n) continue;
+        float y[4] = {acc[i][jj][0] + __uint_as_float(bias[i][0] << 16),
+                      acc[i][jj][1] + __uint_as_float(bias[i][0] & 0xffff0000u),
+                      acc[i][jj][2] + __uint_as_float(bias[i][1] << 16),
+                      acc[i][jj][3] + __uint_as_float(bias[i][1] & 0xffff0000u)};
+        store_row<EPI>(p, m, c_off, n, y);
+      }
+    }
+  };
+  using Unchecked = std::integral_constant<bool, false>;
+  using Checked = std::integral_constant<bool, true>;
+  // whole blocks (every row below m) unchecked when the wave's features are all in range
+  const int whole = min(nb, static_cast<int>(p.m / 32) - b0);
+  int t = 0;
+  if (n_full)
+    for (; t < whole; ++t) block(t, Unchecked{});
+  for (; t < nb; ++t) block(t, Checked{});
+}
+
+template <int EPI>
+hipError_t launch(const GemmParams& p, hipStream_t s) {
+  const int m_blocks = static_cast<int>((p.m + 31) / 32);
+  const int nx = (p.n + 64 * kWaves - 1) / (64 * kWaves);
+  const int cu = compute_units();
+  // blocks per workgroup: about 4 workgroups per compute unit, within the LDS
+  const int max_per = kLdsBytes / (32 * 2 * p.k);
+  const int64_t want = (static_cast<int64_t>(m_blocks) * nx + 4 * (cu > 0 ? cu : 256) - 1) /
+                       (4 * (cu > 0 ? cu : 256));
+  const int per_wg = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(max_per, want)));
+  const dim3 grid(nx, (m_blocks + per_wg - 1) / per_wg);
+  if (p.k == 64)
+    hipLaunchKernelGGL((gemm_kernel<EPI, 2>), grid, dim3(kThreads), 0, s, p, m_blocks, per_wg);
+  else if (p.k == 128)
+    hipLaunchKernelGGL((gemm_kernel<EPI, 4>), grid, dim3(kThreads), 0, s, p, m_blocks, per_wg);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace thin_k
+
 }  // namespace
 
 // Compute units of the current device (cached per device; 0 if unknown).
@@ -770,6 +1079,21 @@ hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s) {
       case EPI_F32: return gemv::launch<EPI_F32>(p, s);
       case EPI_GATED: return gemv::launch<EPI_GATED>(p, s);
       case EPI_RES: return gemv::launch<EPI_RES>(p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  // Few features over a long K (the projection to the latent channels) and
+  // a short K onto many features (the projection from them): stream kernels.
+  const int thin = p.n <= 64 && p.k >= 1024 && p.k % 256 == 0 && p.m >= 256 ? 1
+                   : (p.k == 64 || p.k == 128) && p.n >= 256 && p.m >= 1024 && p.m < (int64_t{1} << 31) ? 2 : 0;
+  if (thin) {
+    switch (epilogue) {
+      case EPI_BF16: return thin == 1 ? thin_n::launch<EPI_BF16>(p, s) : thin_k::launch<EPI_BF16>(p, s);
+      case EPI_GELU: return thin == 1 ? thin_n::launch<EPI_GELU>(p, s) : thin_k::launch<EPI_GELU>(p, s);
+      case EPI_SILU: return thin == 1 ? thin_n::launch<EPI_SILU>(p, s) : thin_k::launch<EPI_SILU>(p, s);
+      case EPI_F32: return thin == 1 ? thin_n::launch<EPI_F32>(p, s) : thin_k::launch<EPI_F32>(p, s);
+      case EPI_GATED: return thin == 1 ? thin_n::launch<EPI_GATED>(p, s) : thin_k::launch<EPI_GATED>(p, s);
+      case EPI_RES: return thin == 1 ? thin_n::launch<EPI_RES>(p, s) : thin_k::launch<EPI_RES>(p, s);
       default: return hipErrorInvalidValue;
     }
   }

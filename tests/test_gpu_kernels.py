@@ -52,17 +52,9 @@ def test_linear_epilogues(M, N, K, epi):
         assert_bf16_ulp(got, ref, f"linear {epi} {M}x{N}x{K}")
 
 
-# Shapes with M >= 1024, N >= 256 and K >= 256 run the large-tile kernel
-# (256 x 256 workgroup tiles, 64-wide K slices streamed through a 3-stage W
-# ring and 2-stage A rings): ragged M and N, 4 to 8 K slices (every residue of
-# the slice count modulo both ring depths), every epilogue, bitwise-equal
-# reruns.  (Smaller K falls to the small-tile kernel: the
-# (1031, 264, 64) shape checks that routing.)
-@pytest.mark.parametrize("M,N,K", [(1100, 520, 256), (1031, 264, 384), (2304, 512, 320),
-                                   (1100, 520, 448), (2304, 512, 512), (1031, 264, 64)])
-@pytest.mark.parametrize("epi", ["bf16", "gelu", "f32", "gated", "res"])
-def test_linear_large_tiles(M, N, K, epi):
-    a, w, b = _gemm_case(200 + M + K, M, N, K)
+def _linear_every_epilogue(M, N, K, epi, seed, what):
+    """One linear layer through dit_linear twice (bitwise-equal reruns) against the oracle."""
+    a, w, b = _gemm_case(seed, M, N, K)
     y = O.linear(_dec(a), _dec(w), _dec(b))
     da, dw, db = dev_bf16(a), dev_bf16(w), dev_bf16(b)
     if epi == "res":
@@ -74,7 +66,7 @@ def test_linear_large_tiles(M, N, K, epi):
             D.dit_linear(da, K, dw, db, M, N, K, D.EPI_RES_F32, x, N)
             outs.append(x)
         torch.cuda.synchronize()
-        assert_parity(host(outs[0]), want, f"large residual {M}x{N}x{K}",
+        assert_parity(host(outs[0]), want, f"{what} residual {M}x{N}x{K}",
                       max_abs=1e-4 * np.abs(want).max(), rel_l2=1e-5)
     elif epi == "gated":
         rows_g = M // 2 + 1
@@ -88,7 +80,7 @@ def test_linear_large_tiles(M, N, K, epi):
                          gate_stride=N, gate_rows=rows_g)
             outs.append(x)
         torch.cuda.synchronize()
-        assert_parity(host(outs[0]), want, f"large gated {M}x{N}x{K}",
+        assert_parity(host(outs[0]), want, f"{what} gated {M}x{N}x{K}",
                       max_abs=1e-4 * np.abs(want).max(), rel_l2=1e-5)
     else:
         code = {"bf16": D.EPI_BF16, "gelu": D.EPI_GELU_BF16, "f32": D.EPI_F32}[epi]
@@ -101,12 +93,80 @@ def test_linear_large_tiles(M, N, K, epi):
         torch.cuda.synchronize()
         got = host(outs[0])
         if epi == "f32":
-            assert_parity(got, y, f"large f32 {M}x{N}x{K}", max_abs=1e-4 * np.abs(y).max(),
+            assert_parity(got, y, f"{what} f32 {M}x{N}x{K}", max_abs=1e-4 * np.abs(y).max(),
                           rel_l2=1e-5)
         else:
             ref = {"bf16": y, "gelu": O.gelu_erf(y)}[epi]
-            assert_bf16_ulp(got, ref, f"large {epi} {M}x{N}x{K}")
-    assert torch.equal(outs[0], outs[1]), "large-tile GEMM rerun differs"
+            assert_bf16_ulp(got, ref, f"{what} {epi} {M}x{N}x{K}")
+    assert torch.equal(outs[0], outs[1]), f"{what} GEMM rerun differs"
+
+
+# Shapes with M >= 1024, N >= 256 and K >= 256 run the large-tile kernel
+# (256 x 256 workgroup tiles, 64-wide K slices streamed through a 3-stage W
+# ring and 2-stage A rings): ragged M and N, 4 to 8 K slices (every residue of
+# the slice count modulo both ring depths), every epilogue, bitwise-equal
+# reruns.  (K = 64 with N >= 256 and M >= 1024 goes to the short-K stream
+# kernel instead: the (1031, 264, 64) shape checks that routing.)
+@pytest.mark.parametrize("M,N,K", [(1100, 520, 256), (1031, 264, 384), (2304, 512, 320),
+                                   (1100, 520, 448), (2304, 512, 512), (1031, 264, 64)])
+@pytest.mark.parametrize("epi", ["bf16", "gelu", "f32", "gated", "res"])
+def test_linear_large_tiles(M, N, K, epi):
+    _linear_every_epilogue(M, N, K, epi, 200 + M + K, "large")
+
+
+# Few features over a long K (N <= 64, K >= 1024 and a multiple of 256,
+# M >= 256: the projection to the latent channels) runs the long-K stream
+# kernel: K split over the 4 waves of a workgroup (odd and even chunk counts
+# per wave), on 256 compute units 32-row workgroups up to 16383 rows, 64-row
+# ones up to 32640 (20000 and 17000 rows), 128-row ones above (33000), N not
+# a multiple of 16.
+@pytest.mark.parametrize("M,N,K", [(300, 64, 1024), (1000, 56, 2048), (20000, 64, 1280),
+                                   (17000, 16, 1024), (33000, 40, 1280)])
+@pytest.mark.parametrize("epi", ["bf16", "gelu", "f32", "gated", "res"])
+def test_linear_long_k_few_features(M, N, K, epi):
+    _linear_every_epilogue(M, N, K, epi, 300 + M + N, "long-K stream")
+
+
+# A short K onto many features (K of 64 or 128, N >= 256, M >= 1024: the
+# projection from the latent channels) runs the short-K stream kernel: W rows
+# held in registers, 32-row token blocks walked with a stride, ragged M and N
+# (a partly and a wholly out-of-range wave of 64 features).
+@pytest.mark.parametrize("M,N,K", [(1100, 520, 64), (3001, 256, 128), (2051, 1288, 64)])
+@pytest.mark.parametrize("epi", ["bf16", "gelu", "f32", "gated", "res"])
+def test_linear_short_k_many_features(M, N, K, epi):
+    _linear_every_epilogue(M, N, K, epi, 400 + M + N, "short-K stream")
+
+
+def test_linear_stream_kernels_grouped_rows():
+    """The two projections of a denoising step in their real addressing: the
+    input projection reads one shared block of latent rows for two batch rows
+    (a_group_stride 0) and writes the visual rows of each batch row, leaving
+    the text rows between them untouched; the output projection reads the
+    visual rows of each batch row out of [batch, n_vis + n_txt, D] and writes
+    them contiguously."""
+    nv, nt, C, Dh = 1500, 37, 64, 512
+    lat, w_in, b_in = _gemm_case(51, nv, Dh, C)
+    y_in = O.linear(_dec(lat), _dec(w_in), _dec(b_in))
+    x = torch.full((2, nv + nt, Dh), float("nan"), dtype=torch.float32, device="cuda")
+    D.dit_linear(dev_bf16(lat), C, dev_bf16(w_in), dev_bf16(b_in), 2 * nv, Dh, C, D.EPI_F32, x, Dh,
+                 group_rows=nv, a_group_stride=0, c_group_stride=(nv + nt) * Dh)
+    torch.cuda.synchronize()
+    got = host(x)
+    assert np.isnan(got[:, nv:]).all(), "text rows were written by the input projection"
+    for bi in range(2):
+        assert_parity(got[bi, :nv], y_in, f"input projection rows of batch row {bi}",
+                      max_abs=1e-4 * np.abs(y_in).max(), rel_l2=1e-5)
+
+    Dk = 1024
+    h = G.normal_bf16(52, (2, nv + nt, Dk))
+    w_out = G.normal_bf16(53, (C, Dk), 0.05)
+    b_out = G.normal_bf16(54, (C,), 0.5)
+    want = np.stack([O.linear(_dec(h[bi, :nv]), _dec(w_out), _dec(b_out)) for bi in range(2)])
+    v = torch.empty((2, nv, C), dtype=torch.bfloat16, device="cuda")
+    D.dit_linear(dev_bf16(h), Dk, dev_bf16(w_out), dev_bf16(b_out), 2 * nv, C, Dk, D.EPI_BF16, v, C,
+                 group_rows=nv, a_group_stride=(nv + nt) * Dk, c_group_stride=nv * C)
+    torch.cuda.synchronize()
+    assert_bf16_ulp(host(v), want, "output projection of the visual rows")
 
 
 # With the optional workspace, the tiles of a last round that would fill fewer
