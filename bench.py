@@ -35,15 +35,16 @@ if ROOT not in sys.path:
 METRIC = "DiT block ms/step + joint-attn TFLOP/s (% bf16 MFMA peak) @32760+512 tok"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
 
-# HBM traffic of one c3 joint-attention launch from two rocprofv3 counter
-# passes (FETCH_SIZE, then WRITE_SIZE, of `bench.py --traffic-probe`), scaled
-# by what the same counters read for a plain 1 GiB device copy (FETCH x2.0,
-# WRITE x1.0); summary and commands in profiles/attn_c3_hbm_traffic.md.  Valid
-# only for the kernel source they were taken on.
+# HBM traffic of one c3 joint-attention call (the attention kernel and the
+# merge of its split last round) from two rocprofv3 counter passes
+# (FETCH_SIZE, then WRITE_SIZE, of `bench.py --traffic-probe`), scaled by what
+# the same counters read for a plain 1 GiB device copy (FETCH x2.0, WRITE
+# x1.0); summary and commands in profiles/attn_c3_hbm_traffic.md.  Valid only
+# for the kernel source they were taken on.
 ATTN_TRAFFIC = {
-    "source_sha256": "b1ad8034477eac8432016ba028e4228f96d872c5a4c716e76c5ca925f7bacef2",
-    "fetch_bytes": 3.7195e9,
-    "write_bytes": 0.3409e9,
+    "source_sha256": "b61e689cf4ce45f34bc78c1e86885d00819876efbccc01a5035a5f83de02d991",
+    "fetch_bytes": 3.8464e9,
+    "write_bytes": 0.3732e9,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     "profile": "profiles/attn_c3_hbm_traffic.md",
@@ -126,10 +127,11 @@ class ClockSampler:
     limit), which the roofline fractions against the nominal peak include.
     Reading that file asks the power-management firmware; at a 5 ms period
     it stretched a 30-call run of the 2.3 ms c2 block from 2.27 to 2.34 ms
-    per call (p90 2.30 -> 2.44), so the period is kept long and the first
-    read comes one period into the region."""
+    per call (p90 2.30 -> 2.44), so after a first read 5 ms into the region
+    (short regions still get one) the period is kept long."""
 
-    def __init__(self, period_s=0.02):
+    def __init__(self, period_s=0.02, first_s=0.005):
+        self.first = first_s
         import glob
         self.path = next(iter(sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))), None)
         self.period = period_s
@@ -151,10 +153,12 @@ class ClockSampler:
         self._stop = threading.Event()
         if self.path:
             def run():
-                while not self._stop.wait(self.period):
+                wait = self.first
+                while not self._stop.wait(wait):
                     v = self._read()
                     if v is not None:
                         self.samples.append(v)
+                    wait = self.period
             self._t = threading.Thread(target=run, daemon=True)
             self._t.start()
         return self
@@ -254,8 +258,11 @@ def traffic_probe(steps):
     qkv = torch.randn((blk.batch, blk.n_tok, 3 * HD), generator=g, device="cuda").to(torch.bfloat16)
     o = torch.empty((blk.batch, blk.n_tok, HD), dtype=torch.bfloat16, device="cuda")
     adesc = D.attn_desc(blk.batch, blk.n_vis, blk.n_txt, blk.heads, blk.head_dim, [226])
+    wsb = D.dit_joint_attention_workspace_bytes()
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     for _ in range(steps):
-        D.dit_joint_attention(adesc, qkv, qkv[..., HD:], qkv[..., 2 * HD:], 3 * HD, o, HD)
+        D.dit_joint_attention(adesc, qkv, qkv[..., HD:], qkv[..., 2 * HD:], 3 * HD, o, HD,
+                              workspace=ws, workspace_bytes=wsb)
     torch.cuda.synchronize()
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -532,9 +539,12 @@ def other_configs(reps, stream):
     q, k, v = (rnd(s.batch, s.n_tok, HD) for _ in range(3))
     o = torch.empty_like(q)
     adesc = D.attn_desc(s.batch, s.n_vis, s.n_txt, s.heads, s.head_dim, [300])
+    a_wsb = D.dit_joint_attention_workspace_bytes()
+    a_ws = torch.empty(a_wsb, dtype=torch.uint8, device="cuda")
 
     def attn():
-        D.dit_joint_attention(adesc, q, k, v, HD, o, HD)
+        # (11920 query tiles on 256 CUs: a last round over half full, not split)
+        D.dit_joint_attention(adesc, q, k, v, HD, o, HD, workspace=a_ws, workspace_bytes=a_wsb)
 
     attn()
     st = timed_stats(attn, max(3, reps // 2), stream)
@@ -798,9 +808,15 @@ def main():
                       device="cuda").to(torch.bfloat16)
     o = torch.empty((blk.batch, blk.n_tok, HD), dtype=torch.bfloat16, device="cuda")
     adesc = D.attn_desc(blk.batch, blk.n_vis, blk.n_txt, blk.heads, blk.head_dim, inp.txt_valid)
+    # with the workspace the block passes it (an under-filled last round of
+    # query tiles -- 80 of 5200 on 256 CUs -- splits along the keys; the
+    # timed call includes the merge of those partials)
+    a_wsb = D.dit_joint_attention_workspace_bytes()
+    a_ws = torch.empty(a_wsb, dtype=torch.uint8, device="cuda")
 
     def attn():
-        D.dit_joint_attention(adesc, qkv, qkv[..., HD:], qkv[..., 2 * HD:], 3 * HD, o, HD)
+        D.dit_joint_attention(adesc, qkv, qkv[..., HD:], qkv[..., 2 * HD:], 3 * HD, o, HD,
+                              workspace=a_ws, workspace_bytes=a_wsb)
 
     attn()
     st_attn = timed_stats(attn, max(5, args.steps), stream)
@@ -921,7 +937,8 @@ def main():
         "other_configs": others,
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_kernel<128, false> (joint attention)",
+            "kernel": "attn_kernel<128, false> + tail_merge_kernel<128> (joint attention; the "
+                      "under-filled last round of query tiles split along the keys and merged)",
             "achieved": round(a_tflops, 1),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

@@ -20,7 +20,8 @@ STATUS = {0: "DIT_OK", 1: "DIT_EINVAL", 2: "DIT_EUNSUPPORTED", 3: "DIT_EWORKSPAC
 EPI_BF16, EPI_GELU_BF16, EPI_SILU_BF16, EPI_F32, EPI_GATED_RES_F32, EPI_RES_F32 = range(6)
 
 EXPORTED = (
-    "dit_joint_attention", "dit_attention_partial", "dit_attention_merge", "dit_linear_workspace_bytes",
+    "dit_joint_attention", "dit_joint_attention_workspace_bytes", "dit_attention_partial",
+    "dit_attention_merge", "dit_linear_workspace_bytes",
     "dit_linear", "dit_adaln_modulate", "dit_qk_rmsnorm_rope",
     "dit_block_workspace_bytes", "dit_block_forward", "dit_euler_step",
     "dit_timestep_features", "dit_cast_f32_bf16", "dit_cast_bf16_f32", "dit_debug_positions",
@@ -145,7 +146,9 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, f32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_int
         sig = {
-            "dit_joint_attention": (st, [ctypes.POINTER(AttnDesc), vp, vp, vp, i64, vp, i64, vp, f32, vp]),
+            "dit_joint_attention": (st, [ctypes.POINTER(AttnDesc), vp, vp, vp, i64, vp, i64, vp, f32, vp,
+                                         ctypes.c_size_t, vp]),
+            "dit_joint_attention_workspace_bytes": (ctypes.c_size_t, []),
             "dit_attention_partial": (st, [ctypes.POINTER(PartialDesc), vp, i64, vp, vp, i64, vp, i64,
                                            vp, f32, vp]),
             "dit_attention_merge": (st, [ctypes.POINTER(MergeDesc), ctypes.POINTER(vp), i64,
@@ -243,10 +246,14 @@ def block_desc(shape, txt_valid, mod_stride=None) -> BlockDesc:
 
 
 def dit_joint_attention(desc: AttnDesc, q, k, v, qkv_row_stride, out, out_row_stride,
-                        lse=None, softmax_scale=0.0, stream=None):
+                        lse=None, softmax_scale=0.0, workspace=None, workspace_bytes=0, stream=None):
     _check(lib().dit_joint_attention(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), qkv_row_stride,
                                      _ptr(out), out_row_stride, _ptr(lse), softmax_scale,
-                                     _stream(stream)))
+                                     _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def dit_joint_attention_workspace_bytes() -> int:
+    return int(lib().dit_joint_attention_workspace_bytes())
 
 
 def partial_desc(batch, n_q, n_k, heads, head_dim, k_valid) -> PartialDesc:

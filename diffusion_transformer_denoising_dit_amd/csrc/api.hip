@@ -274,6 +274,7 @@ hipError_t block_launch(const dit_block_desc* desc, const dit_block_weights* w, 
   for (int b = 0; b < DIT_MAX_BATCH; ++b)
     ap.n_valid[b] = b < B ? desc->attn.n_vis + desc->attn.txt_valid[b] : 0;
   ap.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(desc->attn.head_dim));
+  ap.tail_ws = split;
   e = dit::launch_attention(ap, stream);
   if (e != hipSuccess) { *what = "block: attention"; return e; }
   // 5. x += gate1 * (o W_o^T + b_o)
@@ -385,10 +386,12 @@ const char* dit_status_string(dit_status s) {
   return "unknown dit_status";
 }
 
+size_t dit_joint_attention_workspace_bytes(void) { return dit::kAttnTailWsBytes; }
+
 dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q, const uint16_t* k,
                                const uint16_t* v, int64_t qkv_row_stride, uint16_t* out,
                                int64_t out_row_stride, float* lse, float softmax_scale,
-                               hipStream_t stream) {
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   dit_status s = check_attn_desc(desc);
   if (s != DIT_OK) return s;
   if (!q || !k || !v || !out) return fail(DIT_EINVAL, "NULL q, k, v or out");
@@ -414,13 +417,24 @@ dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q, con
   if (overlap(out, out_bytes, q, in_bytes) || overlap(out, out_bytes, k, in_bytes) ||
       overlap(out, out_bytes, v, in_bytes))
     return fail(DIT_EINVAL, "out overlaps q, k or v");
+  const size_t lse_bytes = lse ? static_cast<size_t>(desc->batch) * desc->heads * n_tok * 4 : 0;
   if (lse) {
-    const size_t lse_bytes = static_cast<size_t>(desc->batch) * desc->heads * n_tok * 4;
     if (overlap(lse, lse_bytes, out, out_bytes) || overlap(lse, lse_bytes, q, in_bytes) ||
         overlap(lse, lse_bytes, k, in_bytes) || overlap(lse, lse_bytes, v, in_bytes))
       return fail(DIT_EINVAL, "lse overlaps q, k, v or out");
   }
+  if (workspace) {
+    if (!aligned(workspace, 256)) return fail(DIT_EINVAL, "workspace not 256-byte aligned");
+    if (workspace_bytes < dit::kAttnTailWsBytes)
+      return fail(DIT_EWORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, dit::kAttnTailWsBytes);
+    const size_t wb = dit::kAttnTailWsBytes;
+    if (overlap(workspace, wb, q, in_bytes) || overlap(workspace, wb, k, in_bytes) ||
+        overlap(workspace, wb, v, in_bytes) || overlap(workspace, wb, out, out_bytes) ||
+        (lse && overlap(workspace, wb, lse, lse_bytes)))
+      return fail(DIT_EINVAL, "workspace overlaps q, k, v, out or lse");
+  }
   dit::AttnParams p{};
+  p.tail_ws = static_cast<float*>(workspace);
   p.q = q;
   p.k = k;
   p.v = v;
@@ -780,6 +794,7 @@ dit_status dit_double_block_forward(const dit_block_desc* desc, const dit_block_
     ap.batch = B;
     for (int b = 0; b < DIT_MAX_BATCH; ++b) ap.n_valid[b] = b < B ? S + desc->attn.txt_valid[b] : 0;
     ap.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(desc->attn.head_dim));
+    ap.tail_ws = split;
     DIT_TRY(dit::launch_attention(ap, stream), "double block: attention");
   }
   // per stream: x += gate1 (o W_o^T + b_o)   (both read o before h2 reuses the buffer)
@@ -883,6 +898,7 @@ dit_status dit_single_block_forward(const dit_block_desc* desc, const dit_single
     for (int b = 0; b < DIT_MAX_BATCH; ++b)
       ap.n_valid[b] = b < B ? desc->attn.n_vis + desc->attn.txt_valid[b] : 0;
     ap.scale_log2 = 1.4426950408889634f / std::sqrt(static_cast<float>(desc->attn.head_dim));
+    ap.tail_ws = split;
     DIT_TRY(dit::launch_attention(ap, stream), "single block: attention");
   }
   // linear2 on [o | GELU(up)], gated residual
@@ -916,8 +932,9 @@ WanWs wan_ws(const dit_block_desc* d) {
 dit::AttnParams attn_params(const uint16_t* q, int64_t q_stride, int64_t q_batch, const uint16_t* k,
                             const uint16_t* v, int64_t kv_stride, int64_t kv_batch, uint16_t* out,
                             int64_t out_stride, int n_q, int n_k, const dit_attn_desc& a,
-                            const int* n_valid) {
+                            const int* n_valid, float* tail_ws) {
   dit::AttnParams ap{};
+  ap.tail_ws = tail_ws;
   ap.q = q; ap.k = k; ap.v = v;
   ap.q_stride = q_stride; ap.kv_stride = kv_stride;
   ap.q_batch = q_batch; ap.kv_batch = kv_batch;
@@ -986,7 +1003,7 @@ dit_status dit_wan_block_forward(const dit_block_desc* desc, const dit_wan_block
     for (int b = 0; b < DIT_MAX_BATCH; ++b) nv[b] = S;
     DIT_TRY(dit::launch_attention(attn_params(big, 3 * D, static_cast<int64_t>(S) * 3 * D, big + D, big + 2 * D,
                                               3 * D, static_cast<int64_t>(S) * 3 * D, hbuf, D, S, S,
-                                              desc->attn, nv),
+                                              desc->attn, nv, split),
                                   stream),
             "wan block: self-attention");
   }
@@ -1016,7 +1033,7 @@ dit_status dit_wan_block_forward(const dit_block_desc* desc, const dit_wan_block
   }
   DIT_TRY(dit::launch_attention(attn_params(big, D, static_cast<int64_t>(S) * D, ckv, ckv + D, 2 * D,
                                             static_cast<int64_t>(L) * 2 * D, hbuf, D, S, L > 0 ? L : 1,
-                                            desc->attn, desc->attn.txt_valid),
+                                            desc->attn, desc->attn.txt_valid, split),
                                 stream),
           "wan block: cross-attention");
   DIT_TRY(dit::launch_gemm(gemm(hbuf, D, w->w_co, w->b_co, M, D, D, x, D, split), DIT_EPI_RES_F32, stream),

@@ -46,6 +46,7 @@
 //    and O is divided by the sum once at the end.  The MFMA accumulators are
 //    VGPRs (the file is built with the VGPR form of MFMA) so the softmax
 //    phase reads the scores without AGPR copies.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -444,23 +445,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // pairs, query tile fastest.  The workgroups resident on one XCD then share
   // one head's K/V stream through that L2 (at c3 this halves the L2-miss
   // bytes of a launch) instead of every XCD streaming every head.
-  int b, h, qt;
+  // Workgroups past p.wg_main take one key range (part) of a query tile of
+  // the split last round instead: tile p.wg_main + (id - p.wg_main) / parts.
+  int b, h, qt, part = -1, tail = 0;
   {
     const int n_qt = (p.n_q + kBM - 1) / kBM;
-    const int total = n_qt * p.heads * p.batch;
+    const int total = p.wg_main;
     const int id = blockIdx.x;
-    const int xcd = id % 8, slot = id / 8;
-    const int per = total / 8, extra = total % 8;
-    const int nid = xcd * per + min(xcd, extra) + slot;
+    int nid;
+    if (id < total) {
+      const int xcd = id % 8, slot = id / 8;
+      const int per = total / 8, extra = total % 8;
+      nid = xcd * per + min(xcd, extra) + slot;
+    } else {
+      tail = (id - total) / p.tail_parts;
+      part = (id - total) % p.tail_parts;
+      nid = total + tail;
+    }
     qt = nid % n_qt;
     h = (nid / n_qt) % p.heads;
     b = nid / (n_qt * p.heads);
   }
   const int n_q = p.n_q;
-  const int n_valid = p.n_valid[b];
-  const int n_tiles = (n_valid + kBN - 1) / kBN;  // fully padded tiles are skipped
+  // Key tiles [tile0, tile0 + n_tiles) of the row's valid range, indexed
+  // from tile0 below (n_valid relative to it as well).
+  int n_tiles = (p.n_valid[b] + kBN - 1) / kBN;  // fully padded tiles are skipped
+  int tile0 = 0, n_valid = p.n_valid[b];
+  if (part >= 0) {
+    tile0 = part * n_tiles / p.tail_parts;
+    const int tile1 = (part + 1) * n_tiles / p.tail_parts;
+    n_valid = min(n_valid, tile1 * kBN) - tile0 * kBN;
+    n_tiles = tile1 - tile0;
+  }
   const int64_t q_base = static_cast<int64_t>(b) * p.q_batch + h * D;
-  const int64_t kv_base = static_cast<int64_t>(b) * p.kv_batch + h * D;
+  const int64_t kv_base = static_cast<int64_t>(b) * p.kv_batch + static_cast<int64_t>(tile0) * kBN * p.kv_stride + h * D;
   const char* kg0 = reinterpret_cast<const char*>(p.k + kv_base);
   const char* vg0 = reinterpret_cast<const char*>(p.v + kv_base);
   const int64_t stride_bytes = p.kv_stride * 2;
@@ -604,6 +622,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   // Combine the two lane halves' partial sums, normalise, store.
   const int q = q_first + lane % 32;
   const float l_tot = sum_halves(st.l_run);
+  if (part >= 0) {
+    // a key range of a split tile: fp32 normalised partial and its
+    // natural-log denominator, row (tail * parts + part) * 256 + query
+    if (q < n_q) {
+      const int64_t prow = (static_cast<int64_t>(tail) * p.tail_parts + part) * kBM + (q - qt * kBM);
+      const float inv = 1.f / l_tot;
+      float* dst = p.tail_o + prow * D;
+#pragma unroll
+      for (int db = 0; db < W::kDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = 32 * db + 8 * g + 4 * hi;
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = st.o[db][4 * g + e] * inv;
+          *reinterpret_cast<f32x4*>(dst + col) = w;
+        }
+      if (hi == 0) p.tail_lse[prow] = st.m_run * 0.69314718055994531f + logf(l_tot);
+    }
+    return;
+  }
   if (q < n_q) {
     const float inv = 1.f / l_tot;
     const int64_t row = (static_cast<int64_t>(b) * n_q + q) * p.out_stride + h * D;
@@ -630,12 +669,81 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
   }
 }
 
+// Merge of the split tiles' key-range partials: one thread per 4 output
+// elements of one query row; weights exp(lse_i - max lse) in fixed part
+// order (deterministic), bf16 output at the row's place, and the merged
+// log-denominator when the caller asked for it.
+template <int D>
+__global__ __launch_bounds__(256) void tail_merge_kernel(AttnParams p) {
+  constexpr int kC = D / 4;
+  const int n_qt = (p.n_q + kBM - 1) / kBM;
+  const int n_tail = n_qt * p.heads * p.batch - p.wg_main;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<int64_t>(n_tail) * kBM * kC) return;
+  const int c = static_cast<int>(idx % kC);
+  const int r = static_cast<int>((idx / kC) % kBM);
+  const int t = static_cast<int>(idx / (kC * kBM));
+  const int nid = p.wg_main + t;
+  const int qt = nid % n_qt, h = (nid / n_qt) % p.heads, b = nid / (n_qt * p.heads);
+  const int q = qt * kBM + r;
+  if (q >= p.n_q) return;
+  const int parts = p.tail_parts;
+  const int64_t row0 = static_cast<int64_t>(t) * parts * kBM + r;
+  float ls[kAttnMaxTailParts];
+  float lmax = -INFINITY;
+  for (int i = 0; i < parts; ++i) {
+    ls[i] = p.tail_lse[row0 + i * kBM];
+    lmax = fmaxf(lmax, ls[i]);
+  }
+  float wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < parts; ++i) {
+    const float w = expf(ls[i] - lmax);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(p.tail_o + (row0 + i * kBM) * D + 4 * c);
+    wsum += w;
+    acc[0] = fmaf(w, o[0], acc[0]);
+    acc[1] = fmaf(w, o[1], acc[1]);
+    acc[2] = fmaf(w, o[2], acc[2]);
+    acc[3] = fmaf(w, o[3], acc[3]);
+  }
+  const float inv = 1.f / wsum;
+  u32x2 out;
+  out[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  out[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  const int64_t orow = (static_cast<int64_t>(b) * p.n_q + q) * p.out_stride + h * D + 4 * c;
+  *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + orow) = out;
+  if (p.lse && c == 0) p.lse[(static_cast<int64_t>(b) * p.heads + h) * p.n_q + q] = lmax + logf(wsum);
+}
+
 }  // namespace
 
-hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
+hipError_t launch_attention(const AttnParams& p_in, hipStream_t s) {
+  AttnParams p = p_in;
   const int64_t n_wg = static_cast<int64_t>((p.n_q + kBM - 1) / kBM) * p.heads * p.batch;
-  if (n_wg * kThreads > 0xffffffffLL) return hipErrorInvalidValue;  // grid size in threads is 32-bit
-  dim3 grid(static_cast<unsigned>(n_wg));
+  // One 512-thread workgroup per CU (128 KB of LDS each): a last round of
+  // f <= CUs/2 query tiles after at least one full round leaves most CUs
+  // idle, so with scratch each of those f tiles is split into
+  // min(CUs/f, 4, fewest key tiles of a row) key ranges and merged after.
+  p.wg_main = static_cast<int>(n_wg);
+  p.tail_parts = 0;
+  p.tail_o = p.tail_lse = nullptr;
+  const int cu = compute_units();
+  const int f = cu > 0 ? static_cast<int>(n_wg % cu) : 0;
+  if (p.tail_ws && !p.out_f32 && cu > 0 && n_wg >= cu && f > 0 && 2 * f <= cu) {
+    int min_tiles = 1 << 30;
+    for (int b = 0; b < p.batch; ++b) min_tiles = std::min(min_tiles, (p.n_valid[b] + kBN - 1) / kBN);
+    // (f * parts <= 256 partial tiles: the size of the scratch)
+    const int parts = std::min({cu / f, 256 / f, kAttnMaxTailParts, min_tiles});
+    if (parts >= 2) {
+      p.wg_main = static_cast<int>(n_wg) - f;
+      p.tail_parts = parts;
+      p.tail_o = p.tail_ws;
+      p.tail_lse = p.tail_ws + static_cast<size_t>(f) * parts * kBM * p.head_dim;
+    }
+  }
+  const int64_t n_launch = p.wg_main + static_cast<int64_t>(n_wg - p.wg_main) * p.tail_parts;
+  if (n_launch * kThreads > 0xffffffffLL) return hipErrorInvalidValue;  // grid size in threads is 32-bit
+  dim3 grid(static_cast<unsigned>(n_launch));
   dim3 block(kThreads);
   if (p.head_dim == 128 && !p.out_f32)
     hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, 0, s, p);
@@ -647,6 +755,15 @@ hipError_t launch_attention(const AttnParams& p, hipStream_t s) {
     hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, 0, s, p);
   else
     return hipErrorInvalidValue;
+  if (p.tail_parts == 0) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = (n_wg - p.wg_main) * kBM * (p.head_dim / 4);
+  dim3 mgrid(static_cast<unsigned>((threads + 255) / 256));
+  if (p.head_dim == 128)
+    hipLaunchKernelGGL((tail_merge_kernel<128>), mgrid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((tail_merge_kernel<64>), mgrid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

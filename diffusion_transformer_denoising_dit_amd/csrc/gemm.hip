@@ -41,9 +41,6 @@
 #include "kernels.h"
 
 namespace dit {
-
-int compute_units();
-
 namespace {
 
 constexpr int kTN = 128;  // W rows (output features) per workgroup

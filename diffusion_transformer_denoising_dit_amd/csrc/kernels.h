@@ -28,6 +28,9 @@ struct GemmParams {
 constexpr int kMaxSplitParts = 256;
 constexpr size_t kSplitWsBytes = static_cast<size_t>(kMaxSplitParts) * 256 * 256 * 4;
 hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s);
+// Compute units of the current device (cached per device; 0 if unknown):
+// the launchers size their last-round splits by it.
+int compute_units();
 
 struct AttnParams {
   const uint16_t* q;
@@ -44,7 +47,22 @@ struct AttnParams {
   int n_q, n_k, heads, head_dim, batch;
   int n_valid[8];     // valid keys of batch row b: [0, n_valid[b]), n_valid[b] <= n_k
   float scale_log2;   // softmax scale * log2(e)
+  // Optional scratch (nullable, bf16 output only) for the split of an
+  // under-filled last round of query tiles along the keys; at least
+  // kAttnTailWsBytes, 256-byte aligned.
+  float* tail_ws;
+  // Set by launch_attention: workgroups [0, wg_main) take whole key ranges;
+  // each of the remaining query tiles is split into tail_parts key ranges
+  // whose fp32 partials (tail_o, tail_lse) a second kernel merges.
+  int wg_main, tail_parts;
+  float* tail_o;
+  float* tail_lse;
 };
+// Scratch of the split last round: at most 256 partial tiles of 256 query
+// rows, head_dim <= 128 fp32 values and one log-denominator each.
+constexpr int kAttnMaxTailParts = 4;
+constexpr size_t kAttnTailWsBytes = static_cast<size_t>(256) * 256 * (128 + 1) * 4;
+static_assert(kAttnTailWsBytes <= kSplitWsBytes, "the block workspaces' split scratch serves both");
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 
 struct MergeParams {

@@ -88,13 +88,27 @@ typedef struct dit_attn_desc {
  *   lse      nullable; fp32 [batch, heads, N]: natural-log softmax
  *            denominator of each row (max included), for merging partials.
  *   softmax_scale  0 -> 1/sqrt(head_dim).
+ *   workspace  optional device scratch (NULL, or >=
+ *            dit_joint_attention_workspace_bytes() bytes, 256-byte aligned,
+ *            not overlapping q, k, v, out or lse; else DIT_EWORKSPACE /
+ *            DIT_EINVAL).  With it, when the 256-query tiles of all rows and
+ *            heads fill the device's compute units at least once and leave a
+ *            last round at most half full, each tile of that round is split
+ *            into 2-4 key ranges attended separately and merged by their
+ *            log-denominators ("Difflet", section 4.3: the partial/merge
+ *            arithmetic of ring attention): the same weighted sum, up to fp32
+ *            and bf16 rounding of the partials (bitwise reproducible on one
+ *            device; the split depends on its compute-unit count).  Its
+ *            contents are overwritten and not read across calls.
  * Scores are accumulated in fp32 from bf16 inputs (MFMA), softmax statistics
  * are fp32, probabilities are rounded to bf16 for the value product. */
+size_t dit_joint_attention_workspace_bytes(void);
 dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q,
                                const uint16_t* k, const uint16_t* v,
                                int64_t qkv_row_stride, uint16_t* out,
                                int64_t out_row_stride, float* lse,
-                               float softmax_scale, hipStream_t stream);
+                               float softmax_scale, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 /* Split joint attention ("Difflet", section 4.3, Ring for joint attention):
  * the key set of each query is cut into partitions -- the text keys with

@@ -69,6 +69,18 @@ def test_attention_argument_errors():
     # query tiles x heads x batch beyond the kernel's 1-D grid (2^30 tokens, 8 heads, 8 rows)
     _expect("DIT_EUNSUPPORTED", f, _attn(batch=8, n_vis=(1 << 30) - 16, heads=8, valid=[4] * 8),
             FAKE, FAKE, FAKE, 1024, FAKE * 2, 1024, stream=0)
+    # optional workspace (the split of an under-filled last round): aligned,
+    # at least dit_joint_attention_workspace_bytes(), overlapping nothing
+    wsb = D.dit_joint_attention_workspace_bytes()
+    assert wsb >= 256 * 256 * 129 * 4
+    ws = FAKE * 8
+    _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE, FAKE, hd, FAKE * 2, hd, workspace=ws + 64,
+            workspace_bytes=wsb, stream=0)
+    msg = _expect("DIT_EWORKSPACE", f, _attn(), FAKE, FAKE, FAKE, hd, FAKE * 2, hd, workspace=ws,
+                  workspace_bytes=wsb - 256, stream=0)
+    assert str(wsb) in msg
+    _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE, FAKE, hd, FAKE * 2, hd, workspace=FAKE * 2 - 4096,
+            workspace_bytes=wsb, stream=0)
 
 
 def test_partial_attention_and_merge_argument_errors():

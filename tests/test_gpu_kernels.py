@@ -12,6 +12,7 @@ import diffusion_transformer_denoising_dit_amd as D
 import oracle as O
 from synthetic import configs as C
 from synthetic import gen as G
+from tests.sampling import sample_rows
 from tests.gpu_util import (assert_bf16_ulp, assert_parity, bits_of, dev_bf16,
                             dev_f32_from_bf16, host)
 
@@ -479,6 +480,85 @@ def test_attention_parity(shape, q_scale):
     o, l = _oracle_attention(shape, inp)
     assert_parity(host(out), o.reshape(host(out).shape), f"{shape.name} q*{q_scale} out")
     assert_parity(host(lse), l, f"{shape.name} lse", max_abs=1e-3, rel_l2=1e-5)
+
+
+# With a workspace, a last round of query tiles that fills at most half of
+# the compute units (after at least one full round; one 512-thread workgroup
+# per CU) is split along the keys into min(CUs/f, 4) ranges whose partials a
+# second kernel merges.  Shapes whose tile count leaves such a round on 256
+# CUs: 264 tiles (8 split 4 ways; head_dim 128 and 64) and 336 tiles of two
+# batch rows with different valid lengths (80 split 3 ways: the last range
+# holds the ragged bound).  Checked: against the oracle on sampled rows that
+# include the split tiles' rows, output and log-denominator at the strict
+# bar; bitwise equal to the call without workspace outside the split tiles,
+# not equal inside them (the split path ran); bitwise-equal reruns.
+SPLIT_SHAPES = [
+    C.AttnShape("split4_d128", batch=1, n_vis=8384, n_txt=64, heads=8, head_dim=128,
+                txt_valid=("fixed", (40,)), seed=47),
+    C.AttnShape("split3_b2", batch=2, n_vis=10600, n_txt=100, heads=4, head_dim=128,
+                txt_valid=("fixed", (37, 100)), seed=48),
+    C.AttnShape("split4_d64", batch=1, n_vis=8400, n_txt=48, heads=8, head_dim=64,
+                txt_valid=("fixed", (48,)), seed=49),
+]
+
+
+def _split_tiles(shape, cu):
+    """(b, h, query tile) of the tiles the launcher splits, [] if none."""
+    n_qt = -(-shape.n_tok // 256)
+    total = n_qt * shape.heads * shape.batch
+    f = total % cu
+    if total < cu or f == 0 or 2 * f > cu:
+        return []
+    return [(nid // (n_qt * shape.heads), (nid // n_qt) % shape.heads, nid % n_qt)
+            for nid in range(total - f, total)]
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=lambda s: s.name)
+def test_attention_split_last_round(shape):
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = _split_tiles(shape, cu)
+    if not tiles:
+        pytest.skip(f"{cu} compute units leave no under-filled last round at this shape")
+    inp = G.attention_inputs(shape, 2.0)
+    B, N, H, d, HD = shape.batch, shape.n_tok, shape.heads, shape.head_dim, shape.hidden
+    q, k, v = dev_bf16(inp["q"]), dev_bf16(inp["k"]), dev_bf16(inp["v"])
+    desc = D.attn_desc(B, shape.n_vis, shape.n_txt, H, d, inp["txt_valid"])
+    wsb = D.dit_joint_attention_workspace_bytes()
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    outs = []
+    for use_ws in (False, True, True):
+        out = torch.empty((B, N, HD), dtype=torch.bfloat16, device="cuda")
+        l = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        D.dit_joint_attention(desc, q, k, v, HD, out, HD, l, workspace=ws if use_ws else None,
+                              workspace_bytes=wsb if use_ws else 0)
+        outs.append((out, l))
+    torch.cuda.synchronize()
+    (o0, l0), (o1, l1), (o2, l2) = outs
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "split attention rerun differs"
+    in_split = np.zeros((B, N, H), bool)
+    for b, h, qt in tiles:
+        in_split[b, qt * 256:(qt + 1) * 256, h] = True
+    g0 = bits_of(o0).reshape(B, N, H, d)
+    g1 = bits_of(o1).reshape(B, N, H, d)
+    np.testing.assert_array_equal(g0[~in_split], g1[~in_split])
+    assert (g0[in_split] != g1[in_split]).any(), "the split path did not run"
+    lse0, lse1 = l0.cpu().numpy().transpose(0, 2, 1), l1.cpu().numpy().transpose(0, 2, 1)
+    np.testing.assert_array_equal(lse0[~in_split], lse1[~in_split])
+    # oracle rows: the sampled set plus 40 rows of every split tile's query range
+    rows = set(sample_rows(shape.n_vis, shape.n_txt, inp["txt_valid"], n_random=32, seed=shape.seed).tolist())
+    rng = np.random.default_rng(shape.seed)
+    for qt in sorted({t[2] for t in tiles}):
+        lo, hi = qt * 256, min(N, (qt + 1) * 256)
+        rows.update(int(r) for r in rng.integers(lo, hi, 40))
+    rows = np.array(sorted(rows), np.int64)
+    qo = _dec(inp["q"][:, rows]).reshape(B, len(rows), H, d)
+    ko = _dec(inp["k"]).reshape(B, N, H, d)
+    vo = _dec(inp["v"]).reshape(B, N, H, d)
+    o, lo_ = O.joint_attention(qo, ko, vo, shape.n_vis, inp["txt_valid"])
+    print(f"{shape.name}: {len(tiles)} split tiles, {int(in_split[:, rows].sum())} sampled "
+          f"(row, head) pairs inside them", flush=True)
+    assert_parity(host(o1)[:, rows], o.reshape(B, len(rows), HD), f"{shape.name} split out")
+    assert_parity(host(l1)[:, :, rows], lo_, f"{shape.name} split lse", max_abs=1e-3, rel_l2=1e-5)
 
 
 def test_attention_padding_is_ignored_bitwise():
