@@ -543,7 +543,7 @@ def other_configs(reps, stream):
     a_ws = torch.empty(a_wsb, dtype=torch.uint8, device="cuda")
 
     def attn():
-        # (11920 query tiles on 256 CUs: a last round over half full, not split)
+        # (11920 query tiles on 256 CUs: a last round of 144, split 3 ways)
         D.dit_joint_attention(adesc, q, k, v, HD, o, HD, workspace=a_ws, workspace_bytes=a_wsb)
 
     attn()

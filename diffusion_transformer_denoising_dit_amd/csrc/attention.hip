@@ -721,19 +721,29 @@ hipError_t launch_attention(const AttnParams& p_in, hipStream_t s) {
   AttnParams p = p_in;
   const int64_t n_wg = static_cast<int64_t>((p.n_q + kBM - 1) / kBM) * p.heads * p.batch;
   // One 512-thread workgroup per CU (128 KB of LDS each): a last round of
-  // f <= CUs/2 query tiles after at least one full round leaves most CUs
-  // idle, so with scratch each of those f tiles is split into
-  // min(CUs/f, 4, fewest key tiles of a row) key ranges and merged after.
+  // f query tiles after at least one full round leaves CUs - f idle.  With
+  // scratch each of those f tiles is split into the number of key ranges p
+  // (2..4, at most the fewest key tiles of a row, f * p partial tiles within
+  // the scratch) whose f * p workgroups finish soonest, ceil(f p / CUs) / p
+  // of a round, if that is under one round; the partials are merged after.
   p.wg_main = static_cast<int>(n_wg);
   p.tail_parts = 0;
   p.tail_o = p.tail_lse = nullptr;
   const int cu = compute_units();
   const int f = cu > 0 ? static_cast<int>(n_wg % cu) : 0;
-  if (p.tail_ws && !p.out_f32 && cu > 0 && n_wg >= cu && f > 0 && 2 * f <= cu) {
+  if (p.tail_ws && !p.out_f32 && cu > 0 && n_wg >= cu && f > 0) {
     int min_tiles = 1 << 30;
     for (int b = 0; b < p.batch; ++b) min_tiles = std::min(min_tiles, (p.n_valid[b] + kBN - 1) / kBN);
-    // (f * parts <= 256 partial tiles: the size of the scratch)
-    const int parts = std::min({cu / f, 256 / f, kAttnMaxTailParts, min_tiles});
+    int parts = 1;
+    double best = 1.0;  // rounds the last f tiles take unsplit
+    for (int q = 2; q <= kAttnMaxTailParts; ++q) {
+      if (q > min_tiles || f * q > kAttnMaxTailTiles) break;
+      const double t = static_cast<double>((f * q + cu - 1) / cu) / q;
+      if (t < best - 1e-9) {
+        best = t;
+        parts = q;
+      }
+    }
     if (parts >= 2) {
       p.wg_main = static_cast<int>(n_wg) - f;
       p.tail_parts = parts;

@@ -58,10 +58,11 @@ struct AttnParams {
   float* tail_o;
   float* tail_lse;
 };
-// Scratch of the split last round: at most 256 partial tiles of 256 query
-// rows, head_dim <= 128 fp32 values and one log-denominator each.
+// Scratch of the split last round: at most kAttnMaxTailTiles partial tiles
+// of 256 query rows, head_dim <= 128 fp32 values and one log-denominator each.
 constexpr int kAttnMaxTailParts = 4;
-constexpr size_t kAttnTailWsBytes = static_cast<size_t>(256) * 256 * (128 + 1) * 4;
+constexpr int kAttnMaxTailTiles = 448;
+constexpr size_t kAttnTailWsBytes = static_cast<size_t>(kAttnMaxTailTiles) * 256 * (128 + 1) * 4;
 static_assert(kAttnTailWsBytes <= kSplitWsBytes, "the block workspaces' split scratch serves both");
 hipError_t launch_attention(const AttnParams& p, hipStream_t s);
 

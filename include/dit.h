@@ -93,9 +93,9 @@ typedef struct dit_attn_desc {
  *            not overlapping q, k, v, out or lse; else DIT_EWORKSPACE /
  *            DIT_EINVAL).  With it, when the 256-query tiles of all rows and
  *            heads fill the device's compute units at least once and leave a
- *            last round at most half full, each tile of that round is split
- *            into 2-4 key ranges attended separately and merged by their
- *            log-denominators ("Difflet", section 4.3: the partial/merge
+ *            part-filled last round that a split finishes sooner, each tile
+ *            of that round is split into 2-4 key ranges attended separately
+ *            and merged by their log-denominators ("Difflet", section 4.3: the partial/merge
  *            arithmetic of ring attention): the same weighted sum, up to fp32
  *            and bf16 rounding of the partials (bitwise reproducible on one
  *            device; the split depends on its compute-unit count).  Its

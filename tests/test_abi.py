@@ -72,7 +72,7 @@ def test_attention_argument_errors():
     # optional workspace (the split of an under-filled last round): aligned,
     # at least dit_joint_attention_workspace_bytes(), overlapping nothing
     wsb = D.dit_joint_attention_workspace_bytes()
-    assert wsb >= 256 * 256 * 129 * 4
+    assert wsb >= 448 * 256 * 129 * 4
     ws = FAKE * 8
     _expect("DIT_EINVAL", f, _attn(), FAKE, FAKE, FAKE, hd, FAKE * 2, hd, workspace=ws + 64,
             workspace_bytes=wsb, stream=0)

@@ -482,16 +482,18 @@ def test_attention_parity(shape, q_scale):
     assert_parity(host(lse), l, f"{shape.name} lse", max_abs=1e-3, rel_l2=1e-5)
 
 
-# With a workspace, a last round of query tiles that fills at most half of
-# the compute units (after at least one full round; one 512-thread workgroup
-# per CU) is split along the keys into min(CUs/f, 4) ranges whose partials a
-# second kernel merges.  Shapes whose tile count leaves such a round on 256
-# CUs: 264 tiles (8 split 4 ways; head_dim 128 and 64) and 336 tiles of two
-# batch rows with different valid lengths (80 split 3 ways: the last range
-# holds the ragged bound).  Checked: against the oracle on sampled rows that
-# include the split tiles' rows, output and log-denominator at the strict
-# bar; bitwise equal to the call without workspace outside the split tiles,
-# not equal inside them (the split path ran); bitwise-equal reruns.
+# With a workspace, the f query tiles of an under-filled last round (after
+# at least one full round; one 512-thread workgroup per CU) are split along
+# the keys into the p ranges (2..4) whose f * p workgroups finish soonest,
+# ceil(f p / CUs) / p of a round, and a second kernel merges the partials.
+# Shapes whose tile count leaves such a round on 256 CUs: 264 tiles (8 split
+# 4 ways; head_dim 128 and 64), 336 tiles of two batch rows with different
+# valid lengths (80 split 3 ways: the last range holds the ragged bound) and
+# 400 tiles (144, more than half the CUs, split 3 ways).  Checked: against
+# the oracle on sampled rows that include the split tiles' rows, output and
+# log-denominator at the strict bar; bitwise equal to the call without
+# workspace outside the split tiles, not equal inside them (the split path
+# ran); bitwise-equal reruns.
 SPLIT_SHAPES = [
     C.AttnShape("split4_d128", batch=1, n_vis=8384, n_txt=64, heads=8, head_dim=128,
                 txt_valid=("fixed", (40,)), seed=47),
@@ -499,6 +501,8 @@ SPLIT_SHAPES = [
                 txt_valid=("fixed", (37, 100)), seed=48),
     C.AttnShape("split4_d64", batch=1, n_vis=8400, n_txt=48, heads=8, head_dim=64,
                 txt_valid=("fixed", (48,)), seed=49),
+    C.AttnShape("split3_f144", batch=1, n_vis=12600, n_txt=100, heads=8, head_dim=128,
+                txt_valid=("fixed", (64,)), seed=50),
 ]
 
 
@@ -507,7 +511,10 @@ def _split_tiles(shape, cu):
     n_qt = -(-shape.n_tok // 256)
     total = n_qt * shape.heads * shape.batch
     f = total % cu
-    if total < cu or f == 0 or 2 * f > cu:
+    if total < cu or f == 0:
+        return []
+    best = min((-(-f * p // cu) / p, p) for p in (1, 2, 3, 4) if f * p <= 448)
+    if best[1] == 1 or best[0] >= 1.0:
         return []
     return [(nid // (n_qt * shape.heads), (nid // n_qt) % shape.heads, nid % n_qt)
             for nid in range(total - f, total)]
