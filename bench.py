@@ -42,7 +42,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
 # x1.0); summary and commands in profiles/attn_c3_hbm_traffic.md.  Valid only
 # for the kernel source they were taken on.
 ATTN_TRAFFIC = {
-    "source_sha256": "b61e689cf4ce45f34bc78c1e86885d00819876efbccc01a5035a5f83de02d991",
+    "source_sha256": "b9db632a3a380a16f05c200579e86a4180aeaa8f0c20a5af838f10deafd89eae",
     "fetch_bytes": 3.8464e9,
     "write_bytes": 0.3732e9,
     "fetch_scale": 2.0,
