@@ -319,7 +319,7 @@ StepLayout step_layout(const dit_model_desc* m) {
   L.feat = o; o += align256(static_cast<size_t>(m->freq_dim) * 2);
   L.c = o; o += align256(D * 2);
   L.s = o; o += align256(D * 2);
-  L.mod = o; o += align256(6 * D * 2);
+  L.mod = o; o += align256(static_cast<size_t>(m->depth) * 6 * D * 2);  // every layer's modulation
   L.fin = o; o += align256(2 * D * 2);
   L.lat = o; o += align256(Bl * nv * C * 2);
   L.x = o; o += align256(B * N * D * 4);
@@ -1102,12 +1102,20 @@ dit_status check_step_args(const dit_model_desc* desc, const dit_model_weights* 
   return DIT_OK;
 }
 
-// Timestep conditioning s and the first block's input tokens x:
+// Timestep conditioning s, the modulations of layers [0, mod_layers) (and,
+// when that is every layer, the final one) and the first block's input
+// tokens x:
 //   f = sinusoidal(t_scale * sigma);  c = SiLU(f W1 + b1);  s = SiLU(c W2 + b2)
+//   mod_l = s W_mod[l] + b_mod[l];  fin = s W_fin + b_fin
 //   x[b] = [bf16(latent) W_in + b_in ; text[b]]
+// The modulations are matrix-vector products bound by their weight reads;
+// they run before the input projection, whose 4-byte-per-element store of x
+// would otherwise leave the caches full of fresh lines whose write-back
+// competes with those reads (at c3 the block modulation took 101 us inside
+// the step after the input projection, against 54 us from a clean cache).
 dit_status step_prologue(const dit_model_desc* desc, const dit_model_weights* w,
                          const float* latent, float sigma, const StepLayout& L, char* ws,
-                         hipStream_t stream) {
+                         int mod_layers, hipStream_t stream) {
   const dit_block_desc& bd = desc->block;
   const int B = bd.attn.batch, nv = bd.attn.n_vis;
   const int64_t N = static_cast<int64_t>(nv) + bd.attn.n_txt;
@@ -1123,6 +1131,17 @@ dit_status step_prologue(const dit_model_desc* desc, const dit_model_weights* w,
           "step: t-mlp 1");
   DIT_TRY(dit::launch_gemm(gemm(cbuf, D, w->t_w2, w->t_b2, 1, D, D, sbuf, D), DIT_EPI_SILU_BF16, stream),
           "step: t-mlp 2");
+  uint16_t* mod = reinterpret_cast<uint16_t*>(ws + L.mod);
+  for (int l = 0; l < mod_layers; ++l)
+    DIT_TRY(dit::launch_gemm(gemm(sbuf, D, w->mod_w[l], w->mod_b[l], 1, 6 * D, D,
+                                  mod + static_cast<int64_t>(l) * 6 * D, 6 * D),
+                             DIT_EPI_BF16, stream),
+            "step: modulation");
+  if (mod_layers == desc->depth)
+    DIT_TRY(dit::launch_gemm(gemm(sbuf, D, w->fin_w, w->fin_b, 1, 2 * D, D,
+                                  reinterpret_cast<uint16_t*>(ws + L.fin), 2 * D),
+                             DIT_EPI_BF16, stream),
+            "step: final modulation");
   DIT_TRY(dit::launch_cast_f32_bf16(latent, C, static_cast<int64_t>(Bl) * nv, C, lat, C, stream),
           "step: latent cast");
   {
@@ -1139,8 +1158,9 @@ dit_status step_prologue(const dit_model_desc* desc, const dit_model_weights* w,
   return DIT_OK;
 }
 
-// The block stack on x, the final adaLN and the projection of the visual rows
-// to the latent channels: v bf16 [batch, n_vis, C] in the workspace.
+// The block stack on x (modulations from the prologue), the final adaLN and
+// the projection of the visual rows to the latent channels: v bf16
+// [batch, n_vis, C] in the workspace.
 dit_status step_denoiser(const dit_model_desc* desc, const dit_model_weights* w,
                          const StepLayout& L, char* ws, hipStream_t stream) {
   dit_block_desc bd = desc->block;
@@ -1148,7 +1168,6 @@ dit_status step_denoiser(const dit_model_desc* desc, const dit_model_weights* w,
   const int B = bd.attn.batch, nv = bd.attn.n_vis;
   const int64_t N = static_cast<int64_t>(nv) + bd.attn.n_txt;
   const int D = bd.hidden, C = desc->latent_channels;
-  uint16_t* sbuf = reinterpret_cast<uint16_t*>(ws + L.s);
   uint16_t* mod = reinterpret_cast<uint16_t*>(ws + L.mod);
   uint16_t* fin = reinterpret_cast<uint16_t*>(ws + L.fin);
   float* x = reinterpret_cast<float*>(ws + L.x);
@@ -1156,15 +1175,11 @@ dit_status step_denoiser(const dit_model_desc* desc, const dit_model_weights* w,
   uint16_t* v = reinterpret_cast<uint16_t*>(ws + L.v);
   char* blk = ws + L.blk;
   for (int l = 0; l < desc->depth; ++l) {
-    DIT_TRY(dit::launch_gemm(gemm(sbuf, D, w->mod_w[l], w->mod_b[l], 1, 6 * D, D, mod, 6 * D),
-                             DIT_EPI_BF16, stream),
-            "step: modulation");
     const char* what = nullptr;
-    const hipError_t e = block_launch(&bd, &w->blocks[l], mod, 0, x, blk, stream, &what);
+    const hipError_t e = block_launch(&bd, &w->blocks[l], mod + static_cast<int64_t>(l) * 6 * D, 0, x, blk,
+                                      stream, &what);
     if (e != hipSuccess) return hip_status(e, what);
   }
-  DIT_TRY(dit::launch_gemm(gemm(sbuf, D, w->fin_w, w->fin_b, 1, 2 * D, D, fin, 2 * D), DIT_EPI_BF16, stream),
-          "step: final modulation");
   DIT_TRY(dit::launch_adaln(x, B * N, D, N, fin, fin + D, 0, bd.ln_eps, hf, stream), "step: final adaln");
   dit::GemmParams g = gemm(hf, D, w->out_w, w->out_b, static_cast<int64_t>(B) * nv, C, D, v, C);
   g.group_rows = nv;
@@ -1202,7 +1217,7 @@ dit_status dit_denoise_step(const dit_model_desc* desc, const dit_model_weights*
                                   workspace_bytes, &L);
   if (st != DIT_OK) return st;
   char* ws = static_cast<char*>(workspace);
-  if ((st = step_prologue(desc, w, latent, sigma, L, ws, stream)) != DIT_OK) return st;
+  if ((st = step_prologue(desc, w, latent, sigma, L, ws, desc->depth, stream)) != DIT_OK) return st;
   if ((st = step_denoiser(desc, w, L, ws, stream)) != DIT_OK) return st;
   // guidance + Euler on the fp32 latent
   const uint16_t* v = reinterpret_cast<const uint16_t*>(ws + L.v);
@@ -1290,17 +1305,13 @@ dit_status dit_cache_probe(const dit_model_desc* desc, const dit_model_weights* 
       overlap(score, 4, saved, feat_bytes))
     return fail(DIT_EINVAL, "saved or score overlaps the workspace or each other");
   char* ws = static_cast<char*>(workspace);
-  if ((st = step_prologue(desc, w, latent, sigma, L, ws, stream)) != DIT_OK) return st;
-  uint16_t* sbuf = reinterpret_cast<uint16_t*>(ws + L.s);
+  if ((st = step_prologue(desc, w, latent, sigma, L, ws, 1, stream)) != DIT_OK) return st;
   uint16_t* mod = reinterpret_cast<uint16_t*>(ws + L.mod);
   const float* x = reinterpret_cast<const float*>(ws + L.x);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.hf);
   float* part = reinterpret_cast<float*>(ws + L.part);
   const int64_t N = static_cast<int64_t>(bd.attn.n_vis) + bd.attn.n_txt;
-  // block 0's modulation and its first adaLN: h = LN(x) (1 + scale1) + shift1
-  DIT_TRY(dit::launch_gemm(gemm(sbuf, D, w->mod_w[0], w->mod_b[0], 1, 6 * D, D, mod, 6 * D),
-                           DIT_EPI_BF16, stream),
-          "probe: modulation");
+  // block 0's first adaLN (its modulation from the prologue): h = LN(x) (1 + scale1) + shift1
   DIT_TRY(dit::launch_adaln(x, rows, D, N, mod, mod + D, 0, bd.ln_eps, h, stream), "probe: adaln");
   if (have_saved)
     DIT_TRY(dit::launch_change_score(h, saved, true, rows * D, true, part, score, stream), "probe: score");
@@ -1345,7 +1356,7 @@ dit_status dit_denoise_step_cached(const dit_model_desc* desc, const dit_model_w
             "cached step: estimate");
     return ok();
   }
-  if ((st = step_prologue(desc, w, latent, sigma, L, ws, stream)) != DIT_OK) return st;
+  if ((st = step_prologue(desc, w, latent, sigma, L, ws, desc->depth, stream)) != DIT_OK) return st;
   if ((st = step_denoiser(desc, w, L, ws, stream)) != DIT_OK) return st;
   const uint16_t* v = reinterpret_cast<const uint16_t*>(ws + L.v);
   DIT_TRY(dit::launch_cached_velocity(latent, v, desc->cfg ? v + n : nullptr, n,

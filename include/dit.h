@@ -339,11 +339,14 @@ dit_status dit_cast_bf16_f32(const uint16_t* in, int64_t ld_in, int64_t rows,
  * Follow the diffusion pipeline).  Steps, in order, all on `stream`:
  *   f    = sinusoidal(t_scale * sigma, freq_dim)                (bf16 [1, F])
  *   c    = SiLU(f W_t1^T + b_t1);  s = SiLU(c W_t2^T + b_t2)    (bf16 [1, D])
+ *   for l < depth:  mod_l = s W_mod[l]^T + b_mod[l]  (bf16 [6, D], shared by
+ *                   every batch row);  (shift, scale) = s W_fin^T + b_fin
+ *                   (all depend on s alone and are computed here, before
+ *                   the input projection)
  *   x[b, :n_vis]  = bf16(latent[lb]) W_in^T + b_in              (fp32)
  *   x[b, n_vis:]  = text[b]                                     (fp32)
- *   for l < depth:  mod_l = s W_mod[l]^T + b_mod[l]  (bf16 [6, D], shared by
- *                   every batch row);  dit_block_forward(x; mod_l)
- *   (shift, scale) = s W_fin^T + b_fin;  h = adaLN(x; shift, scale)
+ *   for l < depth:  dit_block_forward(x; mod_l)
+ *   h = adaLN(x; shift, scale)
  *   v[b] = h[b, :n_vis] W_out^T + b_out                         (bf16)
  *   latent += (sigma_next - sigma) * v        (cfg == 0: each row its own
  *             latent, lb = b), or with cfg == 1 (batch == 2, row 0
