@@ -77,6 +77,10 @@ dit_status check_block_desc(const dit_block_desc* d) {
   dit_status s = check_attn_desc(&d->attn);
   if (s != DIT_OK) return s;
   const dit_attn_desc& a = d->attn;
+  const int64_t rows = static_cast<int64_t>(a.batch) * (static_cast<int64_t>(a.n_vis) + a.n_txt);
+  if (rows > DIT_LINEAR_MAX_M)
+    return fail(DIT_EUNSUPPORTED, "batch x tokens = %lld above %lld rows (the projections' limit)",
+                static_cast<long long>(rows), static_cast<long long>(DIT_LINEAR_MAX_M));
   if (d->hidden != a.heads * a.head_dim)
     return fail(DIT_EINVAL, "hidden %d != heads %d * head_dim %d", d->hidden, a.heads, a.head_dim);
   if (d->hidden % 64 != 0 || d->hidden > 16384)
@@ -160,6 +164,10 @@ dit_status check_linear(const dit_linear_args* a) {
     return fail(DIT_EINVAL, "bad GEMM shape m %lld n %d k %d", static_cast<long long>(a->m), a->n,
                 a->k);
   if (a->m == 0) return DIT_OK;
+  // One 256-row tile per grid row of the general kernel, at most 65535 of them.
+  if (a->m > DIT_LINEAR_MAX_M)
+    return fail(DIT_EUNSUPPORTED, "m %lld above %lld rows", static_cast<long long>(a->m),
+                static_cast<long long>(DIT_LINEAR_MAX_M));
   if (!a->a || !a->w || !a->out) return fail(DIT_EINVAL, "NULL a, w or out");
   if (a->k % 64 != 0) return fail(DIT_EUNSUPPORTED, "k %d must be a multiple of 64", a->k);
   if (a->n % 8 != 0) return fail(DIT_EUNSUPPORTED, "n %d must be a multiple of 8", a->n);

@@ -1035,6 +1035,7 @@ hipError_t launch(const GemmParams& p, hipStream_t s) {
   const int64_t want = (static_cast<int64_t>(m_blocks) * nx + 4 * (cu > 0 ? cu : 256) - 1) /
                        (4 * (cu > 0 ? cu : 256));
   const int per_wg = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(max_per, want)));
+  // (the dispatcher keeps this within 65535 workgroups along y)
   const dim3 grid(nx, (m_blocks + per_wg - 1) / per_wg);
   if (p.k == 64)
     hipLaunchKernelGGL((gemm_kernel<EPI, 2>), grid, dim3(kThreads), 0, s, p, m_blocks, per_wg);
@@ -1082,7 +1083,8 @@ hipError_t launch_gemm(const GemmParams& p, int epilogue, hipStream_t s) {
   // Few features over a long K (the projection to the latent channels) and
   // a short K onto many features (the projection from them): stream kernels.
   const int thin = p.n <= 64 && p.k >= 1024 && p.k % 256 == 0 && p.m >= 256 ? 1
-                   : (p.k == 64 || p.k == 128) && p.n >= 256 && p.m >= 1024 && p.m < (int64_t{1} << 31) ? 2 : 0;
+                   : (p.k == 64 || p.k == 128) && p.n >= 256 && p.m >= 1024 &&
+                             (p.m + 31) / 32 <= int64_t{65535} * (thin_k::kLdsBytes / (64 * p.k)) ? 2 : 0;
   if (thin) {
     switch (epilogue) {
       case EPI_BF16: return thin == 1 ? thin_n::launch<EPI_BF16>(p, s) : thin_k::launch<EPI_BF16>(p, s);

@@ -205,8 +205,10 @@ typedef enum dit_epilogue {
  *         kernel (deterministic; the summation order differs from the
  *         unsplit path's).  Its contents are scratch: overwritten, not read
  *         across calls; calls that share it must be ordered on one stream.
- * Requires k % 64 == 0 (DIT_EUNSUPPORTED otherwise), lda/ldc/strides multiples
- * of 8, pointers 16-byte aligned.  m, n >= 1 (m == 0 is a no-op). */
+ * Requires k % 64 == 0 and m <= DIT_LINEAR_MAX_M (DIT_EUNSUPPORTED otherwise),
+ * lda/ldc/strides multiples of 8, pointers 16-byte aligned.  m, n >= 1
+ * (m == 0 is a no-op). */
+#define DIT_LINEAR_MAX_M (65535LL * 256)
 typedef struct dit_linear_args {
   const uint16_t* a;
   int64_t lda;

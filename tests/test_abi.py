@@ -125,6 +125,9 @@ def test_linear_argument_errors():
     _expect("DIT_EUNSUPPORTED", f, FAKE, 96, FAKE * 2, None, 4, 8, 96, D.EPI_BF16, FAKE * 4, 8, stream=0)
     _expect("DIT_EUNSUPPORTED", f, FAKE, 64, FAKE * 2, None, 4, 12, 64, D.EPI_BF16, FAKE * 4, 16, stream=0)
     _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, 9, FAKE * 4, 8, stream=0)
+    # rows beyond DIT_LINEAR_MAX_M = 65535 * 256 (the general kernel's grid)
+    _expect("DIT_EUNSUPPORTED", f, FAKE, 64, FAKE * 2, None, 65535 * 256 + 1, 8, 64, D.EPI_BF16,
+            FAKE * 4, 8, stream=0)
     _expect("DIT_EINVAL", f, FAKE, 32, FAKE * 2, None, 4, 8, 64, D.EPI_BF16, FAKE * 4, 8, stream=0)
     _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, D.EPI_GATED_RES_F32, FAKE * 4, 8, stream=0)
     _expect("DIT_EINVAL", f, FAKE, 64, FAKE * 2, None, 4, 8, 64, D.EPI_BF16, FAKE + 64, 8, stream=0)
@@ -177,7 +180,8 @@ def test_block_descriptor_errors_and_workspace():
     for over, status in [({"hidden": 320}, "DIT_EINVAL"), ({"mlp": 1000}, "DIT_EUNSUPPORTED"),
                          ({"grid_w": 15}, "DIT_EINVAL"), ({"rope_h": 31}, "DIT_EINVAL"),
                          ({"rope_h": 30}, "DIT_EINVAL"), ({"rope_theta": 0.0}, "DIT_EINVAL"),
-                         ({"mod_stride": -4}, "DIT_EINVAL")]:
+                         ({"mod_stride": -4}, "DIT_EINVAL"),
+                         ({"batch": 8, "n_vis": 2_100_000}, "DIT_EUNSUPPORTED")]:
         d = _block(**over)
         with pytest.raises(D.DitError) as e:
             D.dit_block_workspace_bytes(d)
