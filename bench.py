@@ -799,7 +799,7 @@ def main():
         D.dit_block_forward(bdesc, bw, mod, x, bws, bws_bytes)
 
     block()
-    st_block = timed_stats(block, max(3, args.steps), stream)
+    st_block = timed_stats(block, max(50, args.steps), stream)
     ms_block = st_block["ms"]
 
     # joint attention alone, q/k/v as column blocks of one [N, 3*H*d] buffer (the block layout)
@@ -819,13 +819,13 @@ def main():
                               workspace=a_ws, workspace_bytes=a_wsb)
 
     attn()
-    st_attn = timed_stats(attn, max(5, args.steps), stream)
+    st_attn = timed_stats(attn, max(50, args.steps), stream)
     ms_attn = st_attn["ms"]
     # peaked softmax rows: q scaled by 4 (exact in bf16), so the running
     # maxima move more often and the O/l rescale is skipped less often
     qkv[..., :HD].mul_(4.0)
     attn()
-    st_attn_peaked = timed_stats(attn, max(5, args.steps), stream)
+    st_attn_peaked = timed_stats(attn, max(50, args.steps), stream)
     qkv[..., :HD].mul_(0.25)
     attn()  # o back to the unscaled inputs' output (the split comparison reads it)
     valid = [int(v) for v in inp.txt_valid]
