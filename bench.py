@@ -42,9 +42,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
 # x1.0); summary and commands in profiles/attn_c3_hbm_traffic.md.  Valid only
 # for the kernel source they were taken on.
 ATTN_TRAFFIC = {
-    "source_sha256": "b9db632a3a380a16f05c200579e86a4180aeaa8f0c20a5af838f10deafd89eae",
+    "source_sha256": "985f8e04a5119323f234c51298cd332060b3a4f6e9641d853c8373601098a9ef",
     "fetch_bytes": 3.8464e9,
-    "write_bytes": 0.3732e9,
+    "write_bytes": 0.3746e9,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     "profile": "profiles/attn_c3_hbm_traffic.md",

@@ -70,6 +70,11 @@ constexpr int kBM = kWaves * 32;  // queries per workgroup (32 per wave)
 #define DIT_ATTN_TRAIL 2
 #endif
 constexpr int kTrail = DIT_ATTN_TRAIL;
+// How far (log2 units) the softmax reference of a query may lag its running
+// maximum, once the query's partial sum of weights has reached kLagMinSum,
+// before l and O are rescaled.
+constexpr float kMaxLag = 2.f;
+constexpr float kLagMinSum = 32.f;
 
 template <int D>
 struct Tile {
@@ -344,7 +349,9 @@ __device__ __forceinline__ void mfma_tail(WaveState<D>& st, float c) {
 
 // Softmax phase for key tile j (keys j0 .. j0+63), whose max the MFMA phase
 // already took: mask past the bound (only the tile that holds it), update of
-// the running max with the rescale of l and O when it rose, p = exp2(s*c - m)
+// the reference max with the rescale of l and O when the tile's max passed
+// it (by more than kMaxLag for a query whose weights sum to kLagMinSum or
+// more), p = exp2(s*c - m)
 // of the first 32 keys into the running sum and, rounded to bf16, into
 // pf[0], pf[1]; the other 32 keys only as s*c - m (the next MFMA phase
 // exponentiates them).  VALU only.
@@ -358,12 +365,22 @@ __device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_va
       for (int r = 0; r < 16; ++r)
         if (j0 + 32 * t + 8 * (r / 4) + 4 * hi + (r % 4) >= n_valid) st.s[t][r] = -INFINITY;
   }
-  // Running max.  When no query of the wave sees a score above its running
-  // max, alpha would be exactly 1: the rescale of l and O is skipped,
-  // wave-uniformly (after the first tiles most tiles raise no max), and the
-  // result is bitwise the same as rescaling by 1.
+  // Reference max.  The weights p = exp2(s*c - m) are right for any
+  // reference m, since the final division by l cancels it; with m the exact
+  // running maximum the largest weight is exactly 1 and only the others are
+  // rounded to bf16.  l and O are rescaled (wave-uniformly) when some query
+  // of the wave sees a score above its reference, except that a query whose
+  // sum of weights l has reached kLagMinSum lets the reference lag its
+  // maximum by up to kMaxLag: its largest weight is then at most 2^kMaxLag
+  // and rounded like the others, which moves its output by at most
+  // 2^(kMaxLag-9) / kLagMinSum = 2^-12 of its largest |v| (l only grows
+  // until the next rescale, which makes the reference exact again).  Flat
+  // rows reach that sum within a few tiles, after which their maxima rise
+  // rarely and by little, so most rescales are skipped; peaked rows keep an
+  // exact reference.
   const float m_tile = st.m_tile;
-  if (__builtin_amdgcn_ballot_w64(m_tile > st.m_run) != 0) {
+  const float m_ref = st.l_run >= kLagMinSum ? st.m_run + kMaxLag : st.m_run;
+  if (__builtin_amdgcn_ballot_w64(m_tile > m_ref) != 0) {
     const float m_new = vmax3(st.m_run, m_tile, m_tile);
     const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
     st.m_run = m_new;

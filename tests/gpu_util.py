@@ -85,8 +85,7 @@ def assert_bf16_ulp(got, ref, what="", atol_rel=1e-4):
 # Composite bound factor: the GPU may sit at most TWIN_FACTOR times as far
 # from the bf16-storing fp64 oracle as the oracle's own fp32 twin does (see
 # assert_composite).  Measured on MI355X at every full-size composite:
-# 0.72-1.37 times in max-abs (1.48 before attention split its last round of
-# query tiles along the keys).
+# 0.73-1.27 times in max-abs.
 TWIN_FACTOR = 1.5
 
 
