@@ -101,7 +101,11 @@ typedef struct dit_attn_desc {
  *            device; the split depends on its compute-unit count).  Its
  *            contents are overwritten and not read across calls.
  * Scores are accumulated in fp32 from bf16 inputs (MFMA), softmax statistics
- * are fp32, probabilities are rounded to bf16 for the value product. */
+ * are fp32, probabilities are rounded to bf16 for the value product.  They are
+ * taken relative to a per-query reference that is the running maximum, or,
+ * once a query's weights sum to 32 or more, lags it by at most 2 (log2
+ * units); the largest weight is then rounded like the others, which moves
+ * that query's output by at most 2^-12 of its largest |v|. */
 size_t dit_joint_attention_workspace_bytes(void);
 dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q,
                                const uint16_t* k, const uint16_t* v,
