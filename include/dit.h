@@ -135,7 +135,8 @@ dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q,
  * Strides are multiples of 8 (q, k, v; kv_row_stride at most 2^24) and of 4
  * (out) and at least heads*head_dim; pointers 16-byte aligned (lse 4-byte).
  * out and lse must not overlap q, k, v or each other.  head_dim 64 or 128;
- * ceil(n_q / 256) * heads * batch at most 8388607 (else DIT_EUNSUPPORTED). */
+ * ceil(n_q / 256) * heads * batch at most 8388607 (else DIT_EUNSUPPORTED).
+ * Arithmetic as in dit_joint_attention (the same softmax reference). */
 #define DIT_MAX_PARTS 32
 typedef struct dit_partial_desc {
   int32_t batch;      /* 1..DIT_MAX_BATCH */
