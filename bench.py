@@ -42,7 +42,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
 # x1.0); summary and commands in profiles/attn_c3_hbm_traffic.md.  Valid only
 # for the kernel source they were taken on.
 ATTN_TRAFFIC = {
-    "source_sha256": "985f8e04a5119323f234c51298cd332060b3a4f6e9641d853c8373601098a9ef",
+    "source_sha256": "cf8050442f89ac1dd8356d61ebd08525d091e12f7dc76609ed77b3150c484858",
     "fetch_bytes": 3.8464e9,
     "write_bytes": 0.3746e9,
     "fetch_scale": 2.0,

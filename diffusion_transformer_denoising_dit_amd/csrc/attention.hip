@@ -173,7 +173,8 @@ struct WaveState {
   f32x16 s[2];        // S^T of one tile: s[t][4g + e] = score of key 32t + 8g + 4*hi + e
   f32x16 sh;          // s[1] of the last softmax'ed tile as s*c - m: exponentiated in the next MFMA phase
   bf16x8 pf[4];       // p of one tile as the B operand of four 16-key value steps
-  float m_run;        // running max of the scaled scores (log2 domain)
+  float m_run;        // reference max of the scaled scores (log2 domain): the running
+                      // max, or up to kMaxLag below it
   float m_tile;       // max of the scaled scores of the tile in s (this lane's query)
   float mx[4];        // the four partial max chains of the tile in s
   bf16x8 vt[kTrail > 0 ? kTrail : 1];  // V^T fragments of the value MFMAs issued after the phase barrier
@@ -367,20 +368,21 @@ __device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_va
   }
   // Reference max.  The weights p = exp2(s*c - m) are right for any
   // reference m, since the final division by l cancels it; with m the exact
-  // running maximum the largest weight is exactly 1 and only the others are
-  // rounded to bf16.  l and O are rescaled (wave-uniformly) when some query
-  // of the wave sees a score above its reference, except that a query whose
-  // sum of weights l has reached kLagMinSum lets the reference lag its
-  // maximum by up to kMaxLag: its largest weight is then at most 2^kMaxLag
-  // and rounded like the others, which moves its output by at most
-  // 2^(kMaxLag-9) / kLagMinSum = 2^-12 of its largest |v| (l only grows
-  // until the next rescale, which makes the reference exact again).  Flat
-  // rows reach that sum within a few tiles, after which their maxima rise
-  // rarely and by little, so most rescales are skipped; peaked rows keep an
-  // exact reference.
+  // running maximum, the key that sets a new maximum gets weight exactly 1
+  // and only the others are rounded to bf16.  l and O are rescaled
+  // (wave-uniformly) when some query of the wave sees a score above its
+  // reference, except that a query whose sum of weights l has reached
+  // kLagMinSum lets the reference lag its maximum by up to kMaxLag: weights
+  // then stay below 2^kMaxLag, and a key that sets a new maximum within that
+  // lag is rounded like the others, which moves the output by at most
+  // 2^(kMaxLag-9) / kLagMinSum = 2^-12 of the largest |v| per such key (the
+  // ratio of a weight to l survives later rescales, and l only grows between
+  // them).  Flat rows reach that sum within a few tiles, after which their
+  // maxima rise rarely and by little, so most rescales are skipped; peaked
+  // rows keep an exact reference.
   const float m_tile = st.m_tile;
-  const float m_ref = st.l_run >= kLagMinSum ? st.m_run + kMaxLag : st.m_run;
-  if (__builtin_amdgcn_ballot_w64(m_tile > m_ref) != 0) {
+  const float m_limit = st.l_run >= kLagMinSum ? st.m_run + kMaxLag : st.m_run;
+  if (__builtin_amdgcn_ballot_w64(m_tile > m_limit) != 0) {
     const float m_new = vmax3(st.m_run, m_tile, m_tile);
     const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
     st.m_run = m_new;

@@ -104,8 +104,9 @@ typedef struct dit_attn_desc {
  * are fp32, probabilities are rounded to bf16 for the value product.  They are
  * taken relative to a per-query reference that is the running maximum, or,
  * once a query's weights sum to 32 or more, lags it by at most 2 (log2
- * units); the largest weight is then rounded like the others, which moves
- * that query's output by at most 2^-12 of its largest |v|. */
+ * units); a key that sets a new maximum within that lag then gets a rounded
+ * weight rather than exactly 1, which moves the output by at most 2^-12 of
+ * the largest |v| per such key. */
 size_t dit_joint_attention_workspace_bytes(void);
 dit_status dit_joint_attention(const dit_attn_desc* desc, const uint16_t* q,
                                const uint16_t* k, const uint16_t* v,
