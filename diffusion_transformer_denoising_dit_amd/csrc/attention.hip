@@ -16,8 +16,8 @@
 //    The waves form two groups that alternate between an MFMA phase and a
 //    softmax phase, one phase apart, with a workgroup barrier at every phase
 //    boundary: while one wave of a SIMD multiplies, the other exponentiates.
-//    The softmax work of a tile is split: the max, the running-max update
-//    and half of the exponentials in the softmax phase, the tile max and the
+//    The softmax work of a tile is split: the tile max, the update of the
+//    reference max and half of the exponentials in the softmax phase, the
 //    other half of the exponentials between the MFMAs of the wave's own MFMA
 //    phase (a few independent VALU instructions per MFMA cost no MFMA time
 //    there; long dependent chains would).
@@ -212,7 +212,7 @@ __device__ __forceinline__ void tile_max_step(WaveState<D>& st, int i) {
   else if (k == 1) st.mx[c4] = vmax3(st.mx[c4], st.s[t][r0 + 3], st.s[t][r0 + 4]);
   else if (k == 2) st.mx[c4] = vmax3(st.mx[c4], st.s[t][r0 + 5], st.s[t][r0 + 6]);
   else st.mx[c4] = vmax3(st.mx[c4], st.s[t][r0 + 7], st.s[t][r0 + 7]);
-  asm volatile("" : "+v"(st.mx[c4]));  // keep the step here, not sunk to the end of the phase
+  asm volatile("" : "+v"(st.mx[c4]));  // keep the four chains interleaved in this order
 }
 
 template <int D>
@@ -227,8 +227,8 @@ __device__ __forceinline__ void tile_max_finish(WaveState<D>& st, float c) {
 // placed between them, where it issues while the matrix pipe runs (measured
 // on gfx950: up to ~4 FP32 VALU instructions per 32x32x16 MFMA cost no MFMA
 // time): after each score MFMA one exponential (with its row sum and bf16
-// packing) of the second half of tile j, and after each value MFMA one step
-// of tile j+1's max.  Fragment reads run a fixed number of steps ahead of
+// packing) of the second half of tile j.  Fragment reads run a fixed number
+// of steps ahead of
 // their MFMA (scheduling fences keep the compiler from hoisting all 32 of
 // them, which would cost 128 VGPRs).
 template <int D, bool kPVPart, bool kQKPart, int kTr = 0>
@@ -281,20 +281,6 @@ __device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, con
 #pragma unroll
     for (int i = 0; i < 16; ++i) finish_part(i);
   }
-  // The new tile's max, 32 scores -> 1 in 16 v_max3 on four independent
-  // chains, one step after each value MFMA (there the wave has issue slots
-  // to spare); the softmax phase starts from it.  The tile that holds the
-  // bound needs no mask for this: its key rows past the bound were loaded
-  // as copies of the last valid key's row, so those scores repeat a valid
-  // one and leave the max unchanged (the softmax phase masks them before
-  // exponentiating).
-  auto max_step = [&](int i) { tile_max_step(st, i); };
-  if constexpr (kQKPart) {
-    if constexpr (!kPVPart) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) max_step(i);
-    }
-  }
   if constexpr (kPVPart) {
     st.l_run += lp0 + lp1;
     // keep the sums here, between the MFMAs, rather than let the compiler
@@ -316,41 +302,27 @@ __device__ __forceinline__ void mfma_phase(WaveState<D>& st, const char* sK, con
       if (i + kAhead < kPV) vf[i + kAhead] = vread(i + kAhead);
       __builtin_amdgcn_sched_barrier(0);
       st.o[i % W::kDB] = mfma32x32x16(vf[i], st.pf[i / W::kDB], st.o[i % W::kDB]);
-      if constexpr (kQKPart) {
-        constexpr int kPer = 16 / kPV;
-#pragma unroll
-        for (int n = 0; n < kPer; ++n) max_step(i * kPer + n);
-      }
     }
 #pragma unroll
     for (int j = 0; j < kTr; ++j) st.vt[j] = vf[kPV - kTr + j];
   }
-  if constexpr (kQKPart && kTr == 0) tile_max_finish(st, c);
 }
 
 // The last kTr value MFMAs of an MFMA phase (their V^T fragments already in
-// st.vt), issued right after the barrier that ends the phase, then the rest
-// of the tile max.
-template <int D, bool kQKPart, int kTr>
-__device__ __forceinline__ void mfma_tail(WaveState<D>& st, float c) {
+// st.vt), issued right after the barrier that ends the phase.
+template <int D, int kTr>
+__device__ __forceinline__ void mfma_tail(WaveState<D>& st) {
   using W = WaveState<D>;
   constexpr int kPV = 4 * W::kDB;
 #pragma unroll
   for (int j = 0; j < kTr; ++j) {
     const int i = kPV - kTr + j;
     st.o[i % W::kDB] = mfma32x32x16(st.vt[j], st.pf[i / W::kDB], st.o[i % W::kDB]);
-    if constexpr (kQKPart) {
-      constexpr int kPer = 16 / kPV;
-#pragma unroll
-      for (int n = 0; n < kPer; ++n) tile_max_step(st, i * kPer + n);
-    }
   }
-  if constexpr (kQKPart) tile_max_finish(st, c);
 }
 
-// Softmax phase for key tile j (keys j0 .. j0+63), whose max the MFMA phase
-// already took: mask past the bound (only the tile that holds it), update of
-// the reference max with the rescale of l and O when the tile's max passed
+// Softmax phase for key tile j (keys j0 .. j0+63): the tile max, mask past
+// the bound (only the tile that holds it), update of the reference max with the rescale of l and O when the tile's max passed
 // it (by more than kMaxLag for a query whose weights sum to kLagMinSum or
 // more), p = exp2(s*c - m)
 // of the first 32 keys into the running sum and, rounded to bf16, into
@@ -359,6 +331,15 @@ __device__ __forceinline__ void mfma_tail(WaveState<D>& st, float c) {
 template <int D>
 __device__ __forceinline__ void softmax_phase(WaveState<D>& st, int j0, int n_valid, int hi, float c) {
   using W = WaveState<D>;
+  // The tile's max, 32 scores -> 1 in 16 v_max3 on four independent chains.
+  // The tile that holds the bound needs no mask for this: its key rows past
+  // the bound were loaded as copies of the last valid key's row, so those
+  // scores repeat a valid one and leave the max unchanged.  (Taken here
+  // rather than between the value MFMAs of the MFMA phase: that phase is the
+  // longer of the two once most rescales are skipped.)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) tile_max_step(st, i);
+  tile_max_finish(st, c);
   if (j0 + kBN > n_valid) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -627,7 +608,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_kernel(AttnParams p) {
     mfma_prio(true);
     mfma_phase<D, true, true, kTrail>(st, stage(k + 1), stage(k) + T::kBytes, c);
     barrier_wait(!a_grp, k + 2);
-    mfma_tail<D, true, kTrail>(st, c);  // keeps the matrix pipe busy across the hand-over
+    mfma_tail<D, kTrail>(st);  // keeps the matrix pipe busy across the hand-over
     mfma_prio(false);
     barrier_issue(!a_grp, k + 2);
     softmax_phase<D>(st, (k + 1) * kBN, n_valid, hi, c);
