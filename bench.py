@@ -42,9 +42,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
 # x1.0); summary and commands in profiles/attn_c3_hbm_traffic.md.  Valid only
 # for the kernel source they were taken on.
 ATTN_TRAFFIC = {
-    "source_sha256": "1615dbd07d81e05ee768a46a463ec5fe91d53a86c72b213bdaa120cf13676200",
-    "fetch_bytes": 3.9909e9,
-    "write_bytes": 0.3724e9,
+    "source_sha256": "36de9ff5cc4916a5f0abf43eacb27e7d84ba19c4071fe628692982e9c974185c",
+    "fetch_bytes": 3.8461e9,
+    "write_bytes": 0.3765e9,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
     "profile": "profiles/attn_c3_hbm_traffic.md",
