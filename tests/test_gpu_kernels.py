@@ -482,6 +482,48 @@ def test_attention_parity(shape, q_scale):
     assert_parity(host(lse), l, f"{shape.name} lse", max_abs=1e-3, rel_l2=1e-5)
 
 
+def test_attention_reference_lag():
+    """Designed scores that drive the softmax reference through both of its
+    paths.  q is nonzero in one dimension only, so query i's log2-domain score
+    of key j is f_i * b_j: keys 0..383 are flat (b in [-1, 0]), key 340 (tile
+    5) rises 1.5 above them, key 390 (the last, partly valid tile) rises to 4.
+    With f = 0.5 and 1 a query has summed its weights past 32 (per half row)
+    after two tiles, so at key 340 its reference lags instead of rescaling,
+    and at key 390 (a rise of 2 and 4) it rescales; f = 4 rescales at both;
+    f = 0 keeps every weight at 1.  Every output element must lie within one
+    bf16 unit of the exact value (its own rounding to bf16 is half of that)
+    plus 5e-4 (absolute) for the bf16 rounding of the weights
+    (the lag adds at most 2^-12 of max |v| per lagged key).  Measured on
+    MI355X: the worst element, 7.5e-3 at |o| = 2.9, in the f = 4 rows (the
+    output's own rounding; 0.84 of the bound), the lagged rows within 4.6e-4."""
+    s = C.AttnShape("lag", batch=1, n_vis=384, n_txt=16, heads=1, head_dim=128,
+                    txt_valid=("fixed", (16,)), seed=91)
+    N, d = s.n_tok, s.head_dim
+    rng = np.random.default_rng(91)
+    c = math.log2(math.e) / math.sqrt(d)
+    b = rng.uniform(-1.0, 0.0, N)
+    b[340], b[390] = 1.5, 4.0
+    f = np.array([0.0, 0.5, 1.0, 4.0])[np.arange(N) % 4]
+    q = np.zeros((1, N, d), np.float32)
+    q[0, :, 0] = f / c
+    k = rng.normal(0.0, 0.3, (1, N, d)).astype(np.float32)
+    k[0, :, 0] = b
+    inp = {"q": G.f32_to_bf16_bits(q), "k": G.f32_to_bf16_bits(k),
+           "v": G.normal_bf16(92, (1, N, d)), "txt_valid": np.array([16])}
+    out, lse = _run_attention(s, inp)
+    o, l = _oracle_attention(s, inp)
+    got = host(out)
+    want = o.reshape(got.shape)
+    atol = 5e-4 / float(np.abs(want).max())  # 5e-4 absolute, as a fraction of max |output|
+    assert_bf16_ulp(got, want, "reference lag", atol_rel=atol)
+    assert_parity(host(lse), l, "reference lag lse", max_abs=1e-3, rel_l2=1e-5)
+    for fi in (0.0, 0.5, 1.0, 4.0):  # each regime on its own rows
+        rows = np.nonzero(f == fi)[0]
+        ma = float(np.abs(want[:, rows]).max())
+        assert_bf16_ulp(got[:, rows], want[:, rows], f"reference lag, f = {fi:g}",
+                        atol_rel=5e-4 / max(ma, 1e-30))
+
+
 # With a workspace, the f query tiles of an under-filled last round (after
 # at least one full round; one 512-thread workgroup per CU) are split along
 # the keys into the p ranges (2..4) whose f * p workgroups finish soonest,
